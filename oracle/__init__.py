@@ -1,0 +1,18 @@
+"""Oracle for the int2 draft LM head. TEST INFRASTRUCTURE ONLY.
+
+Only tests/, __graft_entry__.smoke() and bench.py's CPU-baseline leg may import this package.
+The product path (the HIP library and its Python binding) never imports, calls or links it.
+
+Parity status: every function is pinned by the CPU tests in tests/test_oracle_pins.py against
+values fixed by the page or by mathematics (closed forms, exact-grid constructions, brute force
+on small inputs, invariants and byte counts the page prints).
+"""
+from .int2_head import (BLOCK_N, GROUP, bf16_to_f32, block_emit, check_shape, coarse_logits,
+                        dequantize, exact_logits, f32_to_bf16, finalize, group_sums, head, pack,
+                        pack_quarter_split, premultiplied_scales, quantize, rerank_exact,
+                        select_top_r, storage_bytes, unpack_quarter_split)
+
+__all__ = ["BLOCK_N", "GROUP", "bf16_to_f32", "block_emit", "check_shape", "coarse_logits",
+           "dequantize", "exact_logits", "f32_to_bf16", "finalize", "group_sums", "head", "pack",
+           "pack_quarter_split", "premultiplied_scales", "quantize", "rerank_exact",
+           "select_top_r", "storage_bytes", "unpack_quarter_split"]
