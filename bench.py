@@ -1,0 +1,304 @@
+"""Benchmark of the int2 draft LM head on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bands]
+
+A step is one call of the head's per-call path over one batch: group sums of x, the coarse
+int2 pass with its fused block top-8 emit, the top-32 selection, the exact bf16 rerank and the
+argmax, all enqueued on one stream with no host synchronisation. The workload is one rank's
+vocab slice, x[1, 5120] @ W[5120, 124160] (the draft-slot shape), with inputs resident in HBM.
+The stored head (packed codes + scales, 178.8 MB) fits in the 256 MB last-level cache, so the
+steps rotate over COPIES independent copies of it (2.1 GB) and every step reads its copy from
+HBM. The quantise+pack of the bf16 weight is a load-time step and is timed on its own.
+
+Prints one JSON line. `value` is the head's algorithmic HBM bytes per call divided by the
+measured time per call (GB/s); `us_per_call` is the same time. `roofline` covers the coarse
+kernel, the dominant one, timed with HIP events on the launch stream over the timed region.
+`cpu_baseline` times the oracle (test infrastructure, CPU) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/call + HBM GB/s, int2 head 5120×124160 at M=1/16/64; argmax match %"
+WORKLOAD = "draft_slot_m1_k5120_n124160"
+COPIES = 12
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFS = 2500.0
+KC, R = 8, 32
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "coarse_traffic.json")
+COARSE_SRC = os.path.join(ROOT, "bit_quantized_lm_int2_amd", "csrc", "coarse.hip")
+
+
+def head_bytes(M, N, K, kc=KC, R_=R, k=1):
+    """Algorithmic HBM bytes of one call, per kernel (see the design notes for the rules)."""
+    KG = K // 128
+    nblk = (N + 63) // 64
+    cand = M * nblk * kc * 8
+    stored = N * K // 4 + 2 * N * KG * 2
+    b = {
+        "xsum": M * K * 2 + M * KG * 4,
+        "coarse": stored + M * K * 2 + M * KG * 4 + cand,
+        "select": cand + M * R_ * 4,
+        "rerank": M * R_ * 4 + M * R_ * K * 2 + M * K * 2 + M * R_ * 4,
+        "finalize": M * R_ * 8 + M * k * 8,
+    }
+    b["total"] = sum(b.values())
+    return b
+
+
+def coarse_source_hash():
+    h = hashlib.sha256()
+    for name in ("coarse.hip", "device_util.h"):
+        with open(os.path.join(ROOT, "bit_quantized_lm_int2_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(M):
+    """HBM bytes per coarse launch from the committed rocprofv3 counter runs, if they were
+    taken on the current coarse kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != coarse_source_hash():
+        return None
+    return t.get("per_launch_bytes", {}).get(str(M))
+
+
+class Head:
+    """Preallocated buffers and prebuilt ctypes arguments for one M, so a step enqueues five
+    launches with no allocation and little host work."""
+
+    def __init__(self, i2h, torch, x, copies, W, M, N, K):
+        self.lib = i2h.lib()
+        self.x = x
+        dev = x.device
+        KG = K // 128
+        nblk = (N + 63) // 64
+        self.xs = torch.empty(M, KG, dtype=torch.float32, device=dev)
+        self.cs = torch.empty(M, nblk * KC, dtype=torch.float32, device=dev)
+        self.ci = torch.empty(M, nblk * KC, dtype=torch.int32, device=dev)
+        self.sel = torch.empty(M, R, dtype=torch.int32, device=dev)
+        self.ex = torch.empty(M, R, dtype=torch.float32, device=dev)
+        self.oi = torch.empty(M, 1, dtype=torch.int32, device=dev)
+        self.ov = torch.empty(M, 1, dtype=torch.float32, device=dev)
+        ws_n = i2h.workspace_bytes(M, N, K, KC, R)
+        self.ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+        s = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.stream = s
+        self.a_xsum = (P(x), M, K, P(self.xs), s)
+        self.a_coarse = [(P(x), P(self.xs), M, P(p), P(S), P(Z), N, K, KC, P(self.cs), P(self.ci), None, s)
+                         for (p, S, Z) in copies]
+        self.a_select = (P(self.cs), P(self.ci), M, nblk, KC, R, P(self.sel), s)
+        self.a_rerank = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, P(self.ex), s)
+        self.a_final = (P(self.ex), P(self.sel), M, R, 1, P(self.oi), P(self.ov), s)
+        self.a_head = [(P(x), M, P(p), P(S), P(Z), P(W), W.stride(0), N, K, KC, R, 1, P(self.oi), P(self.ov),
+                        None, P(self.ws), ws_n, s) for (p, S, Z) in copies]
+
+    def step(self, i, ev0=None, ev1=None):
+        L = self.lib
+        st = L.i2h_xsum(*self.a_xsum)
+        if ev0 is not None:
+            ev0.record()
+        st |= L.i2h_coarse_topk(*self.a_coarse[i % len(self.a_coarse)])
+        if ev1 is not None:
+            ev1.record()
+        st |= L.i2h_select(*self.a_select)
+        st |= L.i2h_rerank(*self.a_rerank)
+        st |= L.i2h_finalize(*self.a_final)
+        if st:
+            raise RuntimeError(f"libi2h status {st}")
+
+    def fused(self, i):
+        st = self.lib.i2h_head(*self.a_head[i % len(self.a_head)])
+        if st:
+            raise RuntimeError(f"libi2h status {st}")
+
+
+def time_steps(torch, fn, steps, warmup, events=False):
+    """(seconds per step by host clock around a synchronised loop, mean coarse ms by events)."""
+    for i in range(warmup):
+        fn(i, None, None) if events else fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)] if events else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if events:
+            fn(warmup + i, *evs[i])
+        else:
+            fn(warmup + i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    coarse_ms = None
+    if events:
+        coarse_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    return dt, coarse_ms
+
+
+def to_dev_bits(torch, np, b, dev):
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bands", action="store_true")
+    ap.add_argument("--match-rows", type=int, default=32)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_lm_int2_amd as i2h
+    import synth_inputs as si
+
+    i2h.lib()
+    dev = torch.device("cuda:0")
+    cfg = si.WORKLOADS[WORKLOAD]
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    log(f"[bench] generating W [{N}, {K}] and x")
+    Wc = si.gen_weight(N, K)
+    W = Wc.to(dev)
+    nrows = max(args.match_rows, 64)
+    x_all_c = si.gen_x(nrows, K, outliers=cfg["outliers"])
+    x_all = x_all_c.to(dev)
+
+    # load-time pack, timed on its own
+    packed, S, ZS = i2h.pack(W)
+    torch.cuda.synchronize()
+    pk = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        i2h.pack(W, out=(packed, S, ZS))
+        b.record()
+        torch.cuda.synchronize()
+        pk.append(a.elapsed_time(b) * 1e3)
+    pack_us = float(np.median(pk))
+    pack_bytes = N * K * 2 + N * K // 4 + 2 * N * (K // 128) * 2
+    copies = [(packed, S, ZS)] + [(packed.clone(), S.clone(), ZS.clone()) for _ in range(COPIES - 1)]
+    torch.cuda.synchronize()
+
+    def measure(Mb, steps, warmup):
+        x = x_all[:Mb].contiguous()
+        h = Head(i2h, torch, x, copies, W, Mb, N, K)
+        dt, coarse_ms = time_steps(torch, h.step, steps, warmup, events=True)
+        dt_fused, _ = time_steps(torch, h.fused, steps, warmup)
+        torch.cuda.synchronize()
+        return h, dt, coarse_ms, dt_fused
+
+    log(f"[bench] timing M={M}: {args.warmup} warmup + {args.steps} steps")
+    h, dt, coarse_ms, dt_fused = measure(M, args.steps, args.warmup)
+    hb = head_bytes(M, N, K)
+    us = dt * 1e6
+    coarse_us = coarse_ms * 1e3
+    achieved = hb["coarse"] / (coarse_us * 1e-6) / 1e9
+    traffic = traffic_for(M)
+
+    bands = []
+    if not args.no_bands:
+        for Mb in (16, 64):
+            log(f"[bench] timing band M={Mb}")
+            _, dtb, cmsb, dtfb = measure(Mb, max(20, args.steps // 2), max(5, args.warmup // 2))
+            hbb = head_bytes(Mb, N, K)
+            flops = 2.0 * Mb * K * N
+            bands.append(dict(M=Mb, us_per_call=round(dtb * 1e6, 2), us_per_call_fused=round(dtfb * 1e6, 2),
+                              coarse_us=round(cmsb * 1e3, 2),
+                              gbps=round(hbb["total"] / dtb / 1e9, 1),
+                              coarse_gbps=round(hbb["coarse"] / (cmsb * 1e-3) / 1e9, 1),
+                              coarse_hbm_frac=round(hbb["coarse"] / (cmsb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                              coarse_tflops_useful=round(flops / (cmsb * 1e-3) / 1e12, 2),
+                              mfma_util_useful=round(flops / (cmsb * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
+                              coarse_traffic_bytes=traffic_for(Mb)))
+
+    # argmax match against the oracle on the first rows, one call per row as in the timed step
+    result = {}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        log(f"[bench] argmax match on {args.match_rows} rows (GPU calls of M=1)")
+        got = []
+        for r in range(args.match_rows):
+            idx, _ = i2h.head(x_all[r:r + 1].contiguous(), packed, S, ZS, W, kcand=KC, R=R, k=1)
+            got.append(int(idx.item()))
+        Wb, xb = si.bits(Wc), si.bits(x_all_c[:args.match_rows])
+        log("[bench] oracle pack (untimed, load-time step)")
+        po, So, ZSo = oracle.pack(Wb)
+        threads = oracle.int2_head._threads()
+        log("[bench] oracle head, one call of the timed workload (timed)")
+        t0 = time.perf_counter()
+        r1 = oracle.head(xb[:1], Wb, po, So, ZSo, kcand=KC, R=R, k=1)
+        cpu_s = time.perf_counter() - t0
+        log("[bench] oracle head on the match rows")
+        ro = oracle.head(xb, Wb, po, So, ZSo, kcand=KC, R=R, k=1)
+        want = [int(v) for v in ro["idx"][:, 0]]
+        match = sum(int(a == b) for a, b in zip(got, want))
+        ex = oracle.exact_logits(xb, Wb)
+        recall = sum(int(a == b) for a, b in zip(want, ex.argmax(1)))
+        result = dict(argmax_match_pct=round(100.0 * match / len(want), 2), argmax_rows=len(want),
+                      recall_vs_dense_bf16_pct=round(100.0 * recall / len(want), 2))
+        assert int(r1["idx"][0, 0]) == want[0]
+        cpu = dict(value=round(hb["total"] / cpu_s / 1e9, 4), unit="GB/s", us_per_call=round(cpu_s * 1e6, 1),
+                   cores=threads, kind="oracle",
+                   sample=f"one call of the {WORKLOAD} head (coarse over all {N} rows, emit, select, rerank, "
+                          f"argmax) on the numpy oracle with {threads} threads; pack excluded")
+
+    out = {
+        "metric": METRIC,
+        "value": round(hb["total"] / dt / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "K": K, "N": N, "kcand": KC, "R": R, "output": "argmax",
+                   "cold_cache_copies": COPIES, "group": 128, "block_n": 64},
+        "us_per_call": round(us, 2),
+        "us_per_call_fused_entry": round(dt_fused * 1e6, 2),
+        "bytes_per_call": hb["total"],
+        "gbps_packed_only": round(N * K / 4 / dt / 1e9, 1),
+        "hbm_frac": round(hb["total"] / dt / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "coarse_kernel<1>", "kernel_us": round(coarse_us, 2),
+                     "algorithmic_bytes": hb["coarse"]},
+        "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
+                 "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},
+        **result,
+        "bands": bands,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+"""Python binding of libi2h, the int2 speculative-draft LM head for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch provides the
+device memory and the stream; each call enqueues on torch's current stream of the tensors'
+device and returns without synchronising. The names follow the C ABI in include/i2h.h.
+
+    packed, S, ZS = pack(W)                       # W bf16 [N, K] on the GPU
+    idx, val = head(x, packed, S, ZS, W, k=1)     # argmax per row of x bf16 [M, K]
+    idx, val = head(x, packed, S, ZS, W, k=16)    # top-16 drawn from the reranked tokens
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
+           "rerank", "finalize", "workspace_bytes", "head", "GROUP", "BLOCK_N"]
+
+GROUP = 128
+BLOCK_N = 64
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libi2h.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SIGNATURES = {
+    "i2h_version": ([], _INT),
+    "i2h_strerror": ([_INT], ctypes.c_char_p),
+    "i2h_last_hip_error": ([], _INT),
+    "i2h_sizes": ([_I64, _I64, _P, _P], _INT),
+    "i2h_pack": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
+    "i2h_xsum": ([_P, _I64, _I64, _P, _P], _INT),
+    "i2h_coarse_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P], _INT),
+    "i2h_select": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P], _INT),
+    "i2h_rerank": ([_P, _I64, _P, _I64, _I64, _I64, _P, _INT, _P, _P], _INT),
+    "i2h_finalize": ([_P, _P, _I64, _INT, _INT, _P, _P, _P], _INT),
+    "i2h_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
+    "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
+                  _I64, _P], _INT),
+}
+
+
+class I2HError(RuntimeError):
+    """A libi2h call returned a negative status."""
+
+    def __init__(self, name: str, status: int):
+        msg = lib().i2h_strerror(status).decode()
+        if status == -6:
+            msg += f" (hipError {lib().i2h_last_hip_error()})"
+        super().__init__(f"{name}: {msg} [status {status}]")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libi2h. Raises if the library has not been built: there is no fallback."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"libi2h.so not found at {_LIB_PATH}; build it with "
+                              "`python -m bit_quantized_lm_int2_amd.build` (needs hipcc)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise I2HError(name, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _rows(t: torch.Tensor, name: str) -> int:
+    """Row stride of a 2-D tensor whose rows are contiguous."""
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} rows must be contiguous")
+    return t.stride(0)
+
+
+def _dense(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _shape(t: torch.Tensor, name: str, shape) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _head_shapes(x, packed, S, ZS, xs=None):
+    """(M, N, K) after checking that the stored head matches x."""
+    M, K = x.shape
+    N = packed.shape[0]
+    _shape(packed, "packed", (N, K // 4))
+    _need(S, "S", torch.bfloat16, 2)
+    _need(ZS, "ZS", torch.bfloat16, 2)
+    _shape(S, "S", (N, K // GROUP))
+    _shape(ZS, "ZS", (N, K // GROUP))
+    if xs is not None:
+        _need(xs, "xs", torch.float32, 2)
+        _shape(xs, "xs", (M, K // GROUP))
+    return M, N, K
+
+
+def sizes(N: int, K: int):
+    pb, se = ctypes.c_int64(), ctypes.c_int64()
+    _check("i2h_sizes", lib().i2h_sizes(N, K, ctypes.byref(pb), ctypes.byref(se)))
+    return pb.value, se.value
+
+
+def pack(W: torch.Tensor, out=None):
+    """(packed u8 [N, K/4], S bf16 [N, K/128], ZS bf16 [N, K/128]) for a bf16 head W [N, K]."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if out is None:
+        packed = torch.empty(N, K // 4, dtype=torch.uint8, device=W.device)
+        S = torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=W.device)
+        ZS = torch.empty_like(S)
+    else:
+        packed, S, ZS = out
+    _shape(packed, "packed", (N, K // 4))
+    _shape(S, "S", (N, K // GROUP))
+    _shape(ZS, "ZS", (N, K // GROUP))
+    for t, nm in ((packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    _check("i2h_pack", lib().i2h_pack(_ptr(W), _rows(W, "W"), N, K, _ptr(packed), _ptr(S), _ptr(ZS),
+                                      _stream(W)))
+    return packed, S, ZS
+
+
+def xsum(x: torch.Tensor, out=None) -> torch.Tensor:
+    _need(x, "x", torch.bfloat16, 2)
+    _dense(x, "x")
+    M, K = x.shape
+    xs = out if out is not None else torch.empty(M, K // GROUP, dtype=torch.float32, device=x.device)
+    _shape(xs, "xs", (M, K // GROUP))
+    _check("i2h_xsum", lib().i2h_xsum(_ptr(x), M, K, _ptr(xs), _stream(x)))
+    return xs
+
+
+def coarse_topk(x, xs, packed, S, ZS, kcand: int = 8, want_y: bool = False):
+    """(cand_score fp32 [M, NBLK*kcand], cand_idx int32 [M, NBLK*kcand], y bf16 [M, N] or None)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 2)
+    for t, nm in ((x, "x"), (xs, "xs"), (packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    M, N, K = _head_shapes(x, packed, S, ZS, xs)
+    nblk = (N + BLOCK_N - 1) // BLOCK_N
+    cs = torch.empty(M, nblk * kcand, dtype=torch.float32, device=x.device)
+    ci = torch.empty(M, nblk * kcand, dtype=torch.int32, device=x.device)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if want_y else None
+    _check("i2h_coarse_topk", lib().i2h_coarse_topk(_ptr(x), _ptr(xs), M, _ptr(packed), _ptr(S), _ptr(ZS),
+                                                    N, K, kcand, _ptr(cs), _ptr(ci), _ptr(y), _stream(x)))
+    return cs, ci, y
+
+
+def select(cand_score, cand_idx, kcand: int, R: int) -> torch.Tensor:
+    _need(cand_score, "cand_score", torch.float32, 2)
+    _need(cand_idx, "cand_idx", torch.int32, 2)
+    _dense(cand_score, "cand_score")
+    _dense(cand_idx, "cand_idx")
+    M, ncand = cand_score.shape
+    _shape(cand_idx, "cand_idx", (M, ncand))
+    if ncand % kcand:
+        raise ValueError("candidate count is not a multiple of kcand")
+    sel = torch.empty(M, R, dtype=torch.int32, device=cand_score.device)
+    _check("i2h_select", lib().i2h_select(_ptr(cand_score), _ptr(cand_idx), M, ncand // kcand, kcand, R,
+                                          _ptr(sel), _stream(cand_score)))
+    return sel
+
+
+def rerank(x, W, sel) -> torch.Tensor:
+    _need(x, "x", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(sel, "sel", torch.int32, 2)
+    _dense(x, "x")
+    _dense(sel, "sel")
+    M, K = x.shape
+    R = sel.shape[1]
+    _shape(sel, "sel", (M, R))
+    if W.shape[1] != K:
+        raise ValueError("W must have K columns")
+    ex = torch.empty(M, R, dtype=torch.float32, device=x.device)
+    _check("i2h_rerank", lib().i2h_rerank(_ptr(x), M, _ptr(W), _rows(W, "W"), W.shape[0], K, _ptr(sel), R,
+                                          _ptr(ex), _stream(x)))
+    return ex
+
+
+def finalize(exact, sel, k: int = 1):
+    _need(exact, "exact", torch.float32, 2)
+    _need(sel, "sel", torch.int32, 2)
+    _dense(exact, "exact")
+    _dense(sel, "sel")
+    M, R = exact.shape
+    _shape(sel, "sel", (M, R))
+    oi = torch.empty(M, k, dtype=torch.int32, device=exact.device)
+    ov = torch.empty(M, k, dtype=torch.float32, device=exact.device)
+    _check("i2h_finalize", lib().i2h_finalize(_ptr(exact), _ptr(sel), M, R, k, _ptr(oi), _ptr(ov),
+                                              _stream(exact)))
+    return oi, ov
+
+
+def workspace_bytes(M: int, N: int, K: int, kcand: int = 8, R: int = 32) -> int:
+    n = lib().i2h_workspace_bytes(M, N, K, kcand, R)
+    if n < 0:
+        raise I2HError("i2h_workspace_bytes", int(n))
+    return int(n)
+
+
+def head(x, packed, S, ZS, W, kcand: int = 8, R: int = 32, k: int = 1, want_y: bool = False,
+         workspace: torch.Tensor | None = None, out=None):
+    """(idx int32 [M, k], val fp32 [M, k][, y bf16 [M, N]]) for one call of the head."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 2)
+    for t, nm in ((x, "x"), (packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    M, N, K = _head_shapes(x, packed, S, ZS)
+    if tuple(W.shape) != (N, K):
+        raise ValueError(f"W must have shape {(N, K)}, got {tuple(W.shape)}")
+    need = workspace_bytes(M, N, K, kcand, R)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    elif workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if out is None:
+        oi = torch.empty(M, k, dtype=torch.int32, device=x.device)
+        ov = torch.empty(M, k, dtype=torch.float32, device=x.device)
+    else:
+        oi, ov = out
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if want_y else None
+    _check("i2h_head", lib().i2h_head(_ptr(x), M, _ptr(packed), _ptr(S), _ptr(ZS), _ptr(W), _rows(W, "W"), N, K,
+                                      kcand, R, k, _ptr(oi), _ptr(ov), _ptr(y), _ptr(workspace),
+                                      workspace.numel(), _stream(x)))
+    return (oi, ov, y) if want_y else (oi, ov)

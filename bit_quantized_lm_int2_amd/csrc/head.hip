@@ -1,0 +1,94 @@
+// The whole head in one call, plus the library's status helpers.
+//
+// radiance_drafthead.py, _apply_head_int2: group sums of x, the coarse int2 pass with its block
+// candidates, the top-R selection, the exact rerank and the caller's argmax or top-k, in
+// stream order with no host synchronisation.
+#include "device_util.h"
+#include "host_util.h"
+
+namespace i2h {
+
+namespace {
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kAlign = 256;
+int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Workspace {
+  int64_t xs, cand_score, cand_idx, sel, exact, total;
+};
+
+Workspace layout(int64_t M, int64_t N, int64_t K, int kcand, int R) {
+  Workspace w;
+  const int64_t ncand = nblk_of(N) * kcand;
+  w.xs = 0;
+  w.cand_score = up(w.xs + M * (K / I2H_GROUP) * 4);
+  w.cand_idx = up(w.cand_score + M * ncand * 4);
+  w.sel = up(w.cand_idx + M * ncand * 4);
+  w.exact = up(w.sel + M * (int64_t)R * 4);
+  w.total = up(w.exact + M * (int64_t)R * 4);
+  return w;
+}
+
+}  // namespace
+
+int record_hip_error(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return I2H_ERR_HIP;
+}
+
+}  // namespace i2h
+
+extern "C" int i2h_version(void) { return 100; }
+
+extern "C" const char* i2h_strerror(int status) {
+  switch (status) {
+    case I2H_OK: return "ok";
+    case I2H_ERR_ARG: return "invalid argument (null pointer or bad value)";
+    case I2H_ERR_SHAPE: return "unsupported shape (M, N or K)";
+    case I2H_ERR_ALIGN: return "pointer or stride alignment not met";
+    case I2H_ERR_LIMIT: return "kcand, R or k outside the supported limits";
+    case I2H_ERR_WORKSPACE: return "workspace missing or too small";
+    case I2H_ERR_HIP: return "HIP launch failed (see i2h_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int i2h_last_hip_error(void) { return i2h::g_last_hip_error; }
+
+extern "C" int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R) {
+  if (M < 1 || N < 1 || i2h::check_k(K) != I2H_OK || i2h::nblk_of(N) > I2H_MAX_NBLK) return I2H_ERR_SHAPE;
+  if (kcand < 1 || kcand > I2H_MAX_KCAND || R < 1 || R > I2H_MAX_R) return I2H_ERR_LIMIT;
+  return i2h::layout(M, N, K, kcand, R).total;
+}
+
+extern "C" int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t* S,
+                        const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
+                        int kcand, int R, int k, int32_t* out_idx, float* out_val, uint16_t* y,
+                        void* workspace, int64_t ws_bytes, void* stream) {
+  using namespace i2h;
+  if (!x || !packed || !S || !ZS || !W || !out_idx || !out_val) return I2H_ERR_ARG;
+  const int64_t need = i2h_workspace_bytes(M, N, K, kcand, R);
+  if (need < 0) return (int)need;
+  if (k < 1 || k > R || (int64_t)R * kcand > 8192) return I2H_ERR_LIMIT;
+  if (!workspace || ws_bytes < need) return I2H_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return I2H_ERR_ALIGN;
+  if (ldw < K) return I2H_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 2) ||
+      !aligned(ZS, 2) || !aligned(out_idx, 4) || !aligned(out_val, 4) || (y && !aligned(y, 2)))
+    return I2H_ERR_ALIGN;
+  const Workspace w = layout(M, N, K, kcand, R);
+  char* base = static_cast<char*>(workspace);
+  float* xs = reinterpret_cast<float*>(base + w.xs);
+  float* cs = reinterpret_cast<float*>(base + w.cand_score);
+  int32_t* ci = reinterpret_cast<int32_t*>(base + w.cand_idx);
+  int32_t* sel = reinterpret_cast<int32_t*>(base + w.sel);
+  float* ex = reinterpret_cast<float*>(base + w.exact);
+  hipStream_t s = (hipStream_t)stream;
+  int st = xsum_launch(x, M, K, xs, s);
+  if (st == I2H_OK) st = coarse_launch(x, xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s);
+  if (st == I2H_OK) st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
+  if (st == I2H_OK) st = rerank_launch(x, M, W, ldw, N, K, sel, R, ex, s);
+  if (st == I2H_OK) st = finalize_launch(ex, sel, M, R, k, out_idx, out_val, s);
+  return st;
+}

@@ -1,0 +1,39 @@
+// Host-side helpers shared by the entry points of libi2h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "i2h.h"
+
+namespace i2h {
+
+// Records a failed HIP call for i2h_last_hip_error() and returns I2H_ERR_HIP.
+int record_hip_error(hipError_t e);
+
+// Checks the launch that was just enqueued.
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? I2H_OK : record_hip_error(e);
+}
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int check_k(int64_t K) {
+  return (K > 0 && K <= I2H_MAX_K && K % (4 * I2H_GROUP) == 0) ? I2H_OK : I2H_ERR_SHAPE;
+}
+
+inline int64_t nblk_of(int64_t N) { return (N + I2H_BLOCK_N - 1) / I2H_BLOCK_N; }
+
+// Entry points used by i2h_head (same checks and kernels as the exported calls).
+int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s);
+int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                  const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
+                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s);
+int select_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
+                  int kcand, int R, int32_t* sel, hipStream_t s);
+int rerank_launch(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
+                  int64_t K, const int32_t* sel, int R, float* exact, hipStream_t s);
+int finalize_launch(const float* exact, const int32_t* sel, int64_t M, int R, int k,
+                    int32_t* out_idx, float* out_val, hipStream_t s);
+
+}  // namespace i2h

@@ -1,0 +1,153 @@
+/*
+ * i2h: the 2-bit speculative-draft LM head on MI355X (gfx950).
+ *
+ * The head computes logits = x[M, K] @ W[K, N] from a weight stored as int2 codes with an
+ * asymmetric scale and zero point per (vocab row, group of 128 consecutive k), packed quarter-
+ * split, then keeps the best KCAND columns of every 64-column vocab block, reranks the best R of
+ * those exactly against the bf16 weight rows, and returns the argmax or the top-k of the
+ * reranked tokens. Source: the page "radiance_drafthead.py" (2-bit MTP draft head with an exact
+ * rerank); each entry point below names the part of it that defines the operation.
+ *
+ * Conventions for every call:
+ *   - Pointers are device pointers allocated by the caller; the library allocates, frees and
+ *     synchronises nothing and keeps no state between calls. Each call enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL is the legacy default stream) and returns at once.
+ *   - bf16 values are passed as uint16_t bit patterns. Matrices are row-major; `ld*` arguments
+ *     are row strides in elements.
+ *   - Arguments are checked before anything is enqueued. On an error nothing is enqueued and a
+ *     negative I2H_ERR_* code is returned. I2H_ERR_HIP means a HIP launch failed; the HIP error
+ *     code is then available from i2h_last_hip_error() on the calling thread.
+ *   - Shapes: G = 128 (quantisation group), BLOCK_N = 64 (candidate block), K a positive
+ *     multiple of 512 (four quarters of whole groups) and at most 16384, NBLK = ceil(N / 64).
+ *   - Alignment: x, W and packed must be 16-byte aligned, W's row stride a multiple of 8
+ *     elements; fp32/int32 arrays 4-byte aligned, bf16 arrays 2-byte aligned.
+ *   - Inputs must be finite (no NaN or inf in x or W).
+ */
+#ifndef I2H_H_
+#define I2H_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define I2H_API __attribute__((visibility("default")))
+
+#define I2H_OK 0
+#define I2H_ERR_ARG (-1)        /* null pointer or invalid non-shape argument */
+#define I2H_ERR_SHAPE (-2)      /* M, N or K outside the supported shapes */
+#define I2H_ERR_ALIGN (-3)      /* pointer or stride alignment not met */
+#define I2H_ERR_LIMIT (-4)      /* kcand, R or k outside their limits */
+#define I2H_ERR_WORKSPACE (-5)  /* workspace missing or smaller than i2h_workspace_bytes() */
+#define I2H_ERR_HIP (-6)        /* a HIP launch failed; see i2h_last_hip_error() */
+
+#define I2H_GROUP 128
+#define I2H_BLOCK_N 64
+#define I2H_MAX_K 16384
+#define I2H_MAX_KCAND 64
+#define I2H_MAX_R 1024
+#define I2H_MAX_NBLK 8192       /* N <= 524288 for the candidate selection */
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+I2H_API int i2h_version(void);
+
+/* Text for a status code; never NULL. */
+I2H_API const char* i2h_strerror(int status);
+
+/* hipError_t of the last I2H_ERR_HIP returned on the calling thread (0 if none). */
+I2H_API int i2h_last_hip_error(void);
+
+/*
+ * Sizes of the stored head for an [N, K] weight: packed bytes (N * K / 4) and the element count
+ * of each of S and ZS (N * K / 128). Host only.
+ */
+I2H_API int i2h_sizes(int64_t N, int64_t K, int64_t* packed_bytes, int64_t* scale_elems);
+
+/*
+ * Quantise and pack a bf16 head (radiance_drafthead.py, _quantize_head_now: asymmetric min/max
+ * at 2 bits per group; quarter-split packing; scale and zero premultiplied by the dequant bias).
+ *   W       bf16 [N, K], row stride ldw (>= K, multiple of 8); row n is vocab token n.
+ *   packed  u8 [N, K/4] (row stride K/4): byte j of a row holds the codes of k = j, Q+j, 2Q+j
+ *           and 3Q+j (Q = K/4) in bits 0-1, 2-3, 4-5 and 6-7.
+ *   S, ZS   bf16 [N, K/128] (row stride K/128): S = bf16(4 sc), ZS = bf16(4 sc + zp sc).
+ * Per group of 128 consecutive k: sc = max((hi - lo) / 3, 1e-8), zp = clamp(round(-lo / sc),
+ * 0, 3), q = clamp(round(w / sc + zp), 0, 3), all in IEEE fp32 with round-half-even and no
+ * fused multiply-add, so the result is bit-exact against an eager fp32 evaluation.
+ */
+I2H_API int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
+                     uint16_t* S, uint16_t* ZS, void* stream);
+
+/*
+ * Per-group sums of x (radiance_drafthead.py, _apply_head_int2: the fp32 group sums the coarse
+ * kernel uses for the zero point and the dequant bias).
+ *   x   bf16 [M, K] (row stride K);  xs  fp32 [M, K/128]: xs[m, g] = sum of x[m, 128g .. 128g+127].
+ */
+I2H_API int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void* stream);
+
+/*
+ * Coarse int2 logits and block candidates (radiance_drafthead.py, _draft_head_int2 and _emit):
+ *   c[m, n] = sum over groups g of S[n,g] * sum_{k in g} x[m,k] (1 + v[n,k]/4) - xs[m,g] ZS[n,g]
+ * with v the 2-bit code, accumulated in fp32. For every row m and block b of 64 columns, the
+ * kcand best columns (score descending, lower column first on equal scores) are written, best
+ * first, to slots b*kcand .. b*kcand+kcand-1 of
+ *   cand_score fp32 [M, NBLK*kcand] and cand_idx int32 [M, NBLK*kcand] (token index n);
+ * slots past a tail block's real columns get (-inf, -1).
+ *   x bf16 [M, K]; xs fp32 [M, K/128] from i2h_xsum; packed/S/ZS from i2h_pack.
+ *   y   optional bf16 [M, N] (row stride N): the coarse logits rounded to nearest-even; NULL to skip.
+ * Limits: M >= 1 (any size; rows are processed in chunks), 1 <= kcand <= 64.
+ */
+I2H_API int i2h_coarse_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                            const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
+                            float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream);
+
+/*
+ * Top-R selection over the block candidates (radiance_drafthead.py, _apply_head_int2: the
+ * RERANK best block candidates of each row are the ones rescored exactly).
+ *   cand_score/cand_idx as written by i2h_coarse_topk: [M, nblk*kcand], each block's kcand
+ *   entries best first. sel int32 [M, R] receives, best first, the R best candidates by score
+ *   descending then token index ascending; entries with index < 0 never count, and if a row
+ *   has fewer than R valid candidates the remaining sel entries are -1.
+ * Limits: 1 <= nblk <= 8192, 1 <= kcand <= 64, 1 <= R <= 1024.
+ */
+I2H_API int i2h_select(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
+                       int kcand, int R, int32_t* sel, void* stream);
+
+/*
+ * Exact rerank (radiance_drafthead.py, _rerank_exact): exact[m, j] = sum_k x[m,k] W[sel[m,j], k]
+ * over the bf16 weight row of the selected token, accumulated in fp32.
+ *   x bf16 [M, K]; W bf16 [N, K] (row stride ldw); sel int32 [M, R]; exact fp32 [M, R].
+ * A sel entry outside [0, N) gives -inf.
+ */
+I2H_API int i2h_rerank(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
+                       int64_t K, const int32_t* sel, int R, float* exact, void* stream);
+
+/*
+ * Final choice among the reranked tokens (radiance_drafthead.py, module docstring: the argmax
+ * caller wins on the exact scores; _apply_head_int2: a top-k caller draws only from the
+ * reranked tokens). out_idx int32 [M, k] and out_val fp32 [M, k] receive the k best (exact
+ * score descending, token index ascending); k = 1 is the argmax. Entries with sel < 0 never
+ * count; missing places get (-1, -inf). Limits: 1 <= R <= 1024, 1 <= k <= R.
+ */
+I2H_API int i2h_finalize(const float* exact, const int32_t* sel, int64_t M, int R, int k,
+                         int32_t* out_idx, float* out_val, void* stream);
+
+/* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
+I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);
+
+/*
+ * One call of the head: i2h_xsum, i2h_coarse_topk, i2h_select, i2h_rerank and i2h_finalize in
+ * stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
+ * aligned, caller-owned, contents undefined afterwards). Arguments as in those calls; y may be
+ * NULL. The limits of every step apply.
+ */
+I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t* S,
+                     const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
+                     int kcand, int R, int k, int32_t* out_idx, float* out_val, uint16_t* y,
+                     void* workspace, int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* I2H_H_ */

@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status codes before enqueuing anything. No call
+here reaches a kernel launch, so these run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_lm_int2_amd as i2h
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "i2h.h")
+
+OK, ARG, SHAPE, ALIGN, LIMIT, WS = 0, -1, -2, -3, -4, -5
+P = 0x10000          # a 64 KiB-aligned fake device address; never dereferenced on these paths
+ODD = 0x10001
+
+
+def declared():
+    text = open(HEADER).read()
+    return re.findall(r"I2H_API\s+[\w\s\*]+?\b(i2h_\w+)\s*\(", text)
+
+
+def test_header_declares_the_entry_points():
+    names = set(declared())
+    want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
+            "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
+            "i2h_head"}
+    assert names == want
+
+
+def test_library_exports_every_declared_symbol():
+    lib = i2h.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+    assert lib.i2h_version() >= 100
+
+
+def test_strerror_and_last_error():
+    lib = i2h.lib()
+    for code in (OK, ARG, SHAPE, ALIGN, LIMIT, WS, -6, -99):
+        assert lib.i2h_strerror(code)
+    assert lib.i2h_last_hip_error() == 0
+
+
+def test_sizes():
+    assert i2h.sizes(124160, 5120) == (158_924_800, 4_966_400)
+    assert i2h.sizes(4096, 512) == (4096 * 128, 4096 * 4)
+    lib = i2h.lib()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.i2h_sizes(10, 640, ctypes.byref(a), ctypes.byref(b)) == SHAPE
+    assert lib.i2h_sizes(0, 512, ctypes.byref(a), ctypes.byref(b)) == SHAPE
+    assert lib.i2h_sizes(10, 512, None, ctypes.byref(b)) == ARG
+
+
+def test_workspace_bytes():
+    lib = i2h.lib()
+    n = lib.i2h_workspace_bytes(16, 124160, 5120, 8, 32)
+    # xs + candidates (score + index) + sel + exact, each rounded up to 256 bytes
+    assert n >= 16 * 40 * 4 + 2 * 16 * 1940 * 8 * 4 + 2 * 16 * 32 * 4
+    assert n % 256 == 0
+    assert lib.i2h_workspace_bytes(16, 124160, 5000, 8, 32) == SHAPE
+    assert lib.i2h_workspace_bytes(16, 124160, 5120, 0, 32) == LIMIT
+    assert lib.i2h_workspace_bytes(16, 124160, 5120, 8, 2000) == LIMIT
+    assert lib.i2h_workspace_bytes(16, 64 * 8193, 5120, 8, 32) == SHAPE
+
+
+def test_pack_rejections():
+    lib = i2h.lib()
+    assert lib.i2h_pack(None, 512, 4, 512, P, P, P, None) == ARG
+    assert lib.i2h_pack(P, 512, 4, 500, P, P, P, None) == SHAPE
+    assert lib.i2h_pack(P, 256, 4, 512, P, P, P, None) == SHAPE      # ldw < K
+    assert lib.i2h_pack(P, 516, 4, 512, P, P, P, None) == ALIGN      # ldw % 8
+    assert lib.i2h_pack(ODD + 1, 512, 4, 512, P, P, P, None) == ALIGN
+    assert lib.i2h_pack(P, 512, 0, 512, P, P, P, None) == SHAPE
+
+
+def test_coarse_select_rerank_finalize_rejections():
+    lib = i2h.lib()
+    c = lib.i2h_coarse_topk
+    assert c(None, P, 1, P, P, P, 4096, 512, 8, P, P, None, None) == ARG
+    assert c(P, P, 0, P, P, P, 4096, 512, 8, P, P, None, None) == SHAPE
+    assert c(P, P, 1, P, P, P, 4096, 768, 8, P, P, None, None) == SHAPE
+    assert c(P, P, 1, P, P, P, 4096, 512, 0, P, P, None, None) == LIMIT
+    assert c(P, P, 1, P, P, P, 4096, 512, 65, P, P, None, None) == LIMIT
+    assert c(P + 8, P, 1, P, P, P, 4096, 512, 8, P, P, None, None) == ALIGN
+    assert c(P, P, 1, P, P, P, 4096, 512, 8, P, P, ODD, None) == ALIGN
+    s = lib.i2h_select
+    assert s(P, P, 1, 64, 8, 0, P, None) == LIMIT
+    assert s(P, P, 1, 64, 8, 1025, P, None) == LIMIT
+    assert s(P, P, 1, 64, 64, 256, P, None) == LIMIT               # R * kcand > 8192
+    assert s(P, P, 1, 8193, 8, 32, P, None) == SHAPE
+    assert s(P, P, 1, 64, 8, 32, None, None) == ARG
+    r = lib.i2h_rerank
+    assert r(P, 1, P, 512, 4096, 512, P, 0, P, None) == LIMIT
+    assert r(P, 1, P, 500, 4096, 512, P, 32, P, None) == SHAPE
+    assert r(P, 1, P, 516, 4096, 512, P, 32, P, None) == ALIGN
+    assert r(P, 1, None, 512, 4096, 512, P, 32, P, None) == ARG
+    f = lib.i2h_finalize
+    assert f(P, P, 1, 32, 33, P, P, None) == LIMIT
+    assert f(P, P, 1, 32, 0, P, P, None) == LIMIT
+    assert f(P, P, 0, 32, 1, P, P, None) == SHAPE
+    assert f(P, P, 1, 32, 1, P + 2, P, None) == ALIGN
+    x = lib.i2h_xsum
+    assert x(P, 1, 1000, P, None) == SHAPE
+    assert x(P + 4, 1, 512, P, None) == ALIGN
+
+
+def test_head_rejections():
+    lib = i2h.lib()
+    h = lib.i2h_head
+    need = lib.i2h_workspace_bytes(1, 4096, 512, 8, 32)
+    args = [P, 1, P, P, P, P, 512, 4096, 512, 8, 32, 1, P, P, None, P, need, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["x", "M", "packed", "S", "ZS", "W", "ldw", "N", "K", "kcand", "R", "k", "oi", "ov",
+                 "y", "ws", "wsb", "stream"]
+        for k_, v in kw.items():
+            a[names.index(k_)] = v
+        return h(*a)
+
+    assert call(ws=None) == WS
+    assert call(wsb=need - 1) == WS
+    assert call(ws=P + 16) == ALIGN
+    assert call(k=33) == LIMIT
+    assert call(kcand=64, R=256, wsb=1 << 40) == LIMIT
+    assert call(K=640) == SHAPE
+    assert call(W=None) == ARG
+    assert call(ldw=256) == SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(i2h, "_lib", None)
+    monkeypatch.setattr(i2h, "_LIB_PATH", "/nonexistent/libi2h.so")
+    with pytest.raises(ImportError):
+        i2h.lib()

@@ -1,0 +1,304 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Inputs come from synth_inputs; expected values come only from oracle/. Rules in parity_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity_util as pu
+import synth_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def i2h():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import bit_quantized_lm_int2_amd as lib
+    lib.lib()  # the HIP library must load; there is no fallback
+    return lib
+
+
+DEV = "cuda:0"
+
+
+def dev_bf16(b):
+    return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def host(t):
+    if t.dtype == torch.bfloat16:
+        return si.bits(t)
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# pack: bit-exact
+# ---------------------------------------------------------------------------------------------
+def degenerate_rows(K):
+    rows = [np.full(K, 0x3F00, np.uint16),              # constant 0.5
+            np.full(K, 0xBF00, np.uint16),              # constant -0.5
+            np.zeros(K, np.uint16),                     # all zero
+            (np.arange(K) % 7 + 0x3C00).astype(np.uint16),   # all positive (lo > 0)
+            (np.arange(K) % 5 + 0xBC00).astype(np.uint16),   # all negative (hi < 0)
+            np.where(np.arange(K) % 2 == 0, 0x7E00, 0xFE00).astype(np.uint16),  # huge +-2^125
+            np.where(np.arange(K) % 3 == 0, 0x0001, 0x8001).astype(np.uint16)]  # subnormal
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("N,K", [(4096, 512), (1000, 1024), (37, 5120), (5, 2048)])
+def test_pack_bit_exact(i2h, N, K):
+    say(f"pack N={N} K={K}")
+    W = si.bits(si.gen_weight(N, K, seed=100 + N))
+    W = np.concatenate([W, degenerate_rows(K)])
+    p, S, ZS = i2h.pack(dev_bf16(W))
+    po, So, ZSo = oracle.pack(W)
+    assert np.array_equal(host(p), po)
+    assert np.array_equal(host(S), So)
+    assert np.array_equal(host(ZS), ZSo)
+
+
+def test_pack_strided_rows(i2h):
+    K = 1024
+    wide = si.gen_weight(300, K + 64, seed=7).to(DEV)
+    W = wide[:, 32:32 + K]   # row stride K + 64, 64-byte offset
+    p, S, ZS = i2h.pack(W)
+    po, So, ZSo = oracle.pack(si.bits(W))
+    assert np.array_equal(host(p), po) and np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+
+
+def test_pack_exact_grid_head(i2h):
+    from test_oracle_pins import grid_head
+    Wb, q, zp, sc = grid_head(500, 1024, 21)
+    p, S, ZS = i2h.pack(dev_bf16(Wb))
+    assert np.array_equal(host(p), oracle.pack_quarter_split(q.astype(np.uint8)))
+    assert np.array_equal(oracle.bf16_to_f32(host(S)).astype(np.float64), 4 * sc)
+    assert np.array_equal(oracle.bf16_to_f32(host(ZS)).astype(np.float64), (4 + zp) * sc)
+
+
+# ---------------------------------------------------------------------------------------------
+# xsum
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K", [(1, 512), (72, 5120), (3, 16384)])
+def test_xsum(i2h, M, K):
+    xb = si.bits(si.gen_x(M, K, outliers=8, seed=3))
+    xs = host(i2h.xsum(dev_bf16(xb)))
+    want = oracle.group_sums(xb)
+    absx = np.abs(oracle.bf16_to_f32(xb).astype(np.float64)).reshape(M, K // 128, 128).sum(2)
+    assert np.all(np.abs(xs - want) <= 128 * 2.0 ** -24 * absx + 1e-30)
+
+
+# ---------------------------------------------------------------------------------------------
+# selection and finalize on identical inputs: bit-exact, ties included
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,kc,R,grid", [(1, 124160, 8, 32, 0), (5, 4096, 8, 32, 4), (3, 248320, 8, 32, 0),
+                                           (4, 643, 8, 100, 2), (2, 5000, 1, 1, 1), (2, 9000, 64, 128, 8),
+                                           (3, 4096, 8, 1024, 0), (1, 1000, 8, 32, 0.25)])
+def test_select_bit_exact(i2h, M, N, kc, R, grid):
+    say(f"select M={M} N={N} kc={kc} R={R}")
+    sc = si.gen_scores(M, N, seed=N + R).numpy()
+    if grid:
+        sc = (np.round(sc * grid) / grid).astype(np.float32)  # many exact ties
+    cs, ci = oracle.block_emit(sc.astype(np.float64), kc)
+    want = oracle.select_top_r(cs, ci, R)
+    got = i2h.select(torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV), kc, R)
+    assert np.array_equal(host(got), want)
+
+
+def test_select_all_equal_scores(i2h):
+    cs, ci = oracle.block_emit(np.zeros((2, 124160)), 8)
+    want = oracle.select_top_r(cs, ci, 32)
+    got = i2h.select(torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV), 8, 32)
+    assert np.array_equal(host(got), want)
+
+
+@pytest.mark.parametrize("M,R,k,grid", [(3, 32, 1, 0), (3, 32, 16, 2), (2, 100, 100, 1), (4, 1024, 16, 4),
+                                        (1, 1, 1, 0)])
+def test_finalize_bit_exact(i2h, M, R, k, grid):
+    e = si.gen_scores(M, R, seed=R + k).numpy()
+    if grid:
+        e = (np.round(e * grid) / grid).astype(np.float32)
+    sel = si.gen_rows(M, R, 300000, seed=R).numpy()
+    sel[0, R // 2] = -1
+    oi, ov = oracle.finalize(e.astype(np.float64), sel, k)
+    gi, gv = i2h.finalize(torch.from_numpy(e).to(DEV), torch.from_numpy(sel).to(DEV), k)
+    assert np.array_equal(host(gi), oi)
+    assert np.array_equal(host(gv).astype(np.float64), ov)
+
+
+# ---------------------------------------------------------------------------------------------
+# rerank
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,R", [(1, 4096, 512, 32), (16, 20000, 5120, 32), (3, 300, 16384, 7)])
+def test_rerank(i2h, M, N, K, R):
+    xb = si.bits(si.gen_x(M, K, outliers=8, seed=5))
+    Wb = si.bits(si.gen_weight(N, K, seed=6))
+    sel = si.gen_rows(M, R, N, seed=8).numpy()
+    sel[0, 0] = -1
+    sel[-1, -1] = N + 5   # out of range: -inf
+    ex = host(i2h.rerank(dev_bf16(xb), dev_bf16(Wb), torch.from_numpy(sel).to(DEV)))
+    assert np.isneginf(ex[0, 0]) and np.isneginf(ex[-1, -1])
+    s2 = sel.copy()
+    s2[-1, -1] = -1
+    pu.check_rerank(ex, xb, Wb, s2)
+
+
+# ---------------------------------------------------------------------------------------------
+# coarse pass on a head whose every sum is exact in fp32: the whole path is bit-exact,
+# so the tie rules of the emit, selection and finalize are checked exactly
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,kc,R,k", [(3, 4096, 8, 32, 16), (17, 643, 8, 40, 5), (1, 2000, 64, 128, 1),
+                                        (40, 1000, 3, 32, 16)])
+def test_exact_arithmetic_head_bit_exact(i2h, M, N, kc, R, k):
+    from test_oracle_pins import grid_head
+    K = 512
+    Wb, q, zp, sc = grid_head(N, K, 31)
+    # same sc = 2^-4 everywhere keeps every partial sum exact in fp32
+    qg = q.reshape(N, K // 128, 128)
+    w = (2.0 ** -4 * (qg - zp[:, :, None])).reshape(N, K)
+    Wb = oracle.f32_to_bf16(w.astype(np.float32))
+    rng = np.random.default_rng(M)
+    xf = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    xf[0] = 0.0                                   # a row of pure ties
+    xb = oracle.f32_to_bf16(xf)
+    x, W = dev_bf16(xb), dev_bf16(Wb)
+    p, S, ZS = i2h.pack(W)
+    xs = i2h.xsum(x)
+    cs, ci, y = i2h.coarse_topk(x, xs, p, S, ZS, kcand=kc, want_y=True)
+    sel = i2h.select(cs, ci, kc, R)
+    ex = i2h.rerank(x, W, sel)
+    oi, ov = i2h.finalize(ex, sel, k)
+    po, So, ZSo = oracle.pack(Wb)
+    res = oracle.head(xb, Wb, po, So, ZSo, kcand=kc, R=R, k=k)
+    assert np.array_equal(host(y), oracle.f32_to_bf16(res["coarse"].astype(np.float32)))
+    assert np.array_equal(host(ci), res["cand_idx"])
+    assert np.array_equal(host(cs).astype(np.float64), res["cand_score"])
+    assert np.array_equal(host(sel), res["sel"])
+    assert np.array_equal(host(ex).astype(np.float64), res["exact"])
+    assert np.array_equal(host(oi), res["idx"])
+    assert np.array_equal(host(ov).astype(np.float64), res["val"])
+
+
+# ---------------------------------------------------------------------------------------------
+# end to end on Gaussian heads, tolerance rules
+# ---------------------------------------------------------------------------------------------
+def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, rows=None):
+    """GPU step by step and fused, against the oracle; rows: subset of rows the oracle checks."""
+    x, W = dev_bf16(xb), dev_bf16(Wb)
+    p, S, ZS = i2h.pack(W)
+    xs = i2h.xsum(x)
+    cs, ci, y = i2h.coarse_topk(x, xs, p, S, ZS, kcand=kc, want_y=True)
+    sel = i2h.select(cs, ci, kc, R)
+    ex = i2h.rerank(x, W, sel)
+    oi, ov = i2h.finalize(ex, sel, k)
+    hi, hv = i2h.head(x, p, S, ZS, W, kcand=kc, R=R, k=k)
+    torch.cuda.synchronize()
+    assert torch.equal(hi, oi) and torch.equal(hv, ov), "fused call differs from the steps"
+    rows = np.arange(xb.shape[0]) if rows is None else np.asarray(rows)
+    if packed_o is None:
+        packed_o = oracle.pack(Wb)
+        assert np.array_equal(host(p), packed_o[0])
+        assert np.array_equal(host(S), packed_o[1]) and np.array_equal(host(ZS), packed_o[2])
+    po, So, ZSo = packed_o
+    xr = xb[rows]
+    res = oracle.head(xr, Wb, po, So, ZSo, kcand=kc, R=R, k=k, coarse=None if coarse_o is None else coarse_o[rows])
+    c = res["coarse"]
+    yh, csh, cih = host(y)[rows], host(cs)[rows], host(ci)[rows]
+    ok = cih >= 0
+    # Y is the bf16 rounding of the same fp32 logits the candidates carry
+    assert np.array_equal(np.take_along_axis(yh, np.where(ok, cih, 0).astype(np.int64), axis=1)[ok],
+                          oracle.f32_to_bf16(csh[ok]))
+    err = pu.check_coarse_values(yh, c)
+    err32 = pu.coarse_fp32_error(csh, cih, c)
+    cand_ex, cand_tight = pu.check_candidates(csh, cih, c, kc)
+    g_sel = host(sel)[rows]
+    sel_ex, sel_tight = pu.check_selection(g_sel, res["sel"], c)
+    e_g, rerr = pu.check_rerank(host(ex)[rows], xr, Wb, g_sel)
+    fin_ex = pu.check_final(host(oi)[rows], host(ov)[rows], e_g, g_sel, k)
+    match, sel_excused, tie_excused = pu.final_vs_oracle(host(oi)[rows], res, g_sel, e_g)
+    say(f"  rows={len(rows)} coarse_err(bf16 Y)={err:.2e} coarse_err(fp32)={err32:.2e} cand_excused={cand_ex} (tight {cand_tight}) "
+        f"sel_excused_rows={sel_ex} (tight {sel_tight}) rerank_err={rerr:.2e} "
+        f"final match={match} sel_excused={sel_excused} tie_excused={tie_excused + fin_ex}")
+    return dict(match=match, places=len(rows) * k, res=res, gpu_idx=host(oi)[rows])
+
+
+@pytest.mark.parametrize("M,N,K,kc,R,k", [
+    (1, 4096, 512, 8, 32, 1),      # the tiny head
+    (3, 4133, 512, 8, 32, 16),     # ragged tail block of 37 columns
+    (17, 643, 1024, 8, 100, 16),   # tail block with 3 < kcand columns; R above the valid count
+    (33, 3000, 5120, 8, 32, 1),    # three m-tiles of 16 rows, one partly filled
+    (64, 2048, 2048, 16, 64, 16),
+    (72, 1500, 512, 8, 32, 16),    # the 72-row band
+    (130, 700, 512, 4, 16, 4),     # more rows than one launch holds
+    (5, 4096, 16384, 8, 32, 1),    # largest K
+    (2, 2000, 512, 1, 1, 1),       # one candidate per block, one reranked token
+])
+def test_head_parity(i2h, M, N, K, kc, R, k):
+    say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
+    xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=M + K))
+    Wb = si.bits(si.gen_weight(N, K, seed=N + K))
+    run_and_check(i2h, xb, Wb, kc=kc, R=R, k=k)
+
+
+def test_head_zero_rows(i2h):
+    """x rows of zeros: every score ties, the tie rules decide (lowest indices win)."""
+    K, N = 512, 4096
+    xb = si.bits(si.gen_x(4, K, seed=9))
+    xb[1] = 0
+    xb[3] = 0x8000  # negative zeros
+    Wb = si.bits(si.gen_weight(N, K, seed=10))
+    out = run_and_check(i2h, xb, Wb, k=16)
+    want = [b * 64 + j for b in range(4) for j in range(8)][:16]
+    assert list(out["gpu_idx"][1]) == want and list(out["gpu_idx"][3]) == want
+
+
+# ---------------------------------------------------------------------------------------------
+# full sizes: one rank's 124160-row vocab slice at M = 1, 16, 64, and the full 248320-row vocab
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def slice_head():
+    cfg = si.WORKLOADS["draft_band_m64_k5120_n124160"]
+    say("generating the 124160 x 5120 head")
+    Wb = si.bits(si.gen_weight(cfg["N"], cfg["K"]))
+    xb = si.bits(si.gen_x(64, cfg["K"], outliers=cfg["outliers"]))
+    packed_o = oracle.pack(Wb)
+    say("oracle coarse, 64 rows")
+    coarse_o = oracle.coarse_logits(xb, *packed_o)
+    return xb, Wb, packed_o, coarse_o
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_vocab_slice_full_size(i2h, slice_head, M):
+    xb, Wb, packed_o, coarse_o = slice_head
+    say(f"vocab slice M={M}")
+    p, S, ZS = i2h.pack(dev_bf16(Wb))
+    assert np.array_equal(host(p), packed_o[0])
+    assert np.array_equal(host(S), packed_o[1]) and np.array_equal(host(ZS), packed_o[2])
+    out = run_and_check(i2h, xb[:M], Wb, packed_o=packed_o, coarse_o=coarse_o[:M])
+    say(f"  argmax match vs oracle: {out['match']}/{out['places']}")
+
+
+def test_full_vocab_top16(i2h):
+    cfg = si.WORKLOADS["full_vocab_top16_k5120_n248320"]
+    N, K = cfg["N"], cfg["K"]
+    say("generating the 248320 x 5120 head")
+    Wb = si.bits(si.gen_weight(N, K))
+    xb = si.bits(si.gen_x(72, K, outliers=cfg["outliers"]))
+    rows = [0, 31, 71]
+    # the pack is checked bit-exactly on sampled vocab rows
+    p, S, ZS = i2h.pack(dev_bf16(Wb))
+    pick = np.sort(np.random.default_rng(0).choice(N, 4096, replace=False))
+    po, So, ZSo = oracle.pack(Wb[pick])
+    assert np.array_equal(host(p)[pick], po)
+    assert np.array_equal(host(S)[pick], So) and np.array_equal(host(ZS)[pick], ZSo)
+    say("oracle on sampled rows")
+    packed_o = oracle.pack(Wb)
+    out = run_and_check(i2h, xb, Wb, k=16, packed_o=packed_o, rows=rows)
+    say(f"  top-16 match vs oracle: {out['match']}/{out['places']}")
