@@ -187,6 +187,245 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Small-M band (M <= 16): one m-tile, HBM-bound. Differences from coarse_kernel:
+//   * the block's S and ZS rows (contiguous in memory) and, when it fits, x itself are staged
+//     in LDS once per workgroup, so the K loop issues no small scattered loads;
+//   * the packed stream is prefetched two 128-byte spans ahead;
+//   * quarters 0-2 are dequantised with a mask alone. The code bits of quarter t of the low
+//     byte of each bf16 half sit at mantissa bits 2t, 2t+1, so (d & (3 << 2t)) | 0x3F80 reads as
+//     1 + v/D with D = 128, 32, 8 for t = 0, 1, 2 (quarter 3 keeps the shift, D = 4). With
+//     f = D/4 the group's dot P' = sum x (1 + v/D) = xs + dot/D gives
+//       S P - xs ZS = (f S) P' - xs ((f - 1) S + ZS),  P = xs + dot/4,
+//     so the bias change folds into the per-group scale and zero on the accumulator; f S and
+//     (f - 1) S + ZS are exact in fp32 (at most 13 significant bits each). The high byte of each
+//     half is brought down by one shift shared by the four quarters. 12 VALU ops per 16 weights.
+//   * only the accumulator rows that can hold a real row are scaled.
+// ---------------------------------------------------------------------------------------------
+// d0/d1: four packed bytes each. Raw bytes [b0 b1 b2 b3] give weights in k order (0, 2, 1, 3);
+// byte-paired dwords [b0 b2 b1 b3] give them in natural order.
+template <int T>
+__device__ __forceinline__ bf16x8 dequant8_mask(uint32_t d0, uint32_t d1) {
+  constexpr uint32_t kOne = 0x3F803F80u;
+  u32x4 r;
+  if constexpr (T < 3) {
+    constexpr uint32_t m = 0x00030003u << (2 * T);
+    r[0] = (d0 & m) | kOne;
+    r[1] = ((d0 >> 8) & m) | kOne;
+    r[2] = (d1 & m) | kOne;
+    r[3] = ((d1 >> 8) & m) | kOne;
+  } else {
+    r[0] = ((d0 >> 1) & 0x00600060u) | kOne;
+    r[1] = ((d0 >> 9) & 0x00600060u) | kOne;
+    r[2] = ((d1 >> 1) & 0x00600060u) | kOne;
+    r[3] = ((d1 >> 9) & 0x00600060u) | kOne;
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+constexpr float kBiasF[4] = {32.f, 8.f, 2.f, 1.f};  // D/4 for quarters 0..3
+
+// LDS footprint of coarse_small_kernel in bytes.
+__host__ __device__ constexpr size_t small_lds_bytes(int K, int xrows) {
+  return (size_t)64 * (K / kGroup) * 4 + (size_t)(K / kGroup) * 16 * 4 + (size_t)16 * kBlockN * 4 +
+         (size_t)xrows * K * 2;
+}
+
+template <int MAXR, bool XLDS>
+__global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+  constexpr int RR = MAXR < 4 ? MAXR : 4;  // accumulator rows per lane that can be real
+  extern __shared__ __align__(16) uint32_t lds[];
+  const int Q = K >> 2, NG = Q / kGroup, KG = K / kGroup;
+  uint32_t* sz = lds;                                      // [64][KG]: S | ZS << 16
+  float* xsT = reinterpret_cast<float*>(sz + 64 * KG);     // [KG][16]
+  float* cbuf = xsT + KG * 16;                             // [16][64]
+  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + 16 * kBlockN);  // [MAXR][K] when XLDS
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, h = lane >> 4;
+  const int b = blockIdx.x, n0 = b * kBlockN;
+  const int n = n0 + wave * 16 + col;
+  const bool nvalid = n < N;
+
+  // the first two 128-byte spans of the packed stream are requested before the staging below
+  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + 32 * h;
+  u32x4 pa0 = ld16(prow), pa1 = ld16(prow + 16);
+  const int g1 = NG > 1 ? 1 : 0;
+  u32x4 pb0 = ld16(prow + g1 * kGroup), pb1 = ld16(prow + g1 * kGroup + 16);
+
+  // stage S/ZS of rows n0 .. n0+63 (contiguous in memory), zero past N; all loads first
+  constexpr int kSzUnits = 4;  // 16-byte units per thread: 64 * KG / 8 <= 1024 for KG <= 128
+  const int tot = (N - n0 < kBlockN ? N - n0 : kBlockN) * KG;
+  const uint16_t* Sb = S + (int64_t)n0 * KG;
+  const uint16_t* Zb = ZS + (int64_t)n0 * KG;
+  u32x4 sv[kSzUnits], zv[kSzUnits];
+#pragma unroll
+  for (int i = 0; i < kSzUnits; ++i) {
+    const int e0 = (tid + i * kCoarseThreads) * 8;
+    sv[i] = u32x4{0u, 0u, 0u, 0u};
+    zv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (e0 + 8 <= tot) {
+      sv[i] = ld16(Sb + e0);
+      zv[i] = ld16(Zb + e0);
+    } else if (e0 < tot) {
+      for (int j = 0; j < 8; ++j)
+        if (e0 + j < tot) {
+          sv[i][j >> 1] |= (uint32_t)Sb[e0 + j] << (16 * (j & 1));
+          zv[i][j >> 1] |= (uint32_t)Zb[e0 + j] << (16 * (j & 1));
+        }
+    }
+  }
+  // x rows, each group of four k stored as (0, 2, 1, 3): the order in which the mask dequant of a
+  // raw packed dword yields its weights, so the packed bytes need no permute
+  const int xunits = XLDS ? M * (K / 8) : 0;
+  for (int u = tid; u < xunits; u += kCoarseThreads) {
+    const u32x4 v = ld16(x + 8 * u);
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+    *reinterpret_cast<u32x4*>(xl + 8 * u) = o;
+  }
+  if (xs != nullptr) {
+    for (int i = tid; i < KG * 16; i += kCoarseThreads) {
+      const int g = i >> 4, m = i & 15;
+      xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kSzUnits; ++i) {
+    const int e0 = (tid + i * kCoarseThreads) * 8;
+    if (e0 < kBlockN * KG) {
+      u32x4 lo, hi;
+      lo[0] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x07060302u);
+      lo[2] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x05040100u);
+      lo[3] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x07060302u);
+      hi[0] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x05040100u);
+      hi[1] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x07060302u);
+      hi[2] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x05040100u);
+      hi[3] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x07060302u);
+      *reinterpret_cast<u32x4*>(sz + e0) = lo;
+      *reinterpret_cast<u32x4*>(sz + e0 + 4) = hi;
+    }
+  }
+  __syncthreads();
+  if (xs == nullptr) {
+    // group sums from the LDS copy of x (only launched so with x in LDS): one thread per group
+    for (int i = tid; i < KG * 16; i += kCoarseThreads) {
+      const int g = i >> 4, m = i & 15;
+      float sm = 0.f;
+      if (m < M) {
+        const uint16_t* xg = xl + m * K + g * kGroup;
+#pragma unroll
+        for (int j = 0; j < kGroup; j += 8) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xg + j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm += bf16_lo(v[e]) + bf16_hi(v[e]);
+        }
+      }
+      xsT[i] = sm;
+    }
+    __syncthreads();
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t* szr = sz + (wave * 16 + col) * KG;
+  const bool arow = col < M;  // this lane feeds a real row of x to the A operand
+
+  auto body = [&](int gb, const u32x4& c0, const u32x4& c1) {
+    uint32_t dw[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dw[i] = XLDS ? c0[i] : pair_bytes(c0[i]);
+      dw[4 + i] = XLDS ? c1[i] : pair_bytes(c1[i]);
+    }
+    f32x4 p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) p[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        bf16x8 bw;
+        if (t == 0) bw = dequant8_mask<0>(dw[2 * s], dw[2 * s + 1]);
+        else if (t == 1) bw = dequant8_mask<1>(dw[2 * s], dw[2 * s + 1]);
+        else if (t == 2) bw = dequant8_mask<2>(dw[2 * s], dw[2 * s + 1]);
+        else bw = dequant8_mask<3>(dw[2 * s], dw[2 * s + 1]);
+        const int k0 = t * Q + gb * kGroup + 32 * h + 8 * s;
+        u32x4 a = {0u, 0u, 0u, 0u};
+        if (arow) {
+          if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xl + col * K + k0);
+          else a = ld16(x + (int64_t)col * K + k0);
+        }
+        p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int gi = t * NG + gb;
+      const uint32_t w = szr[gi];
+      const float sv = __uint_as_float(w << 16);
+      const float zv = __uint_as_float(w & 0xffff0000u);
+      const float s2 = kBiasF[t] * sv;
+      const float z2 = fmaf(kBiasF[t] - 1.f, sv, zv);
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
+#pragma unroll
+      for (int r = 0; r < RR; ++r) {
+        const float a = fmaf(s2, p[t][r], acc[r]);
+        acc[r] = fmaf(-xv[r], z2, a);
+      }
+    }
+  };
+
+  for (int gb = 0; gb < NG; gb += 2) {
+    {
+      const u32x4 c0 = pa0, c1 = pa1;
+      const int nx = gb + 2 < NG ? gb + 2 : NG - 1;
+      pa0 = ld16(prow + nx * kGroup);
+      pa1 = ld16(prow + nx * kGroup + 16);
+      body(gb, c0, c1);
+    }
+    if (gb + 1 < NG) {
+      const u32x4 c0 = pb0, c1 = pb1;
+      const int nx = gb + 3 < NG ? gb + 3 : NG - 1;
+      pb0 = ld16(prow + nx * kGroup);
+      pb1 = ld16(prow + nx * kGroup + 16);
+      body(gb + 1, c0, c1);
+    }
+  }
+
+  // acc[r] is c[m = 4 h + r][n]
+  if (y != nullptr && nvalid) {
+#pragma unroll
+    for (int r = 0; r < RR; ++r) {
+      const int m = 4 * h + r;
+      if (m < M) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RR; ++r) cbuf[(4 * h + r) * kBlockN + wave * 16 + col] = nvalid ? acc[r] : -__builtin_inff();
+  __syncthreads();
+
+  const int64_t ld = (int64_t)nblk * kc;
+  for (int m = wave; m < M; m += kCoarseThreads / kWave) {
+    float v = cbuf[m * kBlockN + lane];
+    int c = lane;
+    wave_sort_desc(v, c, lane);
+    if (lane < kc) {
+      const int tok = b * kBlockN + c;
+      const bool ok = tok < N;
+      const int64_t at = (int64_t)m * ld + (int64_t)b * kc + lane;
+      cand_score[at] = ok ? v : -__builtin_inff();
+      cand_idx[at] = ok ? tok : -1;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                    float* __restrict__ xs) {
   const int KG = K / kGroup;
@@ -212,6 +451,36 @@ int launch_coarse(const uint16_t* x, const float* xs, int M, const uint8_t* pack
   return check_launch();
 }
 
+template <int MAXR, bool XLDS>
+int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  const int nblk = (int)nblk_of(N);
+  const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
+  hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
+                     packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  return check_launch();
+}
+
+}  // namespace
+
+// True when the coarse kernel for these sizes keeps x in LDS and can sum its groups itself.
+bool coarse_sums_x(int64_t M, int64_t K) {
+  if (M < 1 || check_k(K) != I2H_OK) return false;
+  return (M == 1 && small_lds_bytes((int)K, 1) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4) <= 65536);
+}
+
+namespace {
+
+int small_band(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+               const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  if (M == 1 && small_lds_bytes(K, 1) <= 65536)
+    return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  if (M <= 4 && small_lds_bytes(K, 4) <= 65536)
+    return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  if (M <= 4) return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  return launch_small<16, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+}
+
 // Largest m-tile count whose LDS footprint (xs transposed + the block's logits) fits in 64 KiB.
 int max_mtiles(int64_t K) {
   int mt = 8;
@@ -233,13 +502,16 @@ int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t 
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                   const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
                   float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s) {
-  if (!x || !xs || !packed || !S || !ZS || !cand_score || !cand_idx) return I2H_ERR_ARG;
+  if (!x || !packed || !S || !ZS || !cand_score || !cand_idx) return I2H_ERR_ARG;
+  if (!xs && !coarse_sums_x(M, K)) return I2H_ERR_ARG;  // in-kernel group sums need x in LDS
   if (M < 1 || N < 1 || N > ((int64_t)1 << 30) || check_k(K) != I2H_OK) return I2H_ERR_SHAPE;
   if (kcand < 1 || kcand > I2H_MAX_KCAND) return I2H_ERR_LIMIT;
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(xs, 4) || !aligned(S, 2) || !aligned(ZS, 2) ||
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(xs, 4) || !aligned(S, 16) || !aligned(ZS, 16) ||
       !aligned(cand_score, 4) || !aligned(cand_idx, 4) || (y && !aligned(y, 2)))
     return I2H_ERR_ALIGN;
   const int64_t ld = nblk_of(N) * kcand;
+  if (M <= 16)
+    return small_band(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kcand, cand_score, cand_idx, y, s);
   const int64_t rows_max = 16 * max_mtiles(K);
   for (int64_t m0 = 0; m0 < M; m0 += rows_max) {
     const int mc = (int)(M - m0 < rows_max ? M - m0 : rows_max);
@@ -271,6 +543,7 @@ extern "C" int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void
 extern "C" int i2h_coarse_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                                const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
                                float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream) {
+  if (!xs) return I2H_ERR_ARG;
   return i2h::coarse_launch(x, xs, M, packed, S, ZS, N, K, kcand, cand_score, cand_idx, y,
                             (hipStream_t)stream);
 }

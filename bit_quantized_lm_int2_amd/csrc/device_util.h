@@ -67,4 +67,51 @@ __device__ __forceinline__ int pow2_at_least(int n) {
   return p;
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The 64-bit value of lane `src` (each half read as uint32, so nothing is sign-extended).
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Descending bitonic sort of 64*KPL keys held KPL per lane; key index i = e * 64 + lane.
+template <int KPL>
+__device__ __forceinline__ void wave_sort_keys(uint64_t (&k)[KPL], int lane) {
+  constexpr int n = 64 * KPL;
+#pragma unroll
+  for (int size = 2; size <= n; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 64) {
+        const int es = stride / 64;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          if ((e & es) != 0) continue;
+          const bool desc = ((e * 64) & size) == 0;
+          const uint64_t a = k[e], b = k[e + es];
+          const bool sw = desc ? (a < b) : (a > b);
+          k[e] = sw ? b : a;
+          k[e + es] = sw ? a : b;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < KPL; ++e) {
+          const uint64_t o = shfl_xor_u64(k[e], stride);
+          const bool lower = (lane & stride) == 0;
+          const bool desc = ((e * 64 + lane) & size) == 0;
+          const bool keep_max = lower == desc;
+          const bool o_gt = o > k[e];
+          k[e] = (keep_max == o_gt) ? o : k[e];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace i2h

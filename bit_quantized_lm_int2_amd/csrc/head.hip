@@ -74,8 +74,8 @@ extern "C" int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, con
   if (!workspace || ws_bytes < need) return I2H_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return I2H_ERR_ALIGN;
   if (ldw < K) return I2H_ERR_SHAPE;
-  if (!aligned(x, 16) || !aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 2) ||
-      !aligned(ZS, 2) || !aligned(out_idx, 4) || !aligned(out_val, 4) || (y && !aligned(y, 2)))
+  if (!aligned(x, 16) || !aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 16) ||
+      !aligned(ZS, 16) || !aligned(out_idx, 4) || !aligned(out_val, 4) || (y && !aligned(y, 2)))
     return I2H_ERR_ALIGN;
   const Workspace w = layout(M, N, K, kcand, R);
   char* base = static_cast<char*>(workspace);
@@ -85,10 +85,11 @@ extern "C" int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, con
   int32_t* sel = reinterpret_cast<int32_t*>(base + w.sel);
   float* ex = reinterpret_cast<float*>(base + w.exact);
   hipStream_t s = (hipStream_t)stream;
-  int st = xsum_launch(x, M, K, xs, s);
-  if (st == I2H_OK) st = coarse_launch(x, xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s);
+  // for a few rows the coarse kernel holds x in LDS and sums its groups itself
+  const bool own_sums = coarse_sums_x(M, K);
+  int st = own_sums ? I2H_OK : xsum_launch(x, M, K, xs, s);
+  if (st == I2H_OK) st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s);
   if (st == I2H_OK) st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
-  if (st == I2H_OK) st = rerank_launch(x, M, W, ldw, N, K, sel, R, ex, s);
-  if (st == I2H_OK) st = finalize_launch(ex, sel, M, R, k, out_idx, out_val, s);
+  if (st == I2H_OK) st = rerank_finalize_launch(x, M, W, ldw, N, K, sel, R, k, ex, out_idx, out_val, s);
   return st;
 }

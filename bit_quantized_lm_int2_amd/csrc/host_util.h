@@ -24,6 +24,10 @@ inline int check_k(int64_t K) {
 
 inline int64_t nblk_of(int64_t N) { return (N + I2H_BLOCK_N - 1) / I2H_BLOCK_N; }
 
+// True when the coarse kernel for M rows of K keeps x in LDS and sums its groups itself, so the
+// head needs no separate group-sum launch (coarse_launch then accepts xs == nullptr).
+bool coarse_sums_x(int64_t M, int64_t K);
+
 // Entry points used by i2h_head (same checks and kernels as the exported calls).
 int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s);
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
@@ -33,6 +37,9 @@ int select_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, i
                   int kcand, int R, int32_t* sel, hipStream_t s);
 int rerank_launch(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
                   int64_t K, const int32_t* sel, int R, float* exact, hipStream_t s);
+int rerank_finalize_launch(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
+                           int64_t K, const int32_t* sel, int R, int k, float* exact, int32_t* out_idx,
+                           float* out_val, hipStream_t s);
 int finalize_launch(const float* exact, const int32_t* sel, int64_t M, int R, int k,
                     int32_t* out_idx, float* out_val, hipStream_t s);
 

@@ -93,7 +93,7 @@ extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, ui
   using namespace i2h;
   if (!W || !packed || !S || !ZS) return I2H_ERR_ARG;
   if (N < 1 || check_k(K) != I2H_OK || ldw < K) return I2H_ERR_SHAPE;
-  if (!aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 2) || !aligned(ZS, 2))
+  if (!aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 16) || !aligned(ZS, 16))
     return I2H_ERR_ALIGN;
   const int64_t units = N * (K / 512);
   const int64_t want = (units + kPackWaves - 1) / kPackWaves;

@@ -71,6 +71,85 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __r
     sel[(int64_t)m * R + j] = j < n2 ? rank_key_idx(keys[j]) : -1;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Fast path for R <= 64 and R * KCAND <= 1024, with five barriers per ranking. Each of the 16
+// waves sorts its share of the keys in registers (a bitonic network over shuffles) and keeps
+// its best R' (R' = the power of two >= R). The 16 sorted lists are then merged pairwise in a
+// tree: for sorted lists A and B, max(A[i], B[R'-1-i]) is a bitonic sequence that holds the R'
+// best of both, and one bitonic clean (log2 R' shuffle stages) sorts it.
+// ---------------------------------------------------------------------------------------------
+constexpr int kFastWaves = kSelectThreads / kWave;  // 16
+
+struct FastLds {
+  uint64_t lists[kFastWaves][64];
+  uint64_t top[64];
+};
+
+// Top R (R <= 64) of the keys the waves hold (KPL per lane, 0 = empty), best first, into
+// L.top[0 .. R). Every thread of the block must call it.
+template <int KPL>
+__device__ void block_top_r(uint64_t (&k)[KPL], int R, FastLds& L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Rp = pow2_at_least(R);
+  wave_sort_keys<KPL>(k, lane);
+  if (lane < Rp) L.lists[wave][lane] = k[0];
+  __syncthreads();
+  for (int step = 1; step < kFastWaves; step <<= 1) {
+    if ((wave & (2 * step - 1)) == 0) {
+      const uint64_t a = lane < Rp ? L.lists[wave][lane] : 0ull;
+      const uint64_t b = lane < Rp ? L.lists[wave + step][Rp - 1 - lane] : 0ull;
+      uint64_t v = a > b ? a : b;
+      for (int stride = Rp >> 1; stride > 0; stride >>= 1) {
+        const uint64_t o = shfl_xor_u64(v, stride);
+        const bool lower = (lane & stride) == 0;
+        v = (lower == (o > v)) ? o : v;
+      }
+      if (lane < Rp) L.lists[wave][lane] = v;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < R) L.top[threadIdx.x] = L.lists[0][threadIdx.x];
+  __syncthreads();
+}
+
+template <int KPL>
+__global__ __launch_bounds__(kSelectThreads) void select_fast_kernel(const float* __restrict__ cs,
+                                                                    const int32_t* __restrict__ ci,
+                                                                    int nblk, int kc, int R,
+                                                                    int32_t* __restrict__ sel) {
+  __shared__ FastLds L;
+  const int m = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ld = (int64_t)nblk * kc;
+  const float* s = cs + m * ld;
+  const int32_t* c = ci + m * ld;
+  // stage 1: block maxima, wave w holds blocks w*64*KPL + e*64 + lane
+  uint64_t k1[KPL];
+#pragma unroll
+  for (int e = 0; e < KPL; ++e) {
+    const int b = wave * 64 * KPL + e * 64 + lane;
+    uint64_t key = 0ull;
+    if (b < nblk && c[(int64_t)b * kc] >= 0)
+      key = ((uint64_t)ordered_key(s[(int64_t)b * kc]) << 32) | (uint64_t)(~(uint32_t)b);
+    k1[e] = key;
+  }
+  block_top_r<KPL>(k1, R, L);
+  // stage 2: every entry of the chosen blocks, one per thread
+  const int nb = R < nblk ? R : nblk;
+  const int t = threadIdx.x;
+  uint64_t k2[1] = {0ull};
+  if (t < nb * kc) {
+    const uint64_t bk = L.top[t / kc];
+    if (bk != 0ull) {
+      const int64_t at = (int64_t)(~(uint32_t)bk) * kc + (t % kc);
+      k2[0] = rank_key(s[at], c[at]);
+    }
+  }
+  __syncthreads();  // L.lists and L.top are rewritten below
+  block_top_r<1>(k2, R, L);
+  if (t < R) sel[(int64_t)m * R + t] = rank_key_idx(L.top[t]);
+}
+
 __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ ex,
                                                        const int32_t* __restrict__ sel, int R, int k,
                                                        int32_t* __restrict__ oi, float* __restrict__ ov) {
@@ -104,6 +183,21 @@ int select_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, i
     return I2H_ERR_LIMIT;
   if (!aligned(cand_score, 4) || !aligned(cand_idx, 4) || !aligned(sel, 4)) return I2H_ERR_ALIGN;
   const int64_t nb = R < nblk ? R : nblk;
+  if (R <= 64 && (int64_t)R * kcand <= kSelectThreads) {
+    if (nblk <= 1024)
+      hipLaunchKernelGGL(select_fast_kernel<1>, dim3((unsigned)M), dim3(kSelectThreads), 0, s, cand_score, cand_idx,
+                         (int)nblk, kcand, R, sel);
+    else if (nblk <= 2048)
+      hipLaunchKernelGGL(select_fast_kernel<2>, dim3((unsigned)M), dim3(kSelectThreads), 0, s, cand_score, cand_idx,
+                         (int)nblk, kcand, R, sel);
+    else if (nblk <= 4096)
+      hipLaunchKernelGGL(select_fast_kernel<4>, dim3((unsigned)M), dim3(kSelectThreads), 0, s, cand_score, cand_idx,
+                         (int)nblk, kcand, R, sel);
+    else
+      hipLaunchKernelGGL(select_fast_kernel<8>, dim3((unsigned)M), dim3(kSelectThreads), 0, s, cand_score, cand_idx,
+                         (int)nblk, kcand, R, sel);
+    return check_launch();
+  }
   const int keys = host_pow2(nblk > nb * kcand ? nblk : nb * kcand);
   hipLaunchKernelGGL(select_kernel, dim3((unsigned)M), dim3(kSelectThreads), (size_t)keys * 8, s,
                      cand_score, cand_idx, (int)nblk, kcand, R, sel);

@@ -19,8 +19,8 @@
  *     code is then available from i2h_last_hip_error() on the calling thread.
  *   - Shapes: G = 128 (quantisation group), BLOCK_N = 64 (candidate block), K a positive
  *     multiple of 512 (four quarters of whole groups) and at most 16384, NBLK = ceil(N / 64).
- *   - Alignment: x, W and packed must be 16-byte aligned, W's row stride a multiple of 8
- *     elements; fp32/int32 arrays 4-byte aligned, bf16 arrays 2-byte aligned.
+ *   - Alignment: x, W, packed, S and ZS must be 16-byte aligned, W's row stride a multiple of
+ *     8 elements; fp32/int32 arrays 4-byte aligned, y 2-byte aligned.
  *   - Inputs must be finite (no NaN or inf in x or W).
  */
 #ifndef I2H_H_

@@ -100,7 +100,9 @@ def test_xsum(i2h, M, K):
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,kc,R,grid", [(1, 124160, 8, 32, 0), (5, 4096, 8, 32, 4), (3, 248320, 8, 32, 0),
                                            (4, 643, 8, 100, 2), (2, 5000, 1, 1, 1), (2, 9000, 64, 128, 8),
-                                           (3, 4096, 8, 1024, 0), (1, 1000, 8, 32, 0.25)])
+                                           (3, 4096, 8, 1024, 0), (1, 1000, 8, 32, 0.25),
+                                           (2, 524288, 2, 64, 0), (3, 20000, 16, 64, 2), (2, 20000, 16, 65, 0),
+                                           (2, 70000, 8, 64, 0)])
 def test_select_bit_exact(i2h, M, N, kc, R, grid):
     say(f"select M={M} N={N} kc={kc} R={R}")
     sc = si.gen_scores(M, N, seed=N + R).numpy()
@@ -109,6 +111,18 @@ def test_select_bit_exact(i2h, M, N, kc, R, grid):
     cs, ci = oracle.block_emit(sc.astype(np.float64), kc)
     want = oracle.select_top_r(cs, ci, R)
     got = i2h.select(torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV), kc, R)
+    assert np.array_equal(host(got), want)
+
+
+def test_select_periodic_scores(i2h):
+    """Block scores repeat every 16 blocks, so every wave's list reaches deep into the ties and
+    far more than 64 list entries clear the first-pass bound."""
+    N = 124160
+    c = -(((np.arange(N) // 64) % 16).astype(np.float64))[None, :].repeat(2, 0)
+    c[1] *= 0.5
+    cs, ci = oracle.block_emit(c, 8)
+    want = oracle.select_top_r(cs, ci, 32)
+    got = i2h.select(torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV), 8, 32)
     assert np.array_equal(host(got), want)
 
 
