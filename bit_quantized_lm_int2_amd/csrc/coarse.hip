@@ -202,23 +202,47 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 //     half is brought down by one shift shared by the four quarters. 12 VALU ops per 16 weights.
 //   * only the accumulator rows that can hold a real row are scaled.
 // ---------------------------------------------------------------------------------------------
+// (a & m) | o in one VALU op. gfx9 VOP3 encodings take no literal, so the compiler splits a
+// constant mask and bias into v_and + v_or; with m and o held in VGPRs one v_and_or_b32 does it.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
+  return r;
+}
+
+// A 32-bit constant the compiler cannot fold (kept in a VGPR).
+__device__ __forceinline__ uint32_t vconst(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+struct DqConst {
+  uint32_t one, m0, m1, m2, m3;
+};
+
+__device__ __forceinline__ DqConst dq_const() {
+  return DqConst{vconst(0x3F803F80u), vconst(0x00030003u), vconst(0x000C000Cu), vconst(0x00300030u),
+                 vconst(0x00600060u)};
+}
+
 // d0/d1: four packed bytes each. Raw bytes [b0 b1 b2 b3] give weights in k order (0, 2, 1, 3);
-// byte-paired dwords [b0 b2 b1 b3] give them in natural order.
+// byte-paired dwords [b0 b2 b1 b3] give them in natural order. h0/h1 = d0 >> 8, d1 >> 8.
 template <int T>
-__device__ __forceinline__ bf16x8 dequant8_mask(uint32_t d0, uint32_t d1) {
-  constexpr uint32_t kOne = 0x3F803F80u;
+__device__ __forceinline__ bf16x8 dequant8_mask(uint32_t d0, uint32_t d1, uint32_t h0, uint32_t h1,
+                                                const DqConst& c) {
   u32x4 r;
   if constexpr (T < 3) {
-    constexpr uint32_t m = 0x00030003u << (2 * T);
-    r[0] = (d0 & m) | kOne;
-    r[1] = ((d0 >> 8) & m) | kOne;
-    r[2] = (d1 & m) | kOne;
-    r[3] = ((d1 >> 8) & m) | kOne;
+    const uint32_t m = T == 0 ? c.m0 : (T == 1 ? c.m1 : c.m2);
+    r[0] = and_or(d0, m, c.one);
+    r[1] = and_or(h0, m, c.one);
+    r[2] = and_or(d1, m, c.one);
+    r[3] = and_or(h1, m, c.one);
   } else {
-    r[0] = ((d0 >> 1) & 0x00600060u) | kOne;
-    r[1] = ((d0 >> 9) & 0x00600060u) | kOne;
-    r[2] = ((d1 >> 1) & 0x00600060u) | kOne;
-    r[3] = ((d1 >> 9) & 0x00600060u) | kOne;
+    r[0] = and_or(d0 >> 1, c.m3, c.one);
+    r[1] = and_or(d0 >> 9, c.m3, c.one);
+    r[2] = and_or(d1 >> 1, c.m3, c.one);
+    r[3] = and_or(d1 >> 9, c.m3, c.one);
   }
   return __builtin_bit_cast(bf16x8, r);
 }
@@ -278,8 +302,10 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
         }
     }
   }
-  // x rows, each group of four k stored as (0, 2, 1, 3): the order in which the mask dequant of a
-  // raw packed dword yields its weights, so the packed bytes need no permute
+  // x rows in LDS, laid out by span: xl[m][gb][t][j] holds x[m][t Q + 128 gb + j], so the four
+  // quarters of span gb sit 128 apart and every fragment offset is an immediate; each group of
+  // four k is stored as (0, 2, 1, 3), the order in which the mask dequant of a raw packed dword
+  // yields its weights, so the packed bytes need no permute
   const int xunits = XLDS ? M * (K / 8) : 0;
   for (int u = tid; u < xunits; u += kCoarseThreads) {
     const u32x4 v = ld16(x + 8 * u);
@@ -288,7 +314,9 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     o[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
     o[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
     o[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
-    *reinterpret_cast<u32x4*>(xl + 8 * u) = o;
+    const int m = (8 * u) / K, k = 8 * u - m * K;
+    const int t = k / Q, r = k - t * Q;
+    *reinterpret_cast<u32x4*>(xl + m * K + (r / kGroup) * 512 + t * kGroup + (r % kGroup)) = o;
   }
   if (xs != nullptr) {
     for (int i = tid; i < KG * 16; i += kCoarseThreads) {
@@ -320,7 +348,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       const int g = i >> 4, m = i & 15;
       float sm = 0.f;
       if (m < M) {
-        const uint16_t* xg = xl + m * K + g * kGroup;
+        const int t = g / NG, gb = g - t * NG;
+        const uint16_t* xg = xl + m * K + gb * 512 + t * kGroup;
 #pragma unroll
         for (int j = 0; j < kGroup; j += 8) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(xg + j);
@@ -335,33 +364,36 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const uint32_t* szr = sz + (wave * 16 + col) * KG;
-  const bool arow = col < M;  // this lane feeds a real row of x to the A operand
+  // A-operand rows past M repeat row M-1: their accumulator rows are computed and never used
+  const int arow = col < M ? col : M - 1;
+  const DqConst dqc = dq_const();
 
   auto body = [&](int gb, const u32x4& c0, const u32x4& c1) {
-    uint32_t dw[8];
+    uint32_t dw[8], hw[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dw[i] = XLDS ? c0[i] : pair_bytes(c0[i]);
       dw[4 + i] = XLDS ? c1[i] : pair_bytes(c1[i]);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hw[i] = dw[i] >> 8;
     f32x4 p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint16_t* xa = XLDS ? xl + arow * K + gb * 512 + 32 * h : x + (int64_t)arow * K + gb * kGroup + 32 * h;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         bf16x8 bw;
-        if (t == 0) bw = dequant8_mask<0>(dw[2 * s], dw[2 * s + 1]);
-        else if (t == 1) bw = dequant8_mask<1>(dw[2 * s], dw[2 * s + 1]);
-        else if (t == 2) bw = dequant8_mask<2>(dw[2 * s], dw[2 * s + 1]);
-        else bw = dequant8_mask<3>(dw[2 * s], dw[2 * s + 1]);
-        const int k0 = t * Q + gb * kGroup + 32 * h + 8 * s;
-        u32x4 a = {0u, 0u, 0u, 0u};
-        if (arow) {
-          if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xl + col * K + k0);
-          else a = ld16(x + (int64_t)col * K + k0);
-        }
+        const uint32_t d0 = dw[2 * s], d1 = dw[2 * s + 1], h0 = hw[2 * s], h1 = hw[2 * s + 1];
+        if (t == 0) bw = dequant8_mask<0>(d0, d1, h0, h1, dqc);
+        else if (t == 1) bw = dequant8_mask<1>(d0, d1, h0, h1, dqc);
+        else if (t == 2) bw = dequant8_mask<2>(d0, d1, h0, h1, dqc);
+        else bw = dequant8_mask<3>(d0, d1, h0, h1, dqc);
+        u32x4 a;
+        if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xa + t * kGroup + 8 * s);
+        else a = ld16(xa + t * Q + 8 * s);
         p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
       }
     }
