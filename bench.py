@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bands]
 
-A step is one call of the head's per-call path over one batch: group sums of x, the coarse
-int2 pass with its fused block top-8 emit, the top-32 selection, the exact bf16 rerank and the
-argmax, all enqueued on one stream with no host synchronisation. The workload is one rank's
+A step is one call of the head's per-call path over one batch: the coarse int2 pass with its
+fused block top-8 emit (which sums the groups of x itself at this M), the top-32 selection, and
+the exact bf16 rerank with the argmax, enqueued on one stream with no host synchronisation.
+These are the kernels i2h_head runs; the step enqueues them through the separate entry points
+so that HIP events can bracket the coarse kernel. The single-call entry is timed beside it. The workload is one rank's
 vocab slice, x[1, 5120] @ W[5120, 124160] (the draft-slot shape), with inputs resident in HBM.
 The stored head (packed codes + scales, 178.8 MB) fits in the 256 MB last-level cache, so the
 steps rotate over COPIES independent copies of it (2.1 GB) and every step reads its copy from
@@ -39,18 +41,21 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "coarse_traffic.json")
 COARSE_SRC = os.path.join(ROOT, "bit_quantized_lm_int2_amd", "csrc", "coarse.hip")
 
 
-def head_bytes(M, N, K, kc=KC, R_=R, k=1):
-    """Algorithmic HBM bytes of one call, per kernel (see the design notes for the rules)."""
+def head_bytes(M, N, K, kc=KC, R_=R, k=1, own_sums=False):
+    """Algorithmic HBM bytes of one call, per kernel: every input the step must read and every
+    output it must write once (packed codes, S, ZS, x, the group sums, the block candidates
+    written by the coarse kernel and read by the selection, the selection, the gathered bf16
+    weight rows, the results). With own_sums the coarse kernel sums the groups of x itself and
+    there is no group-sum array."""
     KG = K // 128
     nblk = (N + 63) // 64
     cand = M * nblk * kc * 8
     stored = N * K // 4 + 2 * N * KG * 2
     b = {
-        "xsum": M * K * 2 + M * KG * 4,
-        "coarse": stored + M * K * 2 + M * KG * 4 + cand,
+        "xsum": 0 if own_sums else M * K * 2 + M * KG * 4,
+        "coarse": stored + M * K * 2 + (0 if own_sums else M * KG * 4) + cand,
         "select": cand + M * R_ * 4,
-        "rerank": M * R_ * 4 + M * R_ * K * 2 + M * K * 2 + M * R_ * 4,
-        "finalize": M * R_ * 8 + M * k * 8,
+        "rerank_topk": M * R_ * 4 + M * R_ * K * 2 + M * K * 2 + M * k * 8,
     }
     b["total"] = sum(b.values())
     return b
@@ -84,6 +89,7 @@ class Head:
     def __init__(self, i2h, torch, x, copies, W, M, N, K):
         self.lib = i2h.lib()
         self.x = x
+        self.own_sums = i2h.coarse_sums_x(M, K)
         dev = x.device
         KG = K // 128
         nblk = (N + 63) // 64
@@ -100,25 +106,25 @@ class Head:
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         self.stream = s
         self.a_xsum = (P(x), M, K, P(self.xs), s)
-        self.a_coarse = [(P(x), P(self.xs), M, P(p), P(S), P(Z), N, K, KC, P(self.cs), P(self.ci), None, s)
+        xs_arg = None if self.own_sums else P(self.xs)
+        self.a_coarse = [(P(x), xs_arg, M, P(p), P(S), P(Z), N, K, KC, P(self.cs), P(self.ci), None, s)
                          for (p, S, Z) in copies]
         self.a_select = (P(self.cs), P(self.ci), M, nblk, KC, R, P(self.sel), s)
-        self.a_rerank = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, P(self.ex), s)
-        self.a_final = (P(self.ex), P(self.sel), M, R, 1, P(self.oi), P(self.ov), s)
+        self.a_rerank = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, 1, P(self.ex), P(self.oi),
+                         P(self.ov), s)
         self.a_head = [(P(x), M, P(p), P(S), P(Z), P(W), W.stride(0), N, K, KC, R, 1, P(self.oi), P(self.ov),
                         None, P(self.ws), ws_n, s) for (p, S, Z) in copies]
 
     def step(self, i, ev0=None, ev1=None):
         L = self.lib
-        st = L.i2h_xsum(*self.a_xsum)
+        st = 0 if self.own_sums else L.i2h_xsum(*self.a_xsum)
         if ev0 is not None:
             ev0.record()
         st |= L.i2h_coarse_topk(*self.a_coarse[i % len(self.a_coarse)])
         if ev1 is not None:
             ev1.record()
         st |= L.i2h_select(*self.a_select)
-        st |= L.i2h_rerank(*self.a_rerank)
-        st |= L.i2h_finalize(*self.a_final)
+        st |= L.i2h_rerank_topk(*self.a_rerank)
         if st:
             raise RuntimeError(f"libi2h status {st}")
 
@@ -213,7 +219,7 @@ def main():
 
     log(f"[bench] timing M={M}: {args.warmup} warmup + {args.steps} steps")
     h, dt, coarse_ms, dt_fused = measure(M, args.steps, args.warmup)
-    hb = head_bytes(M, N, K)
+    hb = head_bytes(M, N, K, own_sums=h.own_sums)
     us = dt * 1e6
     coarse_us = coarse_ms * 1e3
     achieved = hb["coarse"] / (coarse_us * 1e-6) / 1e9
@@ -223,8 +229,8 @@ def main():
     if not args.no_bands:
         for Mb in (16, 64):
             log(f"[bench] timing band M={Mb}")
-            _, dtb, cmsb, dtfb = measure(Mb, max(20, args.steps // 2), max(5, args.warmup // 2))
-            hbb = head_bytes(Mb, N, K)
+            hbh, dtb, cmsb, dtfb = measure(Mb, max(20, args.steps // 2), max(5, args.warmup // 2))
+            hbb = head_bytes(Mb, N, K, own_sums=hbh.own_sums)
             flops = 2.0 * Mb * K * N
             bands.append(dict(M=Mb, us_per_call=round(dtb * 1e6, 2), us_per_call_fused=round(dtfb * 1e6, 2),
                               coarse_us=round(cmsb * 1e3, 2),
@@ -289,7 +295,7 @@ def main():
         "hbm_frac": round(hb["total"] / dt / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "coarse_kernel<1>", "kernel_us": round(coarse_us, 2),
+                     "kernel": "coarse_small_kernel<1, true, 10>", "kernel_us": round(coarse_us, 2),
                      "algorithmic_bytes": hb["coarse"]},
         "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
                  "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},

@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
-           "rerank", "finalize", "workspace_bytes", "head", "GROUP", "BLOCK_N"]
+           "rerank", "finalize", "rerank_topk", "coarse_sums_x", "workspace_bytes", "head", "GROUP",
+           "BLOCK_N"]
 
 GROUP = 128
 BLOCK_N = 64
@@ -39,6 +40,8 @@ _SIGNATURES = {
     "i2h_rerank": ([_P, _I64, _P, _I64, _I64, _I64, _P, _INT, _P, _P], _INT),
     "i2h_finalize": ([_P, _P, _I64, _INT, _INT, _P, _P, _P], _INT),
     "i2h_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
+    "i2h_coarse_sums_x": ([_I64, _I64], _INT),
+    "i2h_rerank_topk": ([_P, _I64, _P, _I64, _I64, _I64, _P, _INT, _INT, _P, _P, _P, _P], _INT),
     "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
                   _I64, _P], _INT),
 }
@@ -167,12 +170,20 @@ def xsum(x: torch.Tensor, out=None) -> torch.Tensor:
     return xs
 
 
+def coarse_sums_x(M: int, K: int) -> bool:
+    """True when coarse_topk may be given xs=None (the kernel sums the groups of x itself)."""
+    return bool(lib().i2h_coarse_sums_x(M, K))
+
+
 def coarse_topk(x, xs, packed, S, ZS, kcand: int = 8, want_y: bool = False):
-    """(cand_score fp32 [M, NBLK*kcand], cand_idx int32 [M, NBLK*kcand], y bf16 [M, N] or None)."""
+    """(cand_score fp32 [M, NBLK*kcand], cand_idx int32 [M, NBLK*kcand], y bf16 [M, N] or None).
+
+    xs may be None when coarse_sums_x(M, K)."""
     _need(x, "x", torch.bfloat16, 2)
     _need(packed, "packed", torch.uint8, 2)
     for t, nm in ((x, "x"), (xs, "xs"), (packed, "packed"), (S, "S"), (ZS, "ZS")):
-        _dense(t, nm)
+        if t is not None:
+            _dense(t, nm)
     M, N, K = _head_shapes(x, packed, S, ZS, xs)
     nblk = (N + BLOCK_N - 1) // BLOCK_N
     cs = torch.empty(M, nblk * kcand, dtype=torch.float32, device=x.device)
@@ -226,6 +237,30 @@ def finalize(exact, sel, k: int = 1):
     ov = torch.empty(M, k, dtype=torch.float32, device=exact.device)
     _check("i2h_finalize", lib().i2h_finalize(_ptr(exact), _ptr(sel), M, R, k, _ptr(oi), _ptr(ov),
                                               _stream(exact)))
+    return oi, ov
+
+
+def rerank_topk(x, W, sel, k: int = 1, exact: torch.Tensor | None = None):
+    """Rerank then finalize in one call: (idx int32 [M, k], val fp32 [M, k])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(sel, "sel", torch.int32, 2)
+    _dense(x, "x")
+    _dense(sel, "sel")
+    M, K = x.shape
+    R = sel.shape[1]
+    _shape(sel, "sel", (M, R))
+    if W.shape[1] != K:
+        raise ValueError("W must have K columns")
+    if exact is None and R > 64:
+        exact = torch.empty(M, R, dtype=torch.float32, device=x.device)
+    if exact is not None:
+        _need(exact, "exact", torch.float32, 2)
+        _shape(exact, "exact", (M, R))
+    oi = torch.empty(M, k, dtype=torch.int32, device=x.device)
+    ov = torch.empty(M, k, dtype=torch.float32, device=x.device)
+    _check("i2h_rerank_topk", lib().i2h_rerank_topk(_ptr(x), M, _ptr(W), _rows(W, "W"), W.shape[0], K, _ptr(sel),
+                                                    R, k, _ptr(exact), _ptr(oi), _ptr(ov), _stream(x)))
     return oi, ov
 
 

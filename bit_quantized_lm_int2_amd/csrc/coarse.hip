@@ -249,13 +249,54 @@ __device__ __forceinline__ bf16x8 dequant8_mask(uint32_t d0, uint32_t d1, uint32
 
 constexpr float kBiasF[4] = {32.f, 8.f, 2.f, 1.f};  // D/4 for quarters 0..3
 
-// LDS footprint of coarse_small_kernel in bytes.
+#ifndef I2H_COARSE_PF
+#define I2H_COARSE_PF 4
+#endif
+constexpr int kPf = I2H_COARSE_PF;
+#ifndef I2H_COARSE_SLICE_FENCE
+#define I2H_COARSE_SLICE_FENCE 1
+#endif  // 128-byte spans of the packed stream in flight per lane
+
+// LDS footprint of coarse_small_kernel in bytes: S|ZS for the block's rows, xs transposed, the
+// block's 64-bit ranking keys, and (xrows > 0) x itself.
 __host__ __device__ constexpr size_t small_lds_bytes(int K, int xrows) {
-  return (size_t)64 * (K / kGroup) * 4 + (size_t)(K / kGroup) * 16 * 4 + (size_t)16 * kBlockN * 4 +
+  return (size_t)64 * (K / kGroup) * 4 + (size_t)(K / kGroup) * 16 * 4 + (size_t)16 * kBlockN * 8 +
          (size_t)xrows * K * 2;
 }
 
-template <int MAXR, bool XLDS>
+// Ranking key of a coarse logit in its block: higher value first, then lower column.
+__device__ __forceinline__ uint64_t block_key(float v, int col_in_block) {
+  return ((uint64_t)ordered_key(v) << 32) | (uint64_t)(63 - col_in_block);
+}
+
+// Block top-kc of up to 16 rows whose 64 keys sit in ck[m][64] (unique keys): each lane counts
+// the keys of its row that beat its own; a rank below kc is the lane's output slot.
+__device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, int N, int kc, int64_t ld,
+                                            float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int m = wave; m < M; m += kCoarseThreads / kWave) {
+    const uint64_t* row = ck + m * kBlockN;
+    const uint64_t mine = row[lane];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < kBlockN; j += 2) {
+      const uint64_t a = row[j], c = row[j + 1];
+      rank += (a > mine) + (c > mine);
+    }
+    if (rank < kc) {
+      const int tok = b * kBlockN + 63 - (int)(mine & 63u);
+      const bool ok = tok < N;
+      const int64_t at = (int64_t)m * ld + (int64_t)b * kc + rank;
+      cand_score[at] = ok ? from_ordered_key((uint32_t)(mine >> 32)) : -__builtin_inff();
+      cand_idx[at] = ok ? tok : -1;
+    }
+  }
+}
+
+// NGC > 0: the number of 128-byte spans per packed row (K / 512) is a compile-time constant and
+// the span loop is unrolled completely, so every wait for a prefetched span is exact; NGC = 0
+// runs the loop at run time (the compiler then waits for all loads at each loop header).
+template <int MAXR, bool XLDS, int NGC>
 __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
@@ -263,52 +304,71 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
   constexpr int RR = MAXR < 4 ? MAXR : 4;  // accumulator rows per lane that can be real
   extern __shared__ __align__(16) uint32_t lds[];
-  const int Q = K >> 2, NG = Q / kGroup, KG = K / kGroup;
-  uint32_t* sz = lds;                                      // [64][KG]: S | ZS << 16
-  float* xsT = reinterpret_cast<float*>(sz + 64 * KG);     // [KG][16]
-  float* cbuf = xsT + KG * 16;                             // [16][64]
-  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + 16 * kBlockN);  // [MAXR][K] when XLDS
+  if constexpr (NGC > 0) K = NGC * 512;
+  const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / kGroup;
+  uint32_t* sz = lds;                                        // [64][KG]: S | ZS << 16
+  float* xsT = reinterpret_cast<float*>(sz + 64 * KG);       // [KG][16]
+  uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * 16);  // [16][64] ranking keys
+  uint16_t* xl = reinterpret_cast<uint16_t*>(ck + 16 * kBlockN);  // [MAXR][K] when XLDS
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x, n0 = b * kBlockN;
   const int n = n0 + wave * 16 + col;
   const bool nvalid = n < N;
 
-  // the first two 128-byte spans of the packed stream are requested before the staging below
-  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + 32 * h;
-  u32x4 pa0 = ld16(prow), pa1 = ld16(prow + 16);
-  const int g1 = NG > 1 ? 1 : 0;
-  u32x4 pb0 = ld16(prow + g1 * kGroup), pb1 = ld16(prow + g1 * kGroup + 16);
-
-  // stage S/ZS of rows n0 .. n0+63 (contiguous in memory), zero past N; all loads first
-  constexpr int kSzUnits = 4;  // 16-byte units per thread: 64 * KG / 8 <= 1024 for KG <= 128
-  const int tot = (N - n0 < kBlockN ? N - n0 : kBlockN) * KG;
-  const uint16_t* Sb = S + (int64_t)n0 * KG;
-  const uint16_t* Zb = ZS + (int64_t)n0 * KG;
-  u32x4 sv[kSzUnits], zv[kSzUnits];
+  // Loads complete in issue order as far as the wait counter is concerned, so they are issued in
+  // the order their data is needed: x (resident in L2) first, then this wave's S/ZS rows, then
+  // the first spans of the packed stream.
+  constexpr bool kXReg = XLDS && NGC > 0;  // x staged through registers, group sums reduced there
+  constexpr int kXU = kXReg ? (MAXR * NGC * 64 + kCoarseThreads - 1) / kCoarseThreads : 1;
+  const int xunits = XLDS ? M * (K / 8) : 0;  // 16-byte units of x
+  u32x4 xr[kXU];
+  if constexpr (kXReg) {
 #pragma unroll
-  for (int i = 0; i < kSzUnits; ++i) {
-    const int e0 = (tid + i * kCoarseThreads) * 8;
-    sv[i] = u32x4{0u, 0u, 0u, 0u};
-    zv[i] = u32x4{0u, 0u, 0u, 0u};
-    if (e0 + 8 <= tot) {
-      sv[i] = ld16(Sb + e0);
-      zv[i] = ld16(Zb + e0);
-    } else if (e0 < tot) {
-      for (int j = 0; j < 8; ++j)
-        if (e0 + j < tot) {
-          sv[i][j >> 1] |= (uint32_t)Sb[e0 + j] << (16 * (j & 1));
-          zv[i][j >> 1] |= (uint32_t)Zb[e0 + j] << (16 * (j & 1));
-        }
+    for (int i = 0; i < kXU; ++i) {
+      const int u = tid + i * kCoarseThreads;
+      xr[i] = u < xunits ? ld16(x + 8 * u) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+  constexpr int kSzW = NGC > 0 ? (NGC + 7) / 8 : 4;  // 16-byte S units per lane: 16 rows * KG / 8 / 64 (KG <= 128)
+  const int rows_valid = N - n0 < kBlockN ? N - n0 : kBlockN;
+  const int tot = rows_valid * KG;                   // valid elements of the block's S
+  const int wbase = wave * 16 * KG;                  // this wave's rows start here
+  const uint16_t* Sb = S + (int64_t)n0 * KG;
+  const uint16_t* Zb = ZS + (int64_t)n0 * KG;
+  u32x4 sv[kSzW], zv[kSzW];
+#pragma unroll
+  for (int i = 0; i < kSzW; ++i) {
+    const int e0 = wbase + (lane + i * kWave) * 8;
+    sv[i] = u32x4{0u, 0u, 0u, 0u};
+    zv[i] = u32x4{0u, 0u, 0u, 0u};
+    if ((lane + i * kWave) * 8 < 16 * KG) {
+      if (e0 + 8 <= tot) {
+        sv[i] = ld16(Sb + e0);
+        zv[i] = ld16(Zb + e0);
+      } else if (e0 < tot) {
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < tot) {
+            sv[i][j >> 1] |= (uint32_t)Sb[e0 + j] << (16 * (j & 1));
+            zv[i][j >> 1] |= (uint32_t)Zb[e0 + j] << (16 * (j & 1));
+          }
+      }
+    }
+  }
+  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + 32 * h;
+  u32x4 ring[kPf][2];
+#pragma unroll
+  for (int p = 0; p < kPf; ++p) {
+    const int g = p < NG ? p : NG - 1;
+    ring[p][0] = ld16(prow + g * kGroup);
+    ring[p][1] = ld16(prow + g * kGroup + 16);
+  }
+
   // x rows in LDS, laid out by span: xl[m][gb][t][j] holds x[m][t Q + 128 gb + j], so the four
   // quarters of span gb sit 128 apart and every fragment offset is an immediate; each group of
   // four k is stored as (0, 2, 1, 3), the order in which the mask dequant of a raw packed dword
   // yields its weights, so the packed bytes need no permute
-  const int xunits = XLDS ? M * (K / 8) : 0;
-  for (int u = tid; u < xunits; u += kCoarseThreads) {
-    const u32x4 v = ld16(x + 8 * u);
+  auto put_x = [&](int u, const u32x4& v) {
     u32x4 o;
     o[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
     o[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
@@ -317,6 +377,30 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     const int m = (8 * u) / K, k = 8 * u - m * K;
     const int t = k / Q, r = k - t * Q;
     *reinterpret_cast<u32x4*>(xl + m * K + (r / kGroup) * 512 + t * kGroup + (r % kGroup)) = o;
+  };
+  if constexpr (kXReg) {
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      const int u = tid + i * kCoarseThreads;
+      if (u < xunits) put_x(u, xr[i]);
+      if (xs == nullptr) {
+        // the 16 units of a group of 128 k sit in 16 consecutive lanes
+        float sm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm += bf16_lo(xr[i][e]) + bf16_hi(xr[i][e]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+        if ((tid & 15) == 0 && u < xunits) {
+          const int m = (8 * u) / K, g = (8 * u - m * K) / kGroup;
+          xsT[g * 16 + m] = sm;
+        }
+      }
+    }
+    if (xs == nullptr)
+      for (int i = tid; i < KG * 16; i += kCoarseThreads)
+        if ((i & 15) >= M) xsT[i] = 0.f;
+  } else if constexpr (XLDS) {
+    for (int u = tid; u < xunits; u += kCoarseThreads) put_x(u, ld16(x + 8 * u));
   }
   if (xs != nullptr) {
     for (int i = tid; i < KG * 16; i += kCoarseThreads) {
@@ -324,25 +408,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
     }
   }
-#pragma unroll
-  for (int i = 0; i < kSzUnits; ++i) {
-    const int e0 = (tid + i * kCoarseThreads) * 8;
-    if (e0 < kBlockN * KG) {
-      u32x4 lo, hi;
-      lo[0] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x05040100u);
-      lo[1] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x07060302u);
-      lo[2] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x05040100u);
-      lo[3] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x07060302u);
-      hi[0] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x05040100u);
-      hi[1] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x07060302u);
-      hi[2] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x05040100u);
-      hi[3] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x07060302u);
-      *reinterpret_cast<u32x4*>(sz + e0) = lo;
-      *reinterpret_cast<u32x4*>(sz + e0 + 4) = hi;
-    }
-  }
   __syncthreads();
-  if (xs == nullptr) {
+  if (!kXReg && xs == nullptr) {
     // group sums from the LDS copy of x (only launched so with x in LDS): one thread per group
     for (int i = tid; i < KG * 16; i += kCoarseThreads) {
       const int g = i >> 4, m = i & 15;
@@ -360,6 +427,24 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       xsT[i] = sm;
     }
     __syncthreads();
+  }
+  // this wave's S/ZS rows, interleaved S | ZS << 16; only this wave reads them, so no barrier
+#pragma unroll
+  for (int i = 0; i < kSzW; ++i) {
+    if ((lane + i * kWave) * 8 < 16 * KG) {
+      const int e0 = wbase + (lane + i * kWave) * 8;
+      u32x4 lo, hi;
+      lo[0] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x05040100u);
+      lo[1] = __builtin_amdgcn_perm(zv[i][0], sv[i][0], 0x07060302u);
+      lo[2] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x05040100u);
+      lo[3] = __builtin_amdgcn_perm(zv[i][1], sv[i][1], 0x07060302u);
+      hi[0] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x05040100u);
+      hi[1] = __builtin_amdgcn_perm(zv[i][2], sv[i][2], 0x07060302u);
+      hi[2] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x05040100u);
+      hi[3] = __builtin_amdgcn_perm(zv[i][3], sv[i][3], 0x07060302u);
+      *reinterpret_cast<u32x4*>(sz + e0) = lo;
+      *reinterpret_cast<u32x4*>(sz + e0 + 4) = hi;
+    }
   }
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -396,6 +481,10 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
         else a = ld16(xa + t * Q + 8 * s);
         p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
       }
+#if I2H_COARSE_SLICE_FENCE
+      // keep the next slice's x fragments from being hoisted: 4 live fragments instead of 16
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -414,20 +503,30 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     }
   };
 
-  for (int gb = 0; gb < NG; gb += 2) {
-    {
-      const u32x4 c0 = pa0, c1 = pa1;
-      const int nx = gb + 2 < NG ? gb + 2 : NG - 1;
-      pa0 = ld16(prow + nx * kGroup);
-      pa1 = ld16(prow + nx * kGroup + 16);
-      body(gb, c0, c1);
+  // ring of I2H_COARSE_PF spans in flight: slot p is consumed in place, then refilled with the
+  // span PF ahead (refilling before the body would make the compiler copy the slot out first,
+  // which waits for every load in flight)
+  if constexpr (NGC > 0) {
+#pragma unroll
+    for (int gb = 0; gb < NGC; ++gb) {
+      body(gb, ring[gb % kPf][0], ring[gb % kPf][1]);
+      if (gb + kPf < NGC) {
+        ring[gb % kPf][0] = ld16(prow + (gb + kPf) * kGroup);
+        ring[gb % kPf][1] = ld16(prow + (gb + kPf) * kGroup + 16);
+      }
     }
-    if (gb + 1 < NG) {
-      const u32x4 c0 = pb0, c1 = pb1;
-      const int nx = gb + 3 < NG ? gb + 3 : NG - 1;
-      pb0 = ld16(prow + nx * kGroup);
-      pb1 = ld16(prow + nx * kGroup + 16);
-      body(gb + 1, c0, c1);
+  } else {
+    for (int gb0 = 0; gb0 < NG; gb0 += kPf) {
+#pragma unroll
+      for (int p = 0; p < kPf; ++p) {
+        const int gb = gb0 + p;
+        if (gb < NG) {
+          body(gb, ring[p][0], ring[p][1]);
+          const int nx = gb + kPf < NG ? gb + kPf : NG - 1;
+          ring[p][0] = ld16(prow + nx * kGroup);
+          ring[p][1] = ld16(prow + nx * kGroup + 16);
+        }
+      }
     }
   }
 
@@ -440,22 +539,10 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < RR; ++r) cbuf[(4 * h + r) * kBlockN + wave * 16 + col] = nvalid ? acc[r] : -__builtin_inff();
+  for (int r = 0; r < RR; ++r)
+    ck[(4 * h + r) * kBlockN + wave * 16 + col] = block_key(nvalid ? acc[r] : -__builtin_inff(), wave * 16 + col);
   __syncthreads();
-
-  const int64_t ld = (int64_t)nblk * kc;
-  for (int m = wave; m < M; m += kCoarseThreads / kWave) {
-    float v = cbuf[m * kBlockN + lane];
-    int c = lane;
-    wave_sort_desc(v, c, lane);
-    if (lane < kc) {
-      const int tok = b * kBlockN + c;
-      const bool ok = tok < N;
-      const int64_t at = (int64_t)m * ld + (int64_t)b * kc + lane;
-      cand_score[at] = ok ? v : -__builtin_inff();
-      cand_idx[at] = ok ? tok : -1;
-    }
-  }
+  emit_ranked(ck, M, b, N, kc, (int64_t)nblk * kc, cand_score, cand_idx);
 }
 
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int M, int K,
@@ -488,8 +575,15 @@ int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packe
                  const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
-  hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
-                     packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  if (K == 5120)
+    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 10>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
+                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  else if (K == 512)
+    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 1>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
+                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  else
+    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 0>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
+                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
   return check_launch();
 }
 
@@ -575,7 +669,6 @@ extern "C" int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void
 extern "C" int i2h_coarse_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                                const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
                                float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream) {
-  if (!xs) return I2H_ERR_ARG;
   return i2h::coarse_launch(x, xs, M, packed, S, ZS, N, K, kcand, cand_score, cand_idx, y,
                             (hipStream_t)stream);
 }

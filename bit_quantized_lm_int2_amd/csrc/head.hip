@@ -56,6 +56,8 @@ extern "C" const char* i2h_strerror(int status) {
 
 extern "C" int i2h_last_hip_error(void) { return i2h::g_last_hip_error; }
 
+extern "C" int i2h_coarse_sums_x(int64_t M, int64_t K) { return i2h::coarse_sums_x(M, K) ? 1 : 0; }
+
 extern "C" int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R) {
   if (M < 1 || N < 1 || i2h::check_k(K) != I2H_OK || i2h::nblk_of(N) > I2H_MAX_NBLK) return I2H_ERR_SHAPE;
   if (kcand < 1 || kcand > I2H_MAX_KCAND || R < 1 || R > I2H_MAX_R) return I2H_ERR_LIMIT;

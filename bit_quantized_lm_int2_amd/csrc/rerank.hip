@@ -136,3 +136,10 @@ extern "C" int i2h_rerank(const uint16_t* x, int64_t M, const uint16_t* W, int64
                           int64_t K, const int32_t* sel, int R, float* exact, void* stream) {
   return i2h::rerank_launch(x, M, W, ldw, N, K, sel, R, exact, (hipStream_t)stream);
 }
+
+extern "C" int i2h_rerank_topk(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
+                               int64_t K, const int32_t* sel, int R, int k, float* exact, int32_t* out_idx,
+                               float* out_val, void* stream) {
+  return i2h::rerank_finalize_launch(x, M, W, ldw, N, K, sel, R, k, exact, out_idx, out_val,
+                                     (hipStream_t)stream);
+}

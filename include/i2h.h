@@ -93,7 +93,9 @@ I2H_API int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void* s
  * first, to slots b*kcand .. b*kcand+kcand-1 of
  *   cand_score fp32 [M, NBLK*kcand] and cand_idx int32 [M, NBLK*kcand] (token index n);
  * slots past a tail block's real columns get (-inf, -1).
- *   x bf16 [M, K]; xs fp32 [M, K/128] from i2h_xsum; packed/S/ZS from i2h_pack.
+ *   x bf16 [M, K]; xs fp32 [M, K/128] from i2h_xsum; packed/S/ZS from i2h_pack. xs may be NULL
+ *   when i2h_coarse_sums_x(M, K) is true: the kernel then holds x in LDS and sums its groups
+ *   itself (a few rows); otherwise a NULL xs is I2H_ERR_ARG.
  *   y   optional bf16 [M, N] (row stride N): the coarse logits rounded to nearest-even; NULL to skip.
  * Limits: M >= 1 (any size; rows are processed in chunks), 1 <= kcand <= 64.
  */
@@ -132,12 +134,24 @@ I2H_API int i2h_rerank(const uint16_t* x, int64_t M, const uint16_t* W, int64_t 
 I2H_API int i2h_finalize(const float* exact, const int32_t* sel, int64_t M, int R, int k,
                          int32_t* out_idx, float* out_val, void* stream);
 
+/* 1 if i2h_coarse_topk sums the groups of x itself for these sizes (xs may be NULL), else 0. */
+I2H_API int i2h_coarse_sums_x(int64_t M, int64_t K);
+
+/*
+ * i2h_rerank followed by i2h_finalize, in one kernel when R <= 64 (one workgroup per row; the
+ * exact scores also go to `exact` if it is not NULL). For R > 64 `exact` is required and the two
+ * steps run as separate kernels. Limits as in those calls.
+ */
+I2H_API int i2h_rerank_topk(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,
+                            int64_t K, const int32_t* sel, int R, int k, float* exact, int32_t* out_idx,
+                            float* out_val, void* stream);
+
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);
 
 /*
- * One call of the head: i2h_xsum, i2h_coarse_topk, i2h_select, i2h_rerank and i2h_finalize in
- * stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
+ * One call of the head: i2h_xsum (skipped when i2h_coarse_sums_x), i2h_coarse_topk, i2h_select
+ * and i2h_rerank_topk in stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
  * aligned, caller-owned, contents undefined afterwards). Arguments as in those calls; y may be
  * NULL. The limits of every step apply.
  */

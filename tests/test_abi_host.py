@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = set(declared())
     want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
-            "i2h_head"}
+            "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk"}
     assert names == want
 
 
@@ -52,6 +52,20 @@ def test_sizes():
     assert lib.i2h_sizes(10, 640, ctypes.byref(a), ctypes.byref(b)) == SHAPE
     assert lib.i2h_sizes(0, 512, ctypes.byref(a), ctypes.byref(b)) == SHAPE
     assert lib.i2h_sizes(10, 512, None, ctypes.byref(b)) == ARG
+
+
+def test_coarse_sums_x():
+    lib = i2h.lib()
+    assert lib.i2h_coarse_sums_x(1, 5120) == 1
+    assert lib.i2h_coarse_sums_x(4, 5120) == 1
+    assert lib.i2h_coarse_sums_x(16, 5120) == 0
+    assert lib.i2h_coarse_sums_x(1, 1000) == 0
+    c = lib.i2h_coarse_topk
+    assert c(P, None, 16, P, P, P, 4096, 5120, 8, P, P, None, None) == ARG  # xs required here
+    r = lib.i2h_rerank_topk
+    assert r(P, 1, P, 512, 4096, 512, P, 32, 33, None, P, P, None) == LIMIT
+    assert r(P, 1, P, 512, 4096, 512, P, 65, 1, None, P, P, None) == ARG     # exact needed for R > 64
+    assert r(P, 1, None, 512, 4096, 512, P, 32, 1, None, P, P, None) == ARG
 
 
 def test_workspace_bytes():

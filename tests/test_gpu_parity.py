@@ -203,18 +203,57 @@ def test_exact_arithmetic_head_bit_exact(i2h, M, N, kc, R, k):
 # ---------------------------------------------------------------------------------------------
 # end to end on Gaussian heads, tolerance rules
 # ---------------------------------------------------------------------------------------------
-def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, rows=None):
-    """GPU step by step and fused, against the oracle; rows: subset of rows the oracle checks."""
-    x, W = dev_bf16(xb), dev_bf16(Wb)
-    p, S, ZS = i2h.pack(W)
-    xs = i2h.xsum(x)
+def gpu_paths(i2h, x, W, p, S, ZS, kc, R, k):
+    """The head through its separate entry points, two ways: (a) the kernels i2h_head runs
+    (group sums in the coarse kernel when it can, fused rerank+finalize), checked bit for bit
+    against i2h_head itself; (b) xsum, coarse_topk, select, rerank, finalize one by one."""
+    M, K = x.shape
+    own = i2h.coarse_sums_x(M, K)
+    xs = None if own else i2h.xsum(x)
     cs, ci, y = i2h.coarse_topk(x, xs, p, S, ZS, kcand=kc, want_y=True)
     sel = i2h.select(cs, ci, kc, R)
-    ex = i2h.rerank(x, W, sel)
-    oi, ov = i2h.finalize(ex, sel, k)
+    ex = torch.empty(M, R, dtype=torch.float32, device=x.device)
+    oi, ov = i2h.rerank_topk(x, W, sel, k, exact=ex)
     hi, hv = i2h.head(x, p, S, ZS, W, kcand=kc, R=R, k=k)
     torch.cuda.synchronize()
-    assert torch.equal(hi, oi) and torch.equal(hv, ov), "fused call differs from the steps"
+    assert torch.equal(hi, oi) and torch.equal(hv, ov), "i2h_head differs from its own kernels"
+    a = dict(cs=cs, ci=ci, y=y, sel=sel, ex=ex, oi=oi, ov=ov)
+    xs_b = i2h.xsum(x)
+    cs_b, ci_b, y_b = i2h.coarse_topk(x, xs_b, p, S, ZS, kcand=kc, want_y=True)
+    sel_b = i2h.select(cs_b, ci_b, kc, R)
+    ex_b = i2h.rerank(x, W, sel_b)
+    oi_b, ov_b = i2h.finalize(ex_b, sel_b, k)
+    torch.cuda.synchronize()
+    b = dict(cs=cs_b, ci=ci_b, y=y_b, sel=sel_b, ex=ex_b, oi=oi_b, ov=ov_b)
+    return a, b
+
+
+def check_path(g, res, rows, xr, Wb, kc, k, label):
+    c = res["coarse"]
+    yh, csh, cih = host(g["y"])[rows], host(g["cs"])[rows], host(g["ci"])[rows]
+    ok = cih >= 0
+    # Y is the bf16 rounding of the same fp32 logits the candidates carry
+    assert np.array_equal(np.take_along_axis(yh, np.where(ok, cih, 0).astype(np.int64), axis=1)[ok],
+                          oracle.f32_to_bf16(csh[ok]))
+    err = pu.check_coarse_values(yh, c)
+    err32 = pu.coarse_fp32_error(csh, cih, c)
+    cand_ex, cand_tight = pu.check_candidates(csh, cih, c, kc)
+    g_sel = host(g["sel"])[rows]
+    sel_ex, sel_tight = pu.check_selection(g_sel, res["sel"], c)
+    e_g, rerr = pu.check_rerank(host(g["ex"])[rows], xr, Wb, g_sel)
+    fin_ex = pu.check_final(host(g["oi"])[rows], host(g["ov"])[rows], e_g, g_sel, k)
+    match, sel_excused, tie_excused = pu.final_vs_oracle(host(g["oi"])[rows], res, g_sel, e_g)
+    say(f"  [{label}] rows={len(rows)} coarse_err(bf16 Y)={err:.2e} coarse_err(fp32)={err32:.2e} "
+        f"cand_excused={cand_ex} (tight {cand_tight}) sel_excused_rows={sel_ex} (tight {sel_tight}) "
+        f"rerank_err={rerr:.2e} final match={match} sel_excused={sel_excused} tie_excused={tie_excused + fin_ex}")
+    return match
+
+
+def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, rows=None):
+    """Both GPU paths against the oracle; rows: subset of rows the oracle checks."""
+    x, W = dev_bf16(xb), dev_bf16(Wb)
+    p, S, ZS = i2h.pack(W)
+    a, b = gpu_paths(i2h, x, W, p, S, ZS, kc, R, k)
     rows = np.arange(xb.shape[0]) if rows is None else np.asarray(rows)
     if packed_o is None:
         packed_o = oracle.pack(Wb)
@@ -223,24 +262,9 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     po, So, ZSo = packed_o
     xr = xb[rows]
     res = oracle.head(xr, Wb, po, So, ZSo, kcand=kc, R=R, k=k, coarse=None if coarse_o is None else coarse_o[rows])
-    c = res["coarse"]
-    yh, csh, cih = host(y)[rows], host(cs)[rows], host(ci)[rows]
-    ok = cih >= 0
-    # Y is the bf16 rounding of the same fp32 logits the candidates carry
-    assert np.array_equal(np.take_along_axis(yh, np.where(ok, cih, 0).astype(np.int64), axis=1)[ok],
-                          oracle.f32_to_bf16(csh[ok]))
-    err = pu.check_coarse_values(yh, c)
-    err32 = pu.coarse_fp32_error(csh, cih, c)
-    cand_ex, cand_tight = pu.check_candidates(csh, cih, c, kc)
-    g_sel = host(sel)[rows]
-    sel_ex, sel_tight = pu.check_selection(g_sel, res["sel"], c)
-    e_g, rerr = pu.check_rerank(host(ex)[rows], xr, Wb, g_sel)
-    fin_ex = pu.check_final(host(oi)[rows], host(ov)[rows], e_g, g_sel, k)
-    match, sel_excused, tie_excused = pu.final_vs_oracle(host(oi)[rows], res, g_sel, e_g)
-    say(f"  rows={len(rows)} coarse_err(bf16 Y)={err:.2e} coarse_err(fp32)={err32:.2e} cand_excused={cand_ex} (tight {cand_tight}) "
-        f"sel_excused_rows={sel_ex} (tight {sel_tight}) rerank_err={rerr:.2e} "
-        f"final match={match} sel_excused={sel_excused} tie_excused={tie_excused + fin_ex}")
-    return dict(match=match, places=len(rows) * k, res=res, gpu_idx=host(oi)[rows])
+    match = check_path(a, res, rows, xr, Wb, kc, k, "head kernels")
+    check_path(b, res, rows, xr, Wb, kc, k, "separate calls")
+    return dict(match=match, places=len(rows) * k, res=res, gpu_idx=host(a["oi"])[rows])
 
 
 @pytest.mark.parametrize("M,N,K,kc,R,k", [
