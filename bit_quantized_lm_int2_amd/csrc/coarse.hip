@@ -17,19 +17,13 @@
 // into the result once the group is complete. A byte permute puts bytes (0,2,1,3) of each
 // dword in place so that the bit-pattern dequant yields bf16 pairs in natural k order, which
 // lets the x fragment be one contiguous 16-byte load.
-#include "device_util.h"
+#include "dequant.h"
 #include "host_util.h"
 
 namespace i2h {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-
 constexpr int kCoarseThreads = 256;  // 4 waves x 16 columns = one 64-column block
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3].
 __device__ __forceinline__ uint32_t pair_bytes(uint32_t d) { return __builtin_amdgcn_perm(d, d, 0x03010200u); }
@@ -188,66 +182,14 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small-M band (M <= 16): one m-tile, HBM-bound. Differences from coarse_kernel:
+// Small-M band (M <= 4): one m-tile, HBM-bound. Differences from coarse_kernel:
 //   * the block's S and ZS rows (contiguous in memory) and, when it fits, x itself are staged
 //     in LDS once per workgroup, so the K loop issues no small scattered loads;
-//   * the packed stream is prefetched two 128-byte spans ahead;
-//   * quarters 0-2 are dequantised with a mask alone. The code bits of quarter t of the low
-//     byte of each bf16 half sit at mantissa bits 2t, 2t+1, so (d & (3 << 2t)) | 0x3F80 reads as
-//     1 + v/D with D = 128, 32, 8 for t = 0, 1, 2 (quarter 3 keeps the shift, D = 4). With
-//     f = D/4 the group's dot P' = sum x (1 + v/D) = xs + dot/D gives
-//       S P - xs ZS = (f S) P' - xs ((f - 1) S + ZS),  P = xs + dot/4,
-//     so the bias change folds into the per-group scale and zero on the accumulator; f S and
-//     (f - 1) S + ZS are exact in fp32 (at most 13 significant bits each). The high byte of each
-//     half is brought down by one shift shared by the four quarters. 12 VALU ops per 16 weights.
+//   * the packed stream is prefetched several 128-byte spans ahead;
+//   * quarters 0-2 are dequantised with a mask alone (dequant.h), the high byte of each half
+//     brought down by one shift shared by the four quarters: 12 VALU ops per 16 weights;
 //   * only the accumulator rows that can hold a real row are scaled.
 // ---------------------------------------------------------------------------------------------
-// (a & m) | o in one VALU op. gfx9 VOP3 encodings take no literal, so the compiler splits a
-// constant mask and bias into v_and + v_or; with m and o held in VGPRs one v_and_or_b32 does it.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(o));
-  return r;
-}
-
-// A 32-bit constant the compiler cannot fold (kept in a VGPR).
-__device__ __forceinline__ uint32_t vconst(uint32_t c) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
-  return r;
-}
-
-struct DqConst {
-  uint32_t one, m0, m1, m2, m3;
-};
-
-__device__ __forceinline__ DqConst dq_const() {
-  return DqConst{vconst(0x3F803F80u), vconst(0x00030003u), vconst(0x000C000Cu), vconst(0x00300030u),
-                 vconst(0x00600060u)};
-}
-
-// d0/d1: four packed bytes each. Raw bytes [b0 b1 b2 b3] give weights in k order (0, 2, 1, 3);
-// byte-paired dwords [b0 b2 b1 b3] give them in natural order. h0/h1 = d0 >> 8, d1 >> 8.
-template <int T>
-__device__ __forceinline__ bf16x8 dequant8_mask(uint32_t d0, uint32_t d1, uint32_t h0, uint32_t h1,
-                                                const DqConst& c) {
-  u32x4 r;
-  if constexpr (T < 3) {
-    const uint32_t m = T == 0 ? c.m0 : (T == 1 ? c.m1 : c.m2);
-    r[0] = and_or(d0, m, c.one);
-    r[1] = and_or(h0, m, c.one);
-    r[2] = and_or(d1, m, c.one);
-    r[3] = and_or(h1, m, c.one);
-  } else {
-    r[0] = and_or(d0 >> 1, c.m3, c.one);
-    r[1] = and_or(d0 >> 9, c.m3, c.one);
-    r[2] = and_or(d1 >> 1, c.m3, c.one);
-    r[3] = and_or(d1 >> 9, c.m3, c.one);
-  }
-  return __builtin_bit_cast(bf16x8, r);
-}
-
-constexpr float kBiasF[4] = {32.f, 8.f, 2.f, 1.f};  // D/4 for quarters 0..3
 
 #ifndef I2H_COARSE_PF
 #define I2H_COARSE_PF 4
@@ -369,11 +311,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
   // four k is stored as (0, 2, 1, 3), the order in which the mask dequant of a raw packed dword
   // yields its weights, so the packed bytes need no permute
   auto put_x = [&](int u, const u32x4& v) {
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(v[1], v[0], 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(v[1], v[0], 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(v[3], v[2], 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(v[3], v[2], 0x07060302u);
+    const u32x4 o = x_pair_order(v);
     const int m = (8 * u) / K, k = 8 * u - m * K;
     const int t = k / Q, r = k - t * Q;
     *reinterpret_cast<u32x4*>(xl + m * K + (r / kGroup) * 512 + t * kGroup + (r % kGroup)) = o;
@@ -587,31 +525,43 @@ int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packe
   return check_launch();
 }
 
+// True when the small kernel keeps x in LDS for M rows of K (and then sums the groups itself).
+bool small_sums_x(int64_t M, int64_t K) {
+  return (M == 1 && small_lds_bytes((int)K, 1) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4) <= 65536);
+}
+
 }  // namespace
 
-// True when the coarse kernel for these sizes keeps x in LDS and can sum its groups itself.
+// True when every launch coarse_launch makes for M rows of K sums the groups of x itself: the
+// small kernel with x in LDS (M <= 4) or the tile kernel, per chunk of kTileMaxRows rows.
 bool coarse_sums_x(int64_t M, int64_t K) {
   if (M < 1 || check_k(K) != I2H_OK) return false;
-  return (M == 1 && small_lds_bytes((int)K, 1) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4) <= 65536);
+  for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
+    const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
+    if (!(mc <= 4 ? small_sums_x(mc, K) : tile_supported(mc, K))) return false;
+  }
+  return true;
 }
 
 namespace {
 
+// M <= 4 rows.
 int small_band(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
   if (M == 1 && small_lds_bytes(K, 1) <= 65536)
     return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
   if (M <= 4 && small_lds_bytes(K, 4) <= 65536)
     return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
-  if (M <= 4) return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
-  return launch_small<16, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
 }
 
-// Largest m-tile count whose LDS footprint (xs transposed + the block's logits) fits in 64 KiB.
-int max_mtiles(int64_t K) {
-  int mt = 8;
-  while (mt > 1 && ((K / kGroup) * 16 * mt * 4 + 16 * mt * kBlockN * 4) > 65536) mt >>= 1;
-  return mt;
+// The generic kernel (global A loads, any K) for up to kTileMaxRows rows; needs xs.
+int generic_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  if (!xs) return I2H_ERR_ARG;
+  if (M <= 16) return launch_coarse<1>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  if (M <= 32) return launch_coarse<2>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  return launch_coarse<4>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
 }
 
 }  // namespace
@@ -636,25 +586,22 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
       !aligned(cand_score, 4) || !aligned(cand_idx, 4) || (y && !aligned(y, 2)))
     return I2H_ERR_ALIGN;
   const int64_t ld = nblk_of(N) * kcand;
-  if (M <= 16)
-    return small_band(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kcand, cand_score, cand_idx, y, s);
-  const int64_t rows_max = 16 * max_mtiles(K);
-  for (int64_t m0 = 0; m0 < M; m0 += rows_max) {
-    const int mc = (int)(M - m0 < rows_max ? M - m0 : rows_max);
+  // rows go in chunks of kTileMaxRows; a chunk of at most 4 rows runs the small kernel, a larger
+  // one the tile kernel where it is built for K, else the generic kernel
+  for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
+    const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
     const uint16_t* xc = x + m0 * K;
-    const float* xsc = xs + m0 * (K / kGroup);
+    const float* xsc = xs ? xs + m0 * (K / kGroup) : nullptr;
     float* csc = cand_score + m0 * ld;
     int32_t* cic = cand_idx + m0 * ld;
     uint16_t* yc = y ? y + m0 * N : nullptr;
     int st;
-    if (mc <= 16)
-      st = launch_coarse<1>(xc, xsc, mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
-    else if (mc <= 32)
-      st = launch_coarse<2>(xc, xsc, mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
-    else if (mc <= 64)
-      st = launch_coarse<4>(xc, xsc, mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+    if (mc <= 4 && (xsc || small_sums_x(mc, K)))
+      st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+    else if (tile_supported(mc, K))
+      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, s);
     else
-      st = launch_coarse<8>(xc, xsc, mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+      st = generic_rows(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
     if (st != I2H_OK) return st;
   }
   return I2H_OK;

@@ -1,0 +1,459 @@
+// Coarse int2 logits with the fused block top-KCAND emit, for 5..64 rows of x per launch.
+//
+// radiance_drafthead.py, _draft_head_int2 / _emit: the same arithmetic as the small-M kernel
+// (bit-pattern dequant, scale and zero applied per group to the accumulator, KCAND best columns
+// of every 64-column block per row), laid out for many rows.
+//
+// Layout on gfx950. A workgroup of 4 waves covers 4 consecutive 64-column blocks; wave w owns
+// block 4 blockIdx.x + w whole, as four 16-column MFMA tiles (v_mfma_f32_16x16x32_bf16), so
+// each A fragment of x read from LDS feeds four MFMAs and the block's emit needs no other wave.
+// x is streamed through LDS in stages of 16 KB (all rows, QS quarters of one 128-byte span of
+// the packed rows), double-buffered and shared by the four waves, and the group sums of x are
+// reduced from the staged registers on the way. The wave's S and ZS rows sit in LDS for the
+// whole K loop. The packed stream is loaded one span ahead, after the next stage of x, so that
+// waiting for x never waits for packed bytes that are not needed yet (loads retire in order).
+// The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
+// sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions.
+#include "dequant.h"
+#include "host_util.h"
+
+namespace i2h {
+namespace {
+
+constexpr int kTileThreads = 256;
+constexpr int kNT = 4;     // 16-column MFMA tiles per wave: one 64-column block
+constexpr int kTRow = 65;  // floats per row of a wave's transposed block (odd: no bank conflicts)
+
+template <int MT>
+struct Tile {
+  static constexpr int MR = 16 * MT;                          // rows of x held per launch
+  static constexpr int QS = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // quarters per x stage
+  static constexpr int SPS = 4 / QS;                          // x stages per 128-byte span
+  static constexpr int RS = QS * 256 + 16;                    // LDS bytes per staged x row (padded)
+  static constexpr int XBUF = MR * RS;                        // bytes of one x stage buffer
+  static constexpr int UPT = MR * QS * 16 / kTileThreads;     // 16-byte x units per thread per stage
+  static constexpr int P = MT == 1 ? 4 : (MT == 2 ? 2 : 1);   // emit lanes per row
+};
+
+template <int MT>
+constexpr size_t tile_lds_bytes(int KG) {
+  using T = Tile<MT>;
+  const size_t loop = 2 * (size_t)T::XBUF + 2 * (size_t)T::QS * T::MR * 4 + (size_t)4 * 64 * (KG | 1) * 4;
+  const size_t emit = (size_t)4 * T::MR * kTRow * 4;
+  return loop > emit ? loop : emit;
+}
+
+// fp64 ranking key of (value, column in block): the bits 0x3FF | (ordered_key(v) << 6 | 63 - col)
+// placed in the mantissa of a double in [1, 2), so double order is (value desc, column asc).
+__device__ __forceinline__ double key_f64(float v, int c) {
+  const uint32_t u = ordered_key(v);
+  const uint32_t hi = 0x3FF00000u | (u >> 12);
+  const uint32_t lo = (u << 20) | ((uint32_t)(63 - c) << 14);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ float key_value(double k) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, k);
+  const uint32_t hi = (uint32_t)(b >> 32), lo = (uint32_t)b;
+  return from_ordered_key((hi << 12) | (lo >> 20));
+}
+__device__ __forceinline__ int key_col(double k) {
+  return 63 - (int)(((uint32_t)__builtin_bit_cast(uint64_t, k) >> 14) & 63u);
+}
+
+__device__ __forceinline__ void cx(double& a, double& b) {  // a <- larger, b <- smaller
+  const double hi = __builtin_fmax(a, b), lo = __builtin_fmin(a, b);
+  a = hi;
+  b = lo;
+}
+
+// Descending sort of 8 keys: a 19-comparator network.
+__device__ __forceinline__ void sort8(double* k) {
+  cx(k[0], k[2]); cx(k[1], k[3]); cx(k[4], k[6]); cx(k[5], k[7]);
+  cx(k[0], k[4]); cx(k[1], k[5]); cx(k[2], k[6]); cx(k[3], k[7]);
+  cx(k[0], k[1]); cx(k[2], k[3]); cx(k[4], k[5]); cx(k[6], k[7]);
+  cx(k[2], k[4]); cx(k[3], k[5]);
+  cx(k[1], k[4]); cx(k[3], k[6]);
+  cx(k[1], k[2]); cx(k[3], k[4]); cx(k[5], k[6]);
+}
+
+// a <- the 8 largest of two descending lists a, b (descending): the elementwise maximum of a and
+// reversed b is a bitonic sequence holding them, then three half-cleaner stages.
+__device__ __forceinline__ void merge_top8(double* a, const double* b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = __builtin_fmax(a[i], b[7 - i]);
+#pragma unroll
+  for (int st = 4; st > 0; st >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & st) == 0) cx(a[i], a[i + st]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Block top-kc (kc <= 8) of the wave's block for rows < M. tw[m][c] holds the block's logits
+// (-inf past column N). P lanes share a row, each ranking 64 / P of its columns; the P partial
+// top-8 lists meet through DPP quad permutes.
+template <int MR, int P>
+__device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, int kc, int64_t ld,
+                                          float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+  constexpr int V = 64 / P;
+  const int lane = threadIdx.x & 63;
+  const int row = lane / P, part = lane % P;
+  const float* tr = tw + (row < MR ? row : MR - 1) * kTRow + part * V;
+  double k[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) k[i] = key_f64(tr[i], part * V + i);
+#pragma unroll
+  for (int g = 0; g < V / 8; ++g) sort8(k + 8 * g);
+#pragma unroll
+  for (int w = 8; w < V; w <<= 1)
+#pragma unroll
+    for (int g = 0; g < V; g += 2 * w) merge_top8(k + g, k + g + w);
+  if constexpr (P >= 2) {
+    double o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = dpp_f64<0xB1>(k[i]);  // quad_perm [1,0,3,2]: lane ^ 1
+    merge_top8(k, o);
+  }
+  if constexpr (P >= 4) {
+    double o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = dpp_f64<0x4E>(k[i]);  // quad_perm [2,3,0,1]: lane ^ 2
+    merge_top8(k, o);
+  }
+  if (part == 0 && row < MR && row < M) {
+    const int64_t at = (int64_t)row * ld + (int64_t)b * kc;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < kc) {
+        const int tok = b * kBlockN + key_col(k[i]);
+        const bool ok = tok < N;
+        cand_score[at + i] = ok ? key_value(k[i]) : -__builtin_inff();
+        cand_idx[at + i] = ok ? tok : -1;
+      }
+    }
+  }
+}
+
+// Block top-kc for any kc <= 64: lane c counts the columns of its row that rank before it.
+template <int MR>
+__device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64_t ld,
+                             float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+  const int lane = threadIdx.x & 63;
+  for (int m = 0; m < M && m < MR; ++m) {
+    const float* tr = tw + m * kTRow;
+    const float v = tr[lane];
+    int rank = 0;
+    for (int j = 0; j < kBlockN; ++j) {
+      const float o = tr[j];
+      rank += (o > v) || (o == v && j < lane);
+    }
+    if (rank < kc) {
+      const int tok = b * kBlockN + lane;
+      const bool ok = tok < N;
+      const int64_t at = (int64_t)m * ld + (int64_t)b * kc + rank;
+      cand_score[at] = ok ? v : -__builtin_inff();
+      cand_idx[at] = ok ? tok : -1;
+    }
+  }
+}
+
+// Up to 32 rows two workgroups share a CU (at most 256 registers per lane); 64 rows need more
+// registers (accumulators, per-quarter partial sums, two packed spans) and run one per CU.
+template <int MT, int NGC>
+__global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
+    const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+  using T = Tile<MT>;
+  constexpr int K = NGC * 512, Q = K / 4, NG = NGC, KG = K / kGroup, KGP = KG | 1;
+  constexpr int NST = NG * T::SPS;
+  constexpr int SZU = (64 * KG / 8 + 63) / 64;  // 16-byte units of the wave's S rows per lane
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* xbuf = lds;                                                   // [2][MR][RS]
+  float* xsb = reinterpret_cast<float*>(lds + 2 * T::XBUF);              // [2][QS][MR]
+  uint32_t* szl = reinterpret_cast<uint32_t*>(xsb + 2 * T::QS * T::MR);  // [4][64][KGP]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, h = lane >> 4;
+  const int b = blockIdx.x * 4 + wave;  // this wave's block; >= nblk only in the last workgroup
+  const int n0 = b * kBlockN;
+
+  // --- x stages: unit u = tid + 256 i is 16 bytes (8 k) of row m, quarter t0 + q; the 16 units of
+  // a (row, quarter) group sit in 16 consecutive lanes
+  u32x4 xr[T::UPT];
+  float xsr = 0.f;
+  auto x_load = [&](int st) {
+    const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
+#pragma unroll
+    for (int i = 0; i < T::UPT; ++i) {
+      const int u = tid + i * kTileThreads, j = u & 15, gq = u >> 4;
+      const int q = gq % T::QS, m = gq / T::QS;
+      xr[i] = m < M ? ld16(x + (int64_t)m * K + (t0 + q) * Q + gb * kGroup + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (xs != nullptr && tid < T::QS * T::MR) {
+      const int q = tid / T::MR, m = tid % T::MR;
+      xsr = m < M ? xs[(int64_t)m * KG + (t0 + q) * NG + gb] : 0.f;
+    }
+  };
+  auto x_put = [&](int st) {
+    uint8_t* xb = xbuf + (st & 1) * T::XBUF;
+    float* xsd = xsb + (st & 1) * T::QS * T::MR;
+#pragma unroll
+    for (int i = 0; i < T::UPT; ++i) {
+      const int u = tid + i * kTileThreads, j = u & 15, gq = u >> 4;
+      const int q = gq % T::QS, m = gq / T::QS;
+      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(xr[i]);
+      if (xs == nullptr) {
+        float sm = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sm += bf16_lo(xr[i][e]) + bf16_hi(xr[i][e]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+        if (j == 0) xsd[q * T::MR + m] = sm;
+      }
+    }
+    if (xs != nullptr && tid < T::QS * T::MR) xsd[tid] = xsr;
+  };
+
+  // --- packed rows of the wave's four tiles (rows past N read row N - 1; never emitted)
+  const uint8_t* prow[kNT];
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int n = n0 + 16 * nt + col;
+    prow[nt] = packed + (int64_t)(n < N ? n : N - 1) * Q + 32 * h;
+  }
+  u32x4 ring[2][kNT][2];
+  auto ring_load = [&](int gb) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      ring[gb & 1][nt][0] = ld16(prow[nt] + gb * kGroup);
+      ring[gb & 1][nt][1] = ld16(prow[nt] + gb * kGroup + 16);
+    }
+  };
+
+  // --- prologue: x stage 0, the wave's S/ZS rows, span 0 of the packed rows (in that order)
+  x_load(0);
+  const int rows_valid = N - n0 < kBlockN ? (N - n0 > 0 ? N - n0 : 0) : kBlockN;
+  const int tot = rows_valid * KG;
+  const uint16_t* Sb = S + (int64_t)(n0 < N ? n0 : 0) * KG;
+  const uint16_t* Zb = ZS + (int64_t)(n0 < N ? n0 : 0) * KG;
+  u32x4 sv[SZU], zv[SZU];
+#pragma unroll
+  for (int i = 0; i < SZU; ++i) {
+    const int e0 = 8 * (lane + 64 * i);
+    sv[i] = u32x4{0u, 0u, 0u, 0u};
+    zv[i] = u32x4{0u, 0u, 0u, 0u};
+    if (e0 + 8 <= tot) {
+      sv[i] = ld16(Sb + e0);
+      zv[i] = ld16(Zb + e0);
+    } else if (e0 < tot) {
+      for (int j = 0; j < 8; ++j)
+        if (e0 + j < tot) {
+          sv[i][j >> 1] |= (uint32_t)Sb[e0 + j] << (16 * (j & 1));
+          zv[i][j >> 1] |= (uint32_t)Zb[e0 + j] << (16 * (j & 1));
+        }
+    }
+  }
+  ring_load(0);
+  x_put(0);
+  uint32_t* szw = szl + wave * 64 * KGP;  // this wave's rows: [64][KGP], S | ZS << 16
+#pragma unroll
+  for (int i = 0; i < SZU; ++i) {
+    const int e0 = 8 * (lane + 64 * i);
+    if (e0 < 64 * KG) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = e0 + j, r = e / KG, g = e - r * KG;
+        const uint32_t s16 = (sv[i][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        const uint32_t z16 = (zv[i][j >> 1] >> (16 * (j & 1))) & 0xffffu;
+        szw[r * KGP + g] = s16 | (z16 << 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  // --- K loop
+  f32x4 acc[MT][kNT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const DqConst dqc = dq_const();
+  const uint32_t* szc = szw + col * KGP;
+
+  auto compute = [&](int st) {
+    const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
+    const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + 64 * h;
+    const float* xsd = xsb + (st & 1) * T::QS * T::MR;
+    // dw: the span's packed dwords per tile; hw = dw >> 8, kept for the whole stage when the
+    // registers allow (16 rows), else formed at each use
+    constexpr bool kKeepHw = MT == 1;
+    uint32_t dw[kNT][8], hw[kNT][8];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dw[nt][i] = ring[gb & 1][nt][0][i];
+        dw[nt][4 + i] = ring[gb & 1][nt][1][i];
+        if constexpr (kKeepHw) {
+          hw[nt][i] = dw[nt][i] >> 8;
+          hw[nt][4 + i] = dw[nt][4 + i] >> 8;
+        }
+      }
+#pragma unroll
+    for (int qq = 0; qq < T::QS; ++qq) {
+      const int t = t0 + qq;
+      f32x4 p[MT][kNT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) p[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 a[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + qq * 256 + 16 * s);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          pin(dw[nt][2 * s]);
+          pin(dw[nt][2 * s + 1]);
+          if constexpr (kKeepHw) {
+            pin(hw[nt][2 * s]);
+            pin(hw[nt][2 * s + 1]);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const uint32_t d0 = dw[nt][2 * s], d1 = dw[nt][2 * s + 1];
+          const uint32_t h0 = kKeepHw ? hw[nt][2 * s] : d0 >> 8, h1 = kKeepHw ? hw[nt][2 * s + 1] : d1 >> 8;
+          bf16x8 bw;
+          if (t == 0) bw = dequant8_mask<0>(d0, d1, h0, h1, dqc);
+          else if (t == 1) bw = dequant8_mask<1>(d0, d1, h0, h1, dqc);
+          else if (t == 2) bw = dequant8_mask<2>(d0, d1, h0, h1, dqc);
+          else bw = dequant8_mask<3>(d0, d1, h0, h1, dqc);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            p[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt],
+                                                                0, 0, 0);
+        }
+        // the scheduler may not pull later slices (their x fragments and dequant) into this one
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const int gi = t * NG + gb;
+      float s2[kNT], z2[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        const uint32_t w = szc[16 * nt * KGP + gi];
+        const float sc = __uint_as_float(w << 16), zc = __uint_as_float(w & 0xffff0000u);
+        s2[nt] = kBiasF[t] * sc;
+        z2[nt] = fmaf(kBiasF[t] - 1.f, sc, zc);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsd + qq * T::MR + 16 * mt + 4 * h);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = fmaf(s2[nt], p[mt][nt][r], acc[mt][nt][r]);
+            acc[mt][nt][r] = fmaf(-xv[r], z2[nt], a);
+          }
+      }
+      // the accumulators are complete here: without this the compiler sinks the scaling of every
+      // quarter towards the epilogue and keeps all partial sums alive until then
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) asm volatile("" : "+v"(acc[mt][nt]));
+    }
+  };
+
+#pragma unroll
+  for (int gb = 0; gb < NG; ++gb) {
+#pragma unroll
+    for (int ss = 0; ss < T::SPS; ++ss) {
+      const int st = gb * T::SPS + ss;
+      if (st + 1 < NST) x_load(st + 1);
+      if (ss == 0 && gb + 1 < NG) ring_load(gb + 1);
+      // loads stay where they are issued: hoisted further they would hold registers for nothing
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st);
+      if (st + 1 < NST) {
+        x_put(st + 1);
+        __syncthreads();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // --- epilogue: acc[mt][nt][r] is c[m = 16 mt + 4 h + r][n = n0 + 16 nt + col]
+  if (y != nullptr) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 16 * mt + 4 * h + r, n = n0 + 16 * nt + col;
+          if (m < M && n < N) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[mt][nt][r]);
+        }
+  }
+  __syncthreads();  // every wave is done with the x stages and S/ZS: the transpose reuses them
+  float* tw = reinterpret_cast<float*>(lds) + wave * T::MR * kTRow;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * mt + 4 * h + r, c = 16 * nt + col;
+        tw[m * kTRow + c] = n0 + c < N ? acc[mt][nt][r] : -__builtin_inff();
+      }
+  __syncthreads();
+  if (b >= nblk) return;
+  const int64_t ld = (int64_t)nblk * kc;
+  if (kc <= 8)
+    emit_top8<T::MR, T::P>(tw, M, b, N, kc, ld, cand_score, cand_idx);
+  else
+    emit_counted<T::MR>(tw, M, b, N, kc, ld, cand_score, cand_idx);
+}
+
+template <int MT, int NGC>
+int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+                const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  const int nblk = (int)nblk_of(N);
+  const size_t lds = tile_lds_bytes<MT>(NGC * 4);
+  hipLaunchKernelGGL((coarse_tile_kernel<MT, NGC>), dim3((unsigned)((nblk + 3) / 4)), dim3(kTileThreads), lds, s,
+                     x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, y);
+  return check_launch();
+}
+
+template <int NGC>
+int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+              const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  if (M <= 16) return launch_tile<1, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  if (M <= 32) return launch_tile<2, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  return launch_tile<4, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+}
+
+}  // namespace
+
+bool tile_supported(int64_t M, int64_t K) { return M >= 1 && M <= kTileMaxRows && (K == 512 || K == 5120); }
+
+int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
+                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
+                hipStream_t s) {
+  if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
+  if (K == 5120) return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+  return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+}
+
+}  // namespace i2h

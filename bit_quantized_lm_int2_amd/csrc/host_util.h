@@ -28,6 +28,14 @@ inline int64_t nblk_of(int64_t N) { return (N + I2H_BLOCK_N - 1) / I2H_BLOCK_N; 
 // head needs no separate group-sum launch (coarse_launch then accepts xs == nullptr).
 bool coarse_sums_x(int64_t M, int64_t K);
 
+// The many-row coarse kernel (coarse_tile.hip): up to kTileMaxRows rows of x per launch, for the
+// K it is built for; it sums the groups of x itself when xs is null.
+constexpr int64_t kTileMaxRows = 64;
+bool tile_supported(int64_t M, int64_t K);
+int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
+                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
+                hipStream_t s);
+
 // Entry points used by i2h_head (same checks and kernels as the exported calls).
 int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s);
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,

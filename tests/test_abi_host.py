@@ -58,10 +58,14 @@ def test_coarse_sums_x():
     lib = i2h.lib()
     assert lib.i2h_coarse_sums_x(1, 5120) == 1
     assert lib.i2h_coarse_sums_x(4, 5120) == 1
-    assert lib.i2h_coarse_sums_x(16, 5120) == 0
+    assert lib.i2h_coarse_sums_x(16, 5120) == 1   # the many-row kernel sums x itself
+    assert lib.i2h_coarse_sums_x(64, 5120) == 1
+    assert lib.i2h_coarse_sums_x(130, 512) == 1   # chunks of 64, 64 and 2 rows
+    assert lib.i2h_coarse_sums_x(16, 1024) == 0   # a K the many-row kernel is not built for
+    assert lib.i2h_coarse_sums_x(4, 16384) == 0   # x does not fit in LDS
     assert lib.i2h_coarse_sums_x(1, 1000) == 0
     c = lib.i2h_coarse_topk
-    assert c(P, None, 16, P, P, P, 4096, 5120, 8, P, P, None, None) == ARG  # xs required here
+    assert c(P, None, 16, P, P, P, 4096, 1024, 8, P, P, None, None) == ARG  # xs required here
     r = lib.i2h_rerank_topk
     assert r(P, 1, P, 512, 4096, 512, P, 32, 33, None, P, P, None) == LIMIT
     assert r(P, 1, P, 512, 4096, 512, P, 65, 1, None, P, P, None) == ARG     # exact needed for R > 64

@@ -277,6 +277,10 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (130, 700, 512, 4, 16, 4),     # more rows than one launch holds
     (5, 4096, 16384, 8, 32, 1),    # largest K
     (2, 2000, 512, 1, 1, 1),       # one candidate per block, one reranked token
+    (9, 4133, 512, 8, 32, 16),     # many-row kernel, 16-row tile, ragged tail block
+    (16, 130, 5120, 8, 16, 1),     # three blocks: one workgroup with an idle wave
+    (24, 3001, 5120, 12, 64, 16),  # 32-row tile; kcand above 8 (counted emit)
+    (40, 1000, 512, 3, 16, 4),     # 64-row tile, three candidates per block
 ])
 def test_head_parity(i2h, M, N, K, kc, R, k):
     say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
