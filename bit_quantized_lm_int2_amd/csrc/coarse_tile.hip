@@ -20,26 +20,28 @@
 namespace i2h {
 namespace {
 
-constexpr int kTileThreads = 256;
 constexpr int kNT = 4;     // 16-column MFMA tiles per wave: one 64-column block
 constexpr int kTRow = 65;  // floats per row of a wave's transposed block (odd: no bank conflicts)
 
-template <int MT>
+// WAVES waves per workgroup, one 64-column block each: every x stage loaded into LDS serves
+// 64 * WAVES columns, so more waves mean fewer re-reads of x per packed byte.
+template <int MT, int WAVES>
 struct Tile {
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int MR = 16 * MT;                          // rows of x held per launch
   static constexpr int QS = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // quarters per x stage
   static constexpr int SPS = 4 / QS;                          // x stages per 128-byte span
   static constexpr int RS = QS * 256 + 16;                    // LDS bytes per staged x row (padded)
   static constexpr int XBUF = MR * RS;                        // bytes of one x stage buffer
-  static constexpr int UPT = MR * QS * 16 / kTileThreads;     // 16-byte x units per thread per stage
+  static constexpr int UPT = MR * QS * 16 / THREADS;          // 16-byte x units per thread per stage
   static constexpr int P = MT == 1 ? 4 : (MT == 2 ? 2 : 1);   // emit lanes per row
 };
 
-template <int MT>
+template <int MT, int WAVES>
 constexpr size_t tile_lds_bytes(int KG) {
-  using T = Tile<MT>;
-  const size_t loop = 2 * (size_t)T::XBUF + 2 * (size_t)T::QS * T::MR * 4 + (size_t)4 * 64 * (KG | 1) * 4;
-  const size_t emit = (size_t)4 * T::MR * kTRow * 4;
+  using T = Tile<MT, WAVES>;
+  const size_t loop = 2 * (size_t)T::XBUF + 2 * (size_t)T::QS * T::MR * 4 + (size_t)WAVES * 64 * (KG | 1) * 4;
+  const size_t emit = (size_t)WAVES * T::MR * kTRow * 4;
   return loop > emit ? loop : emit;
 }
 
@@ -166,13 +168,16 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
 
 // Up to 32 rows two workgroups share a CU (at most 256 registers per lane); 64 rows need more
 // registers (accumulators, per-quarter partial sums, two packed spans) and run one per CU.
-template <int MT, int NGC>
-__global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_kernel(
+// XPF: x stages loaded ahead of the one being stored; RPF: packed spans loaded ahead of the one in
+// use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
+// arrives with HBM latency; both are therefore fetched more than one stage ahead.
+template <int MT, int WAVES, int NGC, int XPF, int RPF>
+__global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
     int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
-  using T = Tile<MT>;
+  using T = Tile<MT, WAVES>;
   constexpr int K = NGC * 512, Q = K / 4, NG = NGC, KG = K / kGroup, KGP = KG | 1;
   constexpr int NST = NG * T::SPS;
   constexpr int SZU = (64 * KG / 8 + 63) / 64;  // 16-byte units of the wave's S rows per lane
@@ -182,44 +187,54 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
   uint32_t* szl = reinterpret_cast<uint32_t*>(xsb + 2 * T::QS * T::MR);  // [4][64][KGP]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
-  const int b = blockIdx.x * 4 + wave;  // this wave's block; >= nblk only in the last workgroup
+  const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
   const int n0 = b * kBlockN;
 
   // --- x stages: unit u = tid + 256 i is 16 bytes (8 k) of row m, quarter t0 + q; the 16 units of
-  // a (row, quarter) group sit in 16 consecutive lanes
-  u32x4 xr[T::UPT];
-  float xsr = 0.f;
-  auto x_load = [&](int st) {
+  // a (row, quarter) group sit in 16 consecutive lanes. Every load is issued unconditionally (rows
+  // past M read row M - 1 and are zeroed when stored): a load under a branch makes the compiler's
+  // wait counts assume it may not have been issued, and every later wait then also waits for it.
+  // xsrc is xs, or when own_sums x itself read at one address (the value is unused).
+  const bool own_sums = xs == nullptr;
+  const float* xsrc = own_sums ? reinterpret_cast<const float*>(x) : xs;
+  u32x4 xr[XPF][T::UPT];
+  float xsr[XPF];
+  // load i < UPT of stage st: unit i of x; i == UPT: the group sum (when given)
+  auto x_load_one = [&](int st, int i) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
-#pragma unroll
-    for (int i = 0; i < T::UPT; ++i) {
-      const int u = tid + i * kTileThreads, j = u & 15, gq = u >> 4;
+    if (i < T::UPT) {
+      const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
       const int q = gq % T::QS, m = gq / T::QS;
-      xr[i] = m < M ? ld16(x + (int64_t)m * K + (t0 + q) * Q + gb * kGroup + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+      const int mm = m < M ? m : M - 1;
+      xr[st % XPF][i] = ld16(x + (int64_t)mm * K + (t0 + q) * Q + gb * kGroup + 8 * j);
+    } else {
+      const int q = (tid / T::MR) % T::QS, m = tid % T::MR;
+      xsr[st % XPF] = xsrc[own_sums ? 0 : (int64_t)(m < M ? m : M - 1) * KG + (t0 + q) * NG + gb];
     }
-    if (xs != nullptr && tid < T::QS * T::MR) {
-      const int q = tid / T::MR, m = tid % T::MR;
-      xsr = m < M ? xs[(int64_t)m * KG + (t0 + q) * NG + gb] : 0.f;
-    }
+  };
+  auto x_load = [&](int st) {
+#pragma unroll
+    for (int i = 0; i <= T::UPT; ++i) x_load_one(st, i);
   };
   auto x_put = [&](int st) {
     uint8_t* xb = xbuf + (st & 1) * T::XBUF;
     float* xsd = xsb + (st & 1) * T::QS * T::MR;
 #pragma unroll
     for (int i = 0; i < T::UPT; ++i) {
-      const int u = tid + i * kTileThreads, j = u & 15, gq = u >> 4;
+      const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
       const int q = gq % T::QS, m = gq / T::QS;
-      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(xr[i]);
-      if (xs == nullptr) {
+      const u32x4 v = m < M ? xr[st % XPF][i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(v);
+      if (own_sums) {
         float sm = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sm += bf16_lo(xr[i][e]) + bf16_hi(xr[i][e]);
+        for (int e = 0; e < 4; ++e) sm += bf16_lo(v[e]) + bf16_hi(v[e]);
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
         if (j == 0) xsd[q * T::MR + m] = sm;
       }
     }
-    if (xs != nullptr && tid < T::QS * T::MR) xsd[tid] = xsr;
+    if (!own_sums && tid < T::QS * T::MR) xsd[tid] = tid % T::MR < M ? xsr[st % XPF] : 0.f;
   };
 
   // --- packed rows of the wave's four tiles (rows past N read row N - 1; never emitted)
@@ -227,18 +242,35 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int n = n0 + 16 * nt + col;
-    prow[nt] = packed + (int64_t)(n < N ? n : N - 1) * Q + 32 * h;
+    prow[nt] = packed + (int64_t)(n < N ? n : N - 1) * Q + 16 * h;
   }
-  u32x4 ring[2][kNT][2];
+  constexpr int kSlots = RPF + 1;  // spans RPF ahead of the one in use
+  u32x4 ring[kSlots][kNT][2];
+  auto ring_load_one = [&](int gb, int k) {  // k = 2 nt + half
+    ring[gb % kSlots][k >> 1][k & 1] = ld16(prow[k >> 1] + gb * kGroup + 64 * (k & 1));
+  };
   auto ring_load = [&](int gb) {
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      ring[gb & 1][nt][0] = ld16(prow[nt] + gb * kGroup);
-      ring[gb & 1][nt][1] = ld16(prow[nt] + gb * kGroup + 16);
+    for (int k = 0; k < 2 * kNT; ++k) ring_load_one(gb, k);
+  };
+  // The loads stage st issues for later stages, in this order: x stage st + XPF (UPT units and the
+  // group sums), then, at the first stage of span gb, the packed span gb + RPF. They are spread
+  // over the stage's MFMA slices: issued as one burst, they stall the wave at issue while the
+  // memory pipeline drains, with the current stage's operands already in registers.
+  constexpr int kStageLoads = T::UPT + 1 + 2 * kNT;
+  constexpr int kPerSlice = (kStageLoads + 4 * T::QS - 1) / (4 * T::QS);
+  auto stage_load = [&](int st, int k) {
+    const int gb = st / T::SPS, ss = st % T::SPS;
+    const int nx = st + XPF < NST ? T::UPT + 1 : 0;
+    if (k < nx) {
+      x_load_one(st + XPF, k);
+    } else if (ss == 0 && gb + RPF < NG && k - nx < 2 * kNT) {
+      ring_load_one(gb + RPF, k - nx);
     }
   };
 
-  // --- prologue: x stage 0, the wave's S/ZS rows, span 0 of the packed rows (in that order)
+  // --- prologue: x stage 0, the wave's S/ZS rows, the first packed spans, the next x stages (in
+  // that order)
   x_load(0);
   const int rows_valid = N - n0 < kBlockN ? (N - n0 > 0 ? N - n0 : 0) : kBlockN;
   const int tot = rows_valid * KG;
@@ -261,7 +293,10 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
         }
     }
   }
-  ring_load(0);
+#pragma unroll
+  for (int g = 0; g < RPF && g < NG; ++g) ring_load(g);
+#pragma unroll
+  for (int st = 1; st < XPF && st < NST; ++st) x_load(st);
   x_put(0);
   uint32_t* szw = szl + wave * 64 * KGP;  // this wave's rows: [64][KGP], S | ZS << 16
 #pragma unroll
@@ -290,7 +325,7 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
 
   auto compute = [&](int st) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
-    const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + 64 * h;
+    const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + 32 * h;
     const float* xsd = xsb + (st & 1) * T::QS * T::MR;
     // dw: the span's packed dwords per tile; hw = dw >> 8, kept for the whole stage when the
     // registers allow (16 rows), else formed at each use
@@ -300,8 +335,8 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dw[nt][i] = ring[gb & 1][nt][0][i];
-        dw[nt][4 + i] = ring[gb & 1][nt][1][i];
+        dw[nt][i] = ring[gb % kSlots][nt][0][i];
+        dw[nt][4 + i] = ring[gb % kSlots][nt][1][i];
         if constexpr (kKeepHw) {
           hw[nt][i] = dw[nt][i] >> 8;
           hw[nt][4 + i] = dw[nt][4 + i] >> 8;
@@ -320,7 +355,7 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
         u32x4 a[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + qq * 256 + 16 * s);
+          a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + qq * 256 + 16 * (s & 1) + 128 * (s >> 1));
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           pin(dw[nt][2 * s]);
@@ -344,6 +379,8 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
             p[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt],
                                                                 0, 0, 0);
         }
+#pragma unroll
+        for (int j = 0; j < kPerSlice; ++j) stage_load(st, (qq * 4 + s) * kPerSlice + j);
         // the scheduler may not pull later slices (their x fragments and dequant) into this one
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -381,9 +418,6 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
 #pragma unroll
     for (int ss = 0; ss < T::SPS; ++ss) {
       const int st = gb * T::SPS + ss;
-      if (st + 1 < NST) x_load(st + 1);
-      if (ss == 0 && gb + 1 < NG) ring_load(gb + 1);
-      // loads stay where they are issued: hoisted further they would hold registers for nothing
       __builtin_amdgcn_sched_barrier(0);
       compute(st);
       if (st + 1 < NST) {
@@ -426,22 +460,52 @@ __global__ __launch_bounds__(kTileThreads, MT <= 2 ? 2 : 1) void coarse_tile_ker
     emit_counted<T::MR>(tw, M, b, N, kc, ld, cand_score, cand_idx);
 }
 
-template <int MT, int NGC>
+// Loads ahead: x one stage, the packed stream one span (measured best for the 16-row tile).
+#ifndef I2H_TILE_XPF
+#define I2H_TILE_XPF 1
+#endif
+#ifndef I2H_TILE_RPF
+#define I2H_TILE_RPF 1
+#endif
+
+template <int MT, int WAVES, int NGC>
 int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                 const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
-  const size_t lds = tile_lds_bytes<MT>(NGC * 4);
-  hipLaunchKernelGGL((coarse_tile_kernel<MT, NGC>), dim3((unsigned)((nblk + 3) / 4)), dim3(kTileThreads), lds, s,
-                     x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, y);
+  const size_t lds = tile_lds_bytes<MT, WAVES>(NGC * 4);
+  hipLaunchKernelGGL((coarse_tile_kernel<MT, WAVES, NGC, I2H_TILE_XPF, I2H_TILE_RPF>),
+                     dim3((unsigned)((nblk + WAVES - 1) / WAVES)), dim3(64 * WAVES), lds, s, x, xs, M, packed, S, ZS, N,
+                     kc, nblk, cs, ci, y);
   return check_launch();
 }
+
+#ifndef I2H_TILE_WAVES
+#define I2H_TILE_WAVES 8
+#endif
+// Tiles above 16 rows re-read x (from L2, or beyond it when the packed stream evicts it) for
+// every 64 * WAVES columns, and measure slower than running the 16-row tile per 16 rows, which
+// re-reads the packed stream instead: by default rows go through the 16-row tile.
+#ifndef I2H_TILE_MAXMT
+#define I2H_TILE_MAXMT 1
+#endif
 
 template <int NGC>
 int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
               const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
-  if (M <= 16) return launch_tile<1, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
-  if (M <= 32) return launch_tile<2, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
-  return launch_tile<4, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  if constexpr (I2H_TILE_MAXMT >= 2)
+    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  if constexpr (I2H_TILE_MAXMT >= 4) return launch_tile<4, 4, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  // rows in chunks of 16 through the 16-row tile
+  const int64_t ld = nblk_of(N) * kc, KG = NGC * 4;
+  for (int m0 = 0; m0 < M; m0 += 16) {
+    const int mc = M - m0 < 16 ? M - m0 : 16;
+    const int st = launch_tile<1, I2H_TILE_WAVES, NGC>(x + (int64_t)m0 * NGC * 512, xs ? xs + (int64_t)m0 * KG : nullptr,
+                                                       mc, packed, S, ZS, N, kc, cs + m0 * ld, ci + m0 * ld,
+                                                       y ? y + (int64_t)m0 * N : nullptr, s);
+    if (st != I2H_OK) return st;
+  }
+  return I2H_OK;
 }
 
 }  // namespace
