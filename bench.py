@@ -1,6 +1,7 @@
 """Benchmark of the int2 draft LM head on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bands]
+    python bench.py --traffic-probe    # short run for rocprofv3 counter passes (see below)
 
 A step is one call of the head's per-call path over one batch: the coarse int2 pass with its
 fused block top-8 emit (which sums the groups of x itself at this M), the top-32 selection, and
@@ -61,17 +62,20 @@ def head_bytes(M, N, K, kc=KC, R_=R, k=1, own_sums=False):
     return b
 
 
+COARSE_SOURCES = ("coarse.hip", "coarse_tile.hip", "dequant.h", "device_util.h")
+
+
 def coarse_source_hash():
     h = hashlib.sha256()
-    for name in ("coarse.hip", "device_util.h"):
+    for name in COARSE_SOURCES:
         with open(os.path.join(ROOT, "bit_quantized_lm_int2_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def traffic_for(M):
-    """HBM bytes per coarse launch from the committed rocprofv3 counter runs, if they were
-    taken on the current coarse kernel source; else None."""
+    """HBM bytes (read + write) per coarse call from the committed rocprofv3 counter runs, if they
+    were taken on the current coarse kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -79,7 +83,7 @@ def traffic_for(M):
         return None
     if t.get("source_hash") != coarse_source_hash():
         return None
-    return t.get("per_launch_bytes", {}).get(str(M))
+    return t.get("per_call_bytes", {}).get(str(M))
 
 
 class Head:
@@ -128,6 +132,19 @@ class Head:
         if st:
             raise RuntimeError(f"libi2h status {st}")
 
+    def coarse_only(self, torch, n, first=0):
+        """Mean time of n back-to-back coarse launches (rotating cold copies), by HIP events on the
+        launch stream: the per-launch duration the roofline uses."""
+        L = self.lib
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            if L.i2h_coarse_topk(*self.a_coarse[(first + i) % len(self.a_coarse)]):
+                raise RuntimeError("libi2h coarse launch failed")
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
     def fused(self, i):
         st = self.lib.i2h_head(*self.a_head[i % len(self.a_head)])
         if st:
@@ -160,6 +177,33 @@ def to_dev_bits(torch, np, b, dev):
     return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+def traffic_probe(torch, i2h, si, dev):
+    """Launches for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: the coarse kernel on the timed
+    workload at M = 1, 16, 64 (cold weight copies, 6 launches each), and a plain device copy of a
+    512 MiB buffer (4 launches) whose counter readings give the bytes-per-count factor."""
+    cfg = si.WORKLOADS[WORKLOAD]
+    K, N = cfg["K"], cfg["N"]
+    W = si.gen_weight(N, K).to(dev)
+    packed, S, ZS = i2h.pack(W)
+    del W
+    copies = [(packed, S, ZS)] + [(packed.clone(), S.clone(), ZS.clone()) for _ in range(COPIES - 1)]
+    x_all = si.gen_x(64, K, outliers=cfg["outliers"]).to(dev)
+    for M in (1, 16, 64):
+        x = x_all[:M].contiguous()
+        xs = None if i2h.coarse_sums_x(M, K) else i2h.xsum(x)
+        for i in range(6):
+            p, a, b = copies[(i * 5 + M) % COPIES]
+            i2h.coarse_topk(x, xs, p, a, b, kcand=KC)
+        torch.cuda.synchronize()
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(), "M": [1, 16, 64]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +211,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bands", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the coarse kernel 6 times per M in (1, 16, 64) on cold weight copies, "
+                         "then copy a 512 MiB buffer 4 times (the calibration kernel for HBM byte counters)")
     ap.add_argument("--match-rows", type=int, default=32)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -182,6 +229,9 @@ def main():
 
     i2h.lib()
     dev = torch.device("cuda:0")
+    if args.traffic_probe:
+        traffic_probe(torch, i2h, si, dev)
+        return
     cfg = si.WORKLOADS[WORKLOAD]
     M, K, N = cfg["M"], cfg["K"], cfg["N"]
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
@@ -212,8 +262,10 @@ def main():
     def measure(Mb, steps, warmup):
         x = x_all[:Mb].contiguous()
         h = Head(i2h, torch, x, copies, W, Mb, N, K)
-        dt, coarse_ms = time_steps(torch, h.step, steps, warmup, events=True)
+        dt, _ = time_steps(torch, h.step, steps, warmup)
         dt_fused, _ = time_steps(torch, h.fused, steps, warmup)
+        h.coarse_only(torch, warmup)
+        coarse_ms = h.coarse_only(torch, steps, warmup) * 1e-3
         torch.cuda.synchronize()
         return h, dt, coarse_ms, dt_fused
 
