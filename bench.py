@@ -4,10 +4,10 @@
     python bench.py --traffic-probe    # short run for rocprofv3 counter passes (see below)
 
 A step is one call of the head's per-call path over one batch: the coarse int2 pass with its
-fused block top-8 emit (which sums the groups of x itself at this M), the top-32 selection, and
-the exact bf16 rerank with the argmax, enqueued on one stream with no host synchronisation.
-These are the kernels i2h_head runs; the step enqueues them through the separate entry points
-so that HIP events can bracket the coarse kernel. The single-call entry is timed beside it. The workload is one rank's
+fused block top-8 emit (which sums the groups of x itself), then the top-32 selection, exact
+bf16 rerank and argmax in one kernel, enqueued on one stream with no host synchronisation.
+These are the kernels i2h_head runs, enqueued through their own entry points; the single-call
+entry is timed beside it. The coarse kernel is also timed alone, back to back, for the roofline. The workload is one rank's
 vocab slice, x[1, 5120] @ W[5120, 124160] (the draft-slot shape), with inputs resident in HBM.
 The stored head (packed codes + scales, 178.8 MB) fits in the 256 MB last-level cache, so the
 steps rotate over COPIES independent copies of it (2.1 GB) and every step reads its copy from
@@ -116,6 +116,8 @@ class Head:
         self.a_select = (P(self.cs), P(self.ci), M, nblk, KC, R, P(self.sel), s)
         self.a_rerank = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, 1, P(self.ex), P(self.oi),
                          P(self.ov), s)
+        self.a_srr = (P(self.cs), P(self.ci), M, nblk, KC, R, P(x), P(W), W.stride(0), N, K, 1, None, None,
+                      P(self.oi), P(self.ov), s)
         self.a_head = [(P(x), M, P(p), P(S), P(Z), P(W), W.stride(0), N, K, KC, R, 1, P(self.oi), P(self.ov),
                         None, P(self.ws), ws_n, s) for (p, S, Z) in copies]
 
@@ -127,8 +129,7 @@ class Head:
         st |= L.i2h_coarse_topk(*self.a_coarse[i % len(self.a_coarse)])
         if ev1 is not None:
             ev1.record()
-        st |= L.i2h_select(*self.a_select)
-        st |= L.i2h_rerank_topk(*self.a_rerank)
+        st |= L.i2h_select_rerank_topk(*self.a_srr)
         if st:
             raise RuntimeError(f"libi2h status {st}")
 

@@ -16,7 +16,8 @@ import os
 import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
-           "rerank", "finalize", "rerank_topk", "coarse_sums_x", "workspace_bytes", "head", "GROUP",
+           "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
+           "GROUP",
            "BLOCK_N"]
 
 GROUP = 128
@@ -42,6 +43,8 @@ _SIGNATURES = {
     "i2h_workspace_bytes": ([_I64, _I64, _I64, _INT, _INT], _I64),
     "i2h_coarse_sums_x": ([_I64, _I64], _INT),
     "i2h_rerank_topk": ([_P, _I64, _P, _I64, _I64, _I64, _P, _INT, _INT, _P, _P, _P, _P], _INT),
+    "i2h_select_rerank_topk": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P, _P,
+                                _P], _INT),
     "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
                   _I64, _P], _INT),
 }
@@ -262,6 +265,35 @@ def rerank_topk(x, W, sel, k: int = 1, exact: torch.Tensor | None = None):
     _check("i2h_rerank_topk", lib().i2h_rerank_topk(_ptr(x), M, _ptr(W), _rows(W, "W"), W.shape[0], K, _ptr(sel),
                                                     R, k, _ptr(exact), _ptr(oi), _ptr(ov), _stream(x)))
     return oi, ov
+
+
+def select_rerank_topk(cand_score, cand_idx, kcand: int, R: int, x, W, k: int = 1, want_sel: bool = False):
+    """Selection, exact rerank and top-k in one call: (idx int32 [M, k], val fp32 [M, k]) and, with
+    want_sel, also (sel int32 [M, R], exact fp32 [M, R])."""
+    _need(cand_score, "cand_score", torch.float32, 2)
+    _need(cand_idx, "cand_idx", torch.int32, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    for t, n in ((cand_score, "cand_score"), (cand_idx, "cand_idx"), (x, "x")):
+        _dense(t, n)
+    M, ncand = cand_score.shape
+    _shape(cand_idx, "cand_idx", (M, ncand))
+    _shape(x, "x", (M, x.shape[1]))
+    K = x.shape[1]
+    if ncand % kcand:
+        raise ValueError("candidate count is not a multiple of kcand")
+    if W.shape[1] != K:
+        raise ValueError("W must have K columns")
+    dev = x.device
+    oi = torch.empty(M, k, dtype=torch.int32, device=dev)
+    ov = torch.empty(M, k, dtype=torch.float32, device=dev)
+    sel = torch.empty(M, R, dtype=torch.int32, device=dev) if want_sel else None
+    ex = torch.empty(M, R, dtype=torch.float32, device=dev) if want_sel else None
+    _check("i2h_select_rerank_topk",
+           lib().i2h_select_rerank_topk(_ptr(cand_score), _ptr(cand_idx), M, ncand // kcand, kcand, R, _ptr(x), _ptr(W),
+                                        _rows(W, "W"), W.shape[0], K, k, _ptr(sel), _ptr(ex), _ptr(oi), _ptr(ov),
+                                        _stream(x)))
+    return (oi, ov, sel, ex) if want_sel else (oi, ov)
 
 
 def workspace_bytes(M: int, N: int, K: int, kcand: int = 8, R: int = 32) -> int:

@@ -91,7 +91,11 @@ extern "C" int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, con
   const bool own_sums = coarse_sums_x(M, K);
   int st = own_sums ? I2H_OK : xsum_launch(x, M, K, xs, s);
   if (st == I2H_OK) st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s);
-  if (st == I2H_OK) st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
+  if (st != I2H_OK) return st;
+  if (select_rerank_supported(nblk_of(N), kcand, R, N, K))
+    return select_rerank_launch(cs, ci, M, nblk_of(N), kcand, R, x, W, ldw, N, K, k, nullptr, nullptr, out_idx,
+                                out_val, s);
+  st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
   if (st == I2H_OK) st = rerank_finalize_launch(x, M, W, ldw, N, K, sel, R, k, ex, out_idx, out_val, s);
   return st;
 }

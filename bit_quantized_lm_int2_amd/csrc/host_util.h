@@ -36,6 +36,12 @@ int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* pa
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
                 hipStream_t s);
 
+// The fused selection + exact rerank + top-k kernel (select_rerank.hip) and its limits.
+bool select_rerank_supported(int64_t nblk, int kc, int R, int64_t N, int64_t K);
+int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
+                         const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
+                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s);
+
 // Entry points used by i2h_head (same checks and kernels as the exported calls).
 int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s);
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,

@@ -146,12 +146,28 @@ I2H_API int i2h_rerank_topk(const uint16_t* x, int64_t M, const uint16_t* W, int
                             int64_t K, const int32_t* sel, int R, int k, float* exact, int32_t* out_idx,
                             float* out_val, void* stream);
 
+/*
+ * i2h_select, i2h_rerank and i2h_finalize in one kernel, one workgroup per row
+ * (radiance_drafthead.py, _apply_head_int2 and _rerank_exact): the R best block candidates of each
+ * row, their exact scores against the bf16 weight rows, and the k best of those. Same arguments,
+ * layouts and results as the three calls (bit for bit): cand_score/cand_idx [M, nblk*kcand] with
+ * nblk = ceil(N/64); x bf16 [M, K]; W bf16 rows with leading dimension ldw; sel int32 [M, R] and
+ * exact fp32 [M, R] receive the selection and its exact scores when not NULL; out_idx/out_val
+ * [M, k]. Limits: 1 <= kcand <= 8, 1 <= R <= 64, 1 <= k <= R, N <= 262144 (nblk <= 4096), K a
+ * multiple of 512 up to I2H_MAX_K; outside them I2H_ERR_LIMIT (use the three calls).
+ * Alignment: x and W 16 bytes, ldw a multiple of 8, the rest 4 bytes.
+ */
+I2H_API int i2h_select_rerank_topk(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
+                                   int kcand, int R, const uint16_t* x, const uint16_t* W, int64_t ldw,
+                                   int64_t N, int64_t K, int k, int32_t* sel, float* exact, int32_t* out_idx,
+                                   float* out_val, void* stream);
+
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);
 
 /*
- * One call of the head: i2h_xsum (skipped when i2h_coarse_sums_x), i2h_coarse_topk, i2h_select
- * and i2h_rerank_topk in stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
+ * One call of the head: i2h_xsum (skipped when i2h_coarse_sums_x), i2h_coarse_topk, then
+ * i2h_select_rerank_topk within its limits, else i2h_select and i2h_rerank_topk, in stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
  * aligned, caller-owned, contents undefined afterwards). Arguments as in those calls; y may be
  * NULL. The limits of every step apply.
  */

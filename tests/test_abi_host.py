@@ -26,7 +26,8 @@ def test_header_declares_the_entry_points():
     names = set(declared())
     want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
-            "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk"}
+            "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
+            "i2h_select_rerank_topk"}
     assert names == want
 
 
@@ -154,3 +155,16 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(i2h, "_LIB_PATH", "/nonexistent/libi2h.so")
     with pytest.raises(ImportError):
         i2h.lib()
+
+
+def test_select_rerank_rejects_before_launch():
+    f = i2h.lib().i2h_select_rerank_topk
+    # cand_score, cand_idx, M, nblk, kcand, R, x, W, ldw, N, K, k, sel, exact, out_idx, out_val, stream
+    assert f(None, P, 1, 1940, 8, 32, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == ARG
+    assert f(P, P, 1, 1939, 8, 32, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == SHAPE  # nblk != ceil(N/64)
+    assert f(P, P, 1, 1940, 8, 32, P, P, 5000, 124160, 5120, 1, None, None, P, P, None) == SHAPE  # ldw < K
+    assert f(P, P, 1, 1940, 9, 32, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == LIMIT  # kcand > 8
+    assert f(P, P, 1, 1940, 8, 65, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == LIMIT  # R > 64
+    assert f(P, P, 1, 1940, 8, 32, P, P, 5120, 124160, 5120, 33, None, None, P, P, None) == LIMIT  # k > R
+    assert f(P, P, 1, 4097, 8, 32, P, P, 5120, 262145, 5120, 1, None, None, P, P, None) == LIMIT  # N too large
+    assert f(P, P, 1, 1940, 8, 32, P, P, 5124, 124160, 5120, 1, None, None, P, P, None) == ALIGN  # ldw % 8

@@ -133,6 +133,39 @@ def test_select_all_equal_scores(i2h):
     assert np.array_equal(host(got), want)
 
 
+@pytest.mark.parametrize("M,N,K,kc,R,k,grid", [
+    (1, 124160, 5120, 8, 32, 1, 0),    # the draft-slot shape: two blocks per thread
+    (3, 248320, 5120, 8, 32, 16, 0),   # the full vocabulary: four blocks per thread, top-16
+    (2, 4096, 512, 8, 32, 16, 4),      # many exact score ties
+    (2, 643, 1024, 3, 64, 64, 2),      # kcand 3; R above the number of candidates; every place
+    (4, 9000, 2048, 1, 1, 1, 0),       # one candidate per block, one token
+    (2, 70000, 16384, 8, 64, 16, 1),   # R = 64, the largest K
+])
+def test_select_rerank_fused(i2h, M, N, K, kc, R, k, grid):
+    """The fused selection + rerank + top-k against the three separate calls (bit for bit) and the
+    oracle's selection; exact scores against the fp64 dot where the weight fits on the host."""
+    say(f"select_rerank M={M} N={N} K={K} kc={kc} R={R} k={k}")
+    sc = si.gen_scores(M, N, seed=N + R + 7).numpy()
+    if grid:
+        sc = (np.round(sc * grid) / grid).astype(np.float32)
+    cs, ci = oracle.block_emit(sc.astype(np.float64), kc)
+    want_sel = oracle.select_top_r(cs, ci, R)
+    cs_d, ci_d = torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV)
+    g = torch.Generator(device=DEV).manual_seed(N + K)
+    W = (0.02 * torch.randn(N, K, generator=g, device=DEV)).to(torch.bfloat16)
+    x = torch.randn(M, K, generator=g, device=DEV).to(torch.bfloat16)
+    sel = i2h.select(cs_d, ci_d, kc, R)
+    ex = i2h.rerank(x, W, sel)
+    oi, ov = i2h.finalize(ex, sel, k)
+    fi, fv, fsel, fex = i2h.select_rerank_topk(cs_d, ci_d, kc, R, x, W, k, want_sel=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fsel), want_sel)
+    assert torch.equal(fsel, sel) and torch.equal(fex, ex), "fused selection / exact scores differ"
+    assert torch.equal(fi, oi) and torch.equal(fv, ov), "fused top-k differs"
+    if N * K <= 100_000_000:
+        pu.check_rerank(host(fex), si.bits(x), si.bits(W), host(fsel))
+
+
 @pytest.mark.parametrize("M,R,k,grid", [(3, 32, 1, 0), (3, 32, 16, 2), (2, 100, 100, 1), (4, 1024, 16, 4),
                                         (1, 1, 1, 0)])
 def test_finalize_bit_exact(i2h, M, R, k, grid):
