@@ -5,144 +5,197 @@
 // k = j, Q+j, 2Q+j, 3Q+j (Q = K/4); S = bf16(4 sc), ZS = bf16(4 sc + zp sc).
 //
 // The bytes j = 128 gb + i (i = 0..127) of span gb of a packed row draw on four quantisation
-// groups, one per quarter t (k = tQ + 128 gb + i, group t*NG + gb with NG = K/512), so one wave
-// that reads the four quarters' 128-k stretches (256 contiguous bytes each) holds every input of
-// 128 packed bytes and of four S/ZS pairs.
+// groups, one per quarter t (k = tQ + 128 gb + i, group t*NG + gb with NG = K/512), so the
+// lanes that read the four quarters' 128-k stretches (256 contiguous bytes each) hold every
+// input of 128 packed bytes and of four S/ZS pairs.
 //
 // Bit-exactness: the page evaluates these steps as separate eager fp32 kernels. This file is
 // built with -ffp-contract=off and correctly rounded fp32 division, and the pragma below keeps
-// any multiply-add from being fused.
+// any multiply-add from being fused. It is also built without NaN semantics (min / max need no
+// quieting): W must be finite.
 #include "device_util.h"
 #include "host_util.h"
 
 #pragma clang fp contract(off)
 
+#ifndef I2H_PACK_MAX_WG
+#define I2H_PACK_MAX_WG 65536  // workgroups at most (grid-stride loop beyond)
+#endif
+#ifndef I2H_PACK_STEPS
+#define I2H_PACK_STEPS 2  // loop steps per wave at least, before the cap
+#endif
+
 namespace i2h {
 namespace {
 
-// 16-lane min / max (lanes 16r .. 16r+15 hold one quantisation group): four DPP row rotations
-// (by 1, 2, 4, 8) leave every lane of the row with the reduction of all 16.
-template <int S>
-__device__ __forceinline__ float row_ror(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + S, 0xF, 0xF, true));
+// Reductions over the 4 lanes of a quad (the lanes that share one quantisation group): two DPP
+// quad permutes (lane ^ 1, lane ^ 2); built without NaN semantics, each step is one v_min/v_max
+// with a DPP operand.
+template <int CTRL>
+__device__ __forceinline__ float quad_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float row16_min(float v) {
-  v = fminf(v, row_ror<1>(v));
-  v = fminf(v, row_ror<2>(v));
-  v = fminf(v, row_ror<4>(v));
-  return fminf(v, row_ror<8>(v));
+__device__ __forceinline__ float quad_min(float v) {
+  v = fminf(v, quad_perm<0xB1>(v));
+  return fminf(v, quad_perm<0x4E>(v));
 }
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, row_ror<1>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  return fmaxf(v, row_ror<8>(v));
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, quad_perm<0xB1>(v));
+  return fmaxf(v, quad_perm<0x4E>(v));
 }
 
 __device__ __forceinline__ float clamp03(float v) { return fminf(fmaxf(v, 0.0f), 3.0f); }
 
-// The code clamp(rint(fl(fl(a / b) + c)), 0, 3) (IEEE fp32 division and addition, as the page
-// evaluates it) is first formed from fma(a, 1/b, c) with 1/b from v_rcp_f32 (at most 1 ulp): that
-// argument lies within a few ulps of the exact sum, which changes the rounded code only when the
-// sum is within that distance of a half-integer. Those cases set `near` (exact ties among them)
-// and are redone by the caller with the exact division, so the conversion of the clamped value
-// to a byte (round to nearest) never meets a tie.
-__device__ __forceinline__ float code_arg(float a, float rb, float c, bool& near) {
-  const float sm = __builtin_fmaf(a, rb, c);
-  near = near || fabsf(__builtin_amdgcn_fractf(sm) - 0.5f) < 0x1p-16f;
-  return clamp03(sm);
+// d / 3 correctly rounded (d >= 0): q = RN(d * RN(1/3)), then one FMA residual correction. The
+// residual d - 3q is exact in one FMA, and an exhaustive check over every non-negative finite
+// fp32 d (subnormals included) finds the corrected quotient equal to the IEEE quotient.
+__device__ __forceinline__ float div3_rn(float d) {
+  constexpr float kThird = 1.0f / 3.0f;
+  const float q = __fmul_rn(d, kThird);
+  return __builtin_fmaf(__builtin_fmaf(-q, 3.0f, d), kThird, q);
 }
 
-constexpr int kPackWaves = 8;
-constexpr int kPackUnroll = 4;  // rows a wave loads before it computes
+// fl(a / b) from y = fl(1 / b) (both IEEE round-to-nearest-even) with one FMA correction:
+// q0 = fl(a y) is within an ulp or two of a / b, the residual a - b q0 is exact in one FMA, and
+// fl(q0 + r y) is the correctly rounded quotient. An exhaustive check over every fp32 significand
+// of b and every bf16 significand of a (the sign and powers of two change nothing while no
+// intermediate overflows or underflows) finds no exception. For |a / b| below 2^-75 the residual
+// may underflow; such quotients are far below the 0.5 that a code can turn on.
+__device__ __forceinline__ float quot_rn(float a, float b, float y) {
+  const float q0 = __fmul_rn(a, y);
+  return __builtin_fmaf(__builtin_fmaf(-b, q0, a), y, q0);
+}
 
-// Wave w handles span gb = w % NG of rows w / NG, w / NG + rstep, ... (the grid holds a multiple
-// of NG waves, so rstep = waves / NG). Lane l = 16 t + i holds k = tQ + 128 gb + 8i .. +7 of
-// quarter t (one 16-byte load): the 16 lanes of a DPP row hold one quantisation group. Lane
-// (t, i) forms the 2-bit codes of its 8 weights at bits 2t of 8 bytes; OR-ing the four quarters'
-// lanes (lane ^ 16, lane ^ 32: the gfx950 permlane swaps) gives packed bytes 8i .. 8i+7, written
-// by quarter 0's lane; lane i = 0 of each quarter writes its group's S and ZS.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {  // finite f
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+constexpr int kPackWaves = 4;
+
+// Work is cut into units (row n, span gb): the 128 packed bytes n*Q + 128 gb .. +127, made from
+// the four groups (n, t*NG + gb), t = 0..3. Unit u = n*NG + gb, so the unit's packed bytes start
+// at 128 u. A wave takes four consecutive units per step (a quad, which may straddle rows) and
+// steps through quads with the grid's wave count as stride, loading the next quad's weights
+// before it works on the current one.
+// Lane l = 16 t + 4 g + p works on quarter t of unit 4 quad + g: it loads 16 bytes at 64-byte
+// steps, 32 weights of group (n, t*NG + gb) at offsets 32 c + 8 p + e (c = 0..3, e = 0..7), so
+// each load instruction reads 64 contiguous bytes per group and the quad of lanes p = 0..3
+// together holds the whole group. After the group's min / max (quad reductions), scale, zero and
+// codes, lane (t, g, p) holds the 2-bit codes of output bytes 32 c + 8 p + e of its unit for
+// quarter t; two permlane swap rounds (rows t ^ 1, then t ^ 2) OR the four quarters together,
+// shifting each field into bits 2t on the way, and leave lane (t, g, p) with bytes
+// 32 t + 8 p .. +7, which it stores. Lane p = 0 of each (t, g) writes its group's S and ZS.
 __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
     const uint16_t* __restrict__ W, int64_t ldw, int N, int K, uint8_t* __restrict__ packed,
     uint16_t* __restrict__ S, uint16_t* __restrict__ ZS) {
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   const int lane = threadIdx.x & (kWave - 1);
-  const int t = lane >> 4, i = lane & 15;
+  const int t = lane >> 4, g = (lane >> 2) & 3, p = lane & 3;
   const int Q = K >> 2;
-  const int NG = Q / kGroup;  // 128-byte spans per packed row
+  const int NG = Q / kGroup;  // spans (units) per row
   const int KG = K / kGroup;  // groups per row
-  const int wid = blockIdx.x * kPackWaves + (threadIdx.x >> 6);
-  const int gb = wid % NG;
-  const int rstep = gridDim.x * kPackWaves / NG;
-  const uint16_t* wcol = W + (int64_t)t * Q + gb * kGroup + 8 * i;
-  uint8_t* pcol = packed + gb * kGroup + 8 * i;
-  const int scol = t * NG + gb;
-  for (int n0 = wid / NG; n0 < N; n0 += rstep * kPackUnroll) {
-    u32x4 v[kPackUnroll];
+  const int units = N * NG;   // <= 2^30 (host check)
+  const int quads = (units + 3) >> 2;
+  const int wstep = gridDim.x * kPackWaves;
+  const int q0 = blockIdx.x * kPackWaves + (threadIdx.x >> 6);
+  if (q0 >= quads) return;  // wave-uniform
+  // (row, span) of this lane's unit, advanced by 4 * wstep units per step without a division
+  const int ustep = 4 * wstep;
+  const int dn = ustep / NG, dgb = ustep - dn * NG;
+  int u = 4 * q0 + g;
+  int n = u / NG, gb = u - n * NG;
+  auto load = [&](u32x4 (&v)[4], int un, int ugb) {
+    const int nc = un < N ? un : N - 1;  // past the last unit: a valid row, never stored
+    const uint16_t* src = W + (int64_t)nc * ldw + t * Q + ugb * kGroup + 8 * p;
 #pragma unroll
-    for (int j = 0; j < kPackUnroll; ++j) {
-      const int n = n0 + j * rstep;
-      v[j] = n < N ? *reinterpret_cast<const u32x4*>(wcol + (int64_t)n * ldw) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+  };
+  u32x4 v[4];
+  load(v, n, gb);
+  for (int qd = q0; qd < quads; qd += wstep) {
+    float w[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[8 * c + 2 * e] = bf16_lo(v[c][e]);
+        w[8 * c + 2 * e + 1] = bf16_hi(v[c][e]);
+      }
     }
+    const int cu = u, cn = n, cgb = gb;
+    u += ustep;
+    n += dn;
+    gb += dgb;
+    if (gb >= NG) {
+      gb -= NG;
+      ++n;
+    }
+    load(v, n, gb);
+    float lo = w[0], hi = w[0];
 #pragma unroll
-    for (int j = 0; j < kPackUnroll; ++j) {
-      const int n = n0 + j * rstep;
-      if (n >= N) break;  // wave-uniform
-      float w[8];
+    for (int e = 1; e < 32; ++e) {
+      lo = fminf(lo, w[e]);
+      hi = fmaxf(hi, w[e]);
+    }
+    lo = quad_min(lo);
+    hi = quad_max(hi);
+    const float sc = fmaxf(div3_rn(__fadd_rn(hi, -lo)), 1e-8f);
+    // The page's codes clamp(rint(fl(fl(w / sc) + zp)), 0, 3), with each quotient from quot_rn.
+    // The rounding to an integer is left to the byte conversion below (clamping to [0, 3] first
+    // gives the same code).
+    // Groups whose quotients could overflow, or whose 1 / sc could leave the normal range, take
+    // the IEEE division throughout (never met by a real head).
+    const bool wide = !(sc < 0x1p100f) || !(fmaxf(hi, -lo) < 0x1p100f);
+    const float y = __fdiv_rn(1.0f, sc);
+    float zp = clamp03(__builtin_rintf(quot_rn(-lo, sc, y)));
+    float q[32];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[2 * e] = bf16_lo(v[j][e]);
-        w[2 * e + 1] = bf16_hi(v[j][e]);
-      }
-      float lo = fminf(fminf(fminf(w[0], w[1]), fminf(w[2], w[3])), fminf(fminf(w[4], w[5]), fminf(w[6], w[7])));
-      float hi = fmaxf(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])), fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
-      lo = row16_min(lo);
-      hi = row16_max(hi);
-      const float sc = fmaxf(__fdiv_rn(__fadd_rn(hi, -lo), 3.0f), 1e-8f);
-      // 1 / sc can be subnormal for huge groups: such groups take the exact division throughout
-      bool near = !(sc < 0x1p100f);
-      const float r = __builtin_amdgcn_rcpf(sc);
-      float zp = __builtin_rintf(code_arg(-lo, r, 0.0f, near));
-      float q[8];
+    for (int e = 0; e < 32; ++e) q[e] = clamp03(__fadd_rn(quot_rn(w[e], sc, y), zp));
+    if (__builtin_amdgcn_ballot_w64(wide) != 0ull) {
+      if (wide) {
+        zp = clamp03(rintf(__fdiv_rn(-lo, sc)));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q[e] = code_arg(w[e], r, zp, near);
-      if (__builtin_amdgcn_ballot_w64(near) != 0ull) {
-        if (near) {
-          zp = clamp03(rintf(__fdiv_rn(-lo, sc)));
+        for (int e = 0; e < 32; ++e) q[e] = clamp03(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
+      }
+    }
+    // codes as bytes: v_cvt_pk_u8_f32 rounds to nearest with ties to even (as rint does) and
+    // saturates; word (c, h) holds bytes 32 c + 8 p + 4 h .. +3
+    uint32_t wd[4][2];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) q[e] = clamp03(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
-        }
-      }
-      // codes as bytes (exact: integral or off a tie), then each quarter's at bits 2t
-      uint32_t lo4 = 0, hi4 = 0;
+    for (int c = 0; c < 4; ++c) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo4 = __builtin_amdgcn_cvt_pk_u8_f32(q[e], e, lo4);
-        hi4 = __builtin_amdgcn_cvt_pk_u8_f32(q[4 + e], e, hi4);
+      for (int h = 0; h < 2; ++h) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_cvt_pk_u8_f32(q[8 * c + 4 * h + e], e, acc);
+        wd[c][h] = acc;
       }
-      lo4 <<= 2 * t;
-      hi4 <<= 2 * t;
-      {
-        const auto a = __builtin_amdgcn_permlane16_swap(lo4, lo4, false, false);
-        lo4 |= (lane & 16) ? a[0] : a[1];
-        const auto b = __builtin_amdgcn_permlane16_swap(hi4, hi4, false, false);
-        hi4 |= (lane & 16) ? b[0] : b[1];
-        const auto c = __builtin_amdgcn_permlane32_swap(lo4, lo4, false, false);
-        lo4 |= (lane & 32) ? c[0] : c[1];
-        const auto d = __builtin_amdgcn_permlane32_swap(hi4, hi4, false, false);
-        hi4 |= (lane & 32) ? d[0] : d[1];
-      }
-      if (t == 0) {
-        uint32_t* dst = reinterpret_cast<uint32_t*>(pcol + (int64_t)n * Q);
-        dst[0] = lo4;
-        dst[1] = hi4;
-      }
-      if (i == 0) {
+    }
+    // Round 1 (rows t, t ^ 1): after the swap of (wd[c], wd[c + 1]), c even, both results hold
+    // the word c + (t & 1) of rows 2(t >> 1) and 2(t >> 1) + 1, in that order.
+    // Round 2 (rows t, t ^ 2): after the swap of (x, y), both results hold the word t of rows
+    // {0, 1} and of rows {2, 3}, in that order.
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto a = __builtin_amdgcn_permlane16_swap(wd[0][h], wd[1][h], false, false);
+      const uint32_t x = a[0] | (a[1] << 2);
+      const auto b = __builtin_amdgcn_permlane16_swap(wd[2][h], wd[3][h], false, false);
+      const uint32_t y = b[0] | (b[1] << 2);
+      const auto z = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+      out[h] = z[0] | (z[1] << 4);
+    }
+    if (cu < units) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(packed + (int64_t)cu * kGroup + 32 * t + 8 * p);
+      dst[0] = out[0];
+      dst[1] = out[1];
+      if (p == 0) {
         const float s4 = __fmul_rn(4.0f, sc);
         const float zs = __fadd_rn(s4, __fmul_rn(zp, sc));
-        const int64_t at = (int64_t)n * KG + scol;
-        S[at] = (uint16_t)f32_to_bf16_rne(s4);
-        ZS[at] = (uint16_t)f32_to_bf16_rne(zs);
+        const int64_t at = (int64_t)cn * KG + t * NG + cgb;
+        S[at] = (uint16_t)bf16_bits_rne(s4);
+        ZS[at] = (uint16_t)bf16_bits_rne(zs);
       }
     }
   }
@@ -166,12 +219,13 @@ extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, ui
   if (N < 1 || check_k(K) != I2H_OK || ldw < K) return I2H_ERR_SHAPE;
   if (!aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 16) || !aligned(ZS, 16))
     return I2H_ERR_ALIGN;
-  if (N > (int64_t)1 << 30) return I2H_ERR_SHAPE;
-  // a multiple of NG waves (each wave keeps one span), about 8 rows per wave at large N
-  const int64_t NG = K / 512;
-  const int64_t per = (N + 7) / 8 < 2048 ? (N + 7) / 8 : 2048;
-  const int grid = (int)(NG * (per < 1 ? 1 : per));
-  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(kPackWaves * kWave), 0, (hipStream_t)stream, W,
+  // units (row, 128-byte span) are counted in 32 bits, with room for the grid stride
+  if (N * (K / 512) > (int64_t)1 << 30) return I2H_ERR_SHAPE;
+  const int64_t quads = (N * (K / 512) + 3) / 4;
+  const int64_t per_wg = (int64_t)kPackWaves * I2H_PACK_STEPS;
+  int64_t grid = (quads + per_wg - 1) / per_wg;
+  grid = grid < 1 ? 1 : (grid > I2H_PACK_MAX_WG ? I2H_PACK_MAX_WG : grid);
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kPackWaves * kWave), 0, (hipStream_t)stream, W,
                      ldw, (int)N, (int)K, packed, S, ZS);
   return check_launch();
 }

@@ -74,6 +74,7 @@ I2H_API int i2h_sizes(int64_t N, int64_t K, int64_t* packed_bytes, int64_t* scal
  * Per group of 128 consecutive k: sc = max((hi - lo) / 3, 1e-8), zp = clamp(round(-lo / sc),
  * 0, 3), q = clamp(round(w / sc + zp), 0, 3), all in IEEE fp32 with round-half-even and no
  * fused multiply-add, so the result is bit-exact against an eager fp32 evaluation.
+ * W must be finite. Limits: N * K / 512 <= 2^30.
  */
 I2H_API int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
                      uint16_t* S, uint16_t* ZS, void* stream);
