@@ -9,7 +9,10 @@
 // blocks; a block's list is best first, so the R best entries of the row lie in the R best
 // blocks), then the entries of the R best blocks are gathered and ranked, and the R weight rows
 // are gathered with every load in flight.
-// Ranking runs in registers on fp64-coded keys (wave_rank.h); 16 waves meet in a merge tree.
+// Ranking works on fp64-coded keys (wave_rank.h), unique within a row. Both rankings are a radix
+// select: the bits every key shares with the largest are skipped, then 4-bit digits are counted
+// with wave ballots (no atomics) until at most 64 keys can still be among the R best; those are
+// gathered and one wave sorts them.
 // The exact dot products use the same lane mapping and summation order as rerank.hip, so both
 // paths give the same bits.
 #include "dequant.h"
@@ -25,28 +28,204 @@ constexpr int kSrMaxR = 64, kSrMaxKc = 8;
 constexpr int kSrChunk = 10;  // 512-k steps of the two weight rows a wave has in flight at once
 
 struct SrLds {
-  double lists[kSrWaves][64];
-  double top[64];
+  uint64_t list[128];       // keys gathered for the final sort of a selection
+  double top[64];           // a selection, best first, 0-padded
+  uint64_t cand[64];        // per-wave t-th best keys (lower bound of the R-th best)
+  uint32_t cnt[kSrWaves][16];  // per-wave digit counts of one radix pass
+  uint64_t wmax[kSrWaves], wor[kSrWaves];
+  int32_t wnum[kSrWaves];
+  int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
+  uint64_t lower;
   int32_t sel[kSrMaxR];
   float ex[kSrMaxR];
 };
 constexpr size_t kSrLdsHead = (sizeof(SrLds) + 15) / 16 * 16;
 
-// The 64 best of the first NW (a power of two) waves' 64-lists, best first, into L.top. Every
-// thread of the block calls it with its lane's entry of its wave's sorted list.
-__device__ void merge_waves(SrLds& L, double mine, int NW) {
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {  // keys: doubles in [1, 2) or 0
+  double d = __builtin_bit_cast(double, v);
+  d = __builtin_fmax(d, lane_xor_f64<1>(d));
+  d = __builtin_fmax(d, lane_xor_f64<2>(d));
+  d = __builtin_fmax(d, lane_xor_f64<4>(d));
+  d = __builtin_fmax(d, lane_xor_f64<8>(d));
+  d = __builtin_fmax(d, lane_xor_f64<16>(d));
+  d = __builtin_fmax(d, lane_xor_f64<32>(d));
+  return __builtin_bit_cast(uint64_t, d);
+}
+__device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo |= lane_xor<1>(lo); hi |= lane_xor<1>(hi);
+  lo |= lane_xor<2>(lo); hi |= lane_xor<2>(hi);
+  lo |= lane_xor<4>(lo); hi |= lane_xor<4>(hi);
+  lo |= lane_xor<8>(lo); hi |= lane_xor<8>(hi);
+  lo |= lane_xor<16>(lo); hi |= lane_xor<16>(hi);
+  lo |= lane_xor<32>(lo); hi |= lane_xor<32>(hi);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Appends the keys with `take` set to L.list (at most `cap` stored; L.dec[3] counts them all):
+// one atomic per wave, lanes placed by their rank in the wave's ballot.
+__device__ __forceinline__ void wave_append(SrLds& L, uint64_t key, bool take, int cap) {
+  const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
+  if (bal == 0) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  if (lane == 0) base = atomicAdd(&L.dec[3], __builtin_popcountll(bal));
+  base = __shfl(base, 0);
+  const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+  if (take && at < cap) L.list[at] = key;
+}
+
+// Radix select of the R largest keys: the bits every key shares with the largest are skipped,
+// then 4-bit digits are counted with wave ballots until at most 64 keys can still be among the R
+// best. On return, the keys whose 52 low bits, shifted right by *shift, are at least
+// *prefix >> *shift are the R best plus at most 64 - R others.
+template <int BPT>
+__device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shift_out, uint64_t* prefix_out) {
+  constexpr uint64_t kLow = (1ull << 52) - 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave < NW) L.lists[wave][lane] = mine;
+  uint64_t mx = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) mx = k[j] > mx ? k[j] : mx;
+  mx = wave_max_u64(mx);
+  if (lane == 0) L.wmax[wave] = mx;
   __syncthreads();
-  for (int step = 1; step < NW; step <<= 1) {
-    // an active wave reads its list and its partner's (inactive at this step) and rewrites its own
-    if ((wave & (2 * step - 1)) == 0 && wave < NW) {
-      const double v = wave_merge64_f64(L.lists[wave][lane], L.lists[wave + step]);
-      L.lists[wave][lane] = v;
+#pragma unroll
+  for (int w = 0; w < kSrWaves; ++w) mx = L.wmax[w] > mx ? L.wmax[w] : mx;
+  uint64_t df = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) df |= k[j] != 0 ? (k[j] ^ mx) & kLow : 0ull;
+  df = wave_or_u64(df);
+  if (lane == 0) L.wor[wave] = df;
+  __syncthreads();
+  df = 0;
+#pragma unroll
+  for (int w = 0; w < kSrWaves; ++w) df |= L.wor[w];
+  // more than 64 distinct keys: df != 0
+  int shift = (64 - __builtin_clzll(df) + 3) & ~3, need = R;
+  uint64_t prefix = mx & kLow & ~((1ull << shift) - 1);
+  while (true) {
+    shift -= 4;
+    uint32_t mine = 0;  // lane d < 16: this wave's count of digit d
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const uint64_t kl = k[j] & kLow;
+      const bool cand = k[j] != 0 && (kl >> (shift + 4)) == (prefix >> (shift + 4));
+      const int dig = (int)(kl >> shift) & 15;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const uint32_t c = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(cand && dig == d));
+        mine += lane == d ? c : 0u;
+      }
+    }
+    if (lane < 16) L.cnt[wave][lane] = mine;
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t tot = 0;
+      if (lane < 16)
+#pragma unroll
+        for (int w = 0; w < kSrWaves; ++w) tot += L.cnt[w][lane];
+      // above = keys in higher digits: inclusive suffix sum over lanes 0..15, minus own
+      uint32_t suf = tot;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o, 16);
+        suf += (lane & 15) + o < 16 ? v : 0u;
+      }
+      const uint32_t above = suf - tot;
+      const bool hit = lane < 16 && above < (uint32_t)need && above + tot >= (uint32_t)need;
+      const int d = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(hit));
+      if (lane == d) {
+        L.dec[0] = d;
+        L.dec[1] = need - (int)above;
+        L.dec[2] = (int)tot;
+      }
     }
     __syncthreads();
+    const int d = L.dec[0], inbin = L.dec[2];
+    need = L.dec[1];
+    prefix |= (uint64_t)d << shift;
+    // L.dec and L.cnt are rewritten only after the next pass's first barrier
+    if (inbin == need || (R - need) + inbin <= 64) break;
   }
-  if (wave == 0) L.top[lane] = L.lists[0][lane];
+  *shift_out = shift;
+  *prefix_out = prefix;
+}
+
+// The R (<= 64) largest of the keys the block's threads hold (BPT each, 0 = none), best first
+// and 0-padded, into L.top. Keys are the bit patterns of the fp64 ranking keys: valid ones share
+// their top 12 bits, so the 52 low bits order them, and they are unique. `lower`, if not 0, is
+// at most the R-th largest key (0: unknown). Every thread of the block calls it.
+//
+// Fast path: a lower bound T of the R-th largest key (if not given: the smallest of the waves'
+// t-th best keys, t = ceil(R / 16), since the 16 t keys at or above it are distinct); if at most
+// 128 keys are at or above T they are gathered, sorted (two waves for more than 64) and the best
+// R kept. Otherwise radix_narrow leaves at most 64 to gather and sort.
+template <int BPT>
+__device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower) {
+  constexpr uint64_t kLow = (1ull << 52) - 1;
+  constexpr int kCap = 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
+  if (lower != 0) __syncthreads();
+  if (lower == 0) {
+    const int t = (R + kSrWaves - 1) / kSrWaves;  // 1..4
+    uint64_t kk[BPT];
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) kk[j] = k[j];
+    uint64_t mx = 0;
+    for (int i = 0; i < t; ++i) {
+      mx = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) mx = kk[j] > mx ? kk[j] : mx;
+      mx = wave_max_u64(mx);
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) kk[j] = kk[j] == mx ? 0ull : kk[j];  // keys are unique
+    }
+    if (lane == 0) L.wmax[wave] = mx;  // this wave's t-th best (0: fewer than t keys)
+    __syncthreads();
+    lower = L.wmax[0];
+#pragma unroll
+    for (int w = 1; w < kSrWaves; ++w) lower = L.wmax[w] < lower ? L.wmax[w] : lower;
+  }
+  // gather every key at or above the bound while there is room, counting all of them
+  const uint64_t lo = lower != 0 ? lower : 1ull;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) wave_append(L, k[j], k[j] >= lo, kCap);
+  __syncthreads();
+  int n = L.dec[3];
+  if (n > kCap) {  // block-uniform: narrow down by digits, then gather again
+    int shift = 0;
+    uint64_t prefix = 0;
+    radix_narrow<BPT>(L, k, R, &shift, &prefix);
+    if (tid == 0) L.dec[3] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      wave_append(L, k[j], k[j] != 0 && ((k[j] & kLow) >> shift) >= (prefix >> shift), kCap);
+    __syncthreads();
+    n = L.dec[3];  // at most 64
+  }
+  // sort: one wave for up to 64 keys; else waves 0 and 1 sort 64 each in place and wave 0 merges
+  if (n <= 64) {
+    if (wave == 0) {
+      double v[1] = {lane < n ? __builtin_bit_cast(double, L.list[lane]) : 0.0};
+      wave_sort_f64<1>(v);
+      L.top[lane] = lane < R ? v[0] : 0.0;
+    }
+  } else {
+    if (wave < 2) {
+      const int i = wave * 64 + lane;
+      double v[1] = {i < n ? __builtin_bit_cast(double, L.list[i]) : 0.0};
+      wave_sort_f64<1>(v);
+      L.list[i] = __builtin_bit_cast(uint64_t, v[0]);  // each wave rewrites only what it read
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const double a = __builtin_bit_cast(double, L.list[lane]);
+      const double m = wave_merge64_f64(a, reinterpret_cast<const double*>(L.list + 64));
+      L.top[lane] = lane < R ? m : 0.0;
+    }
+  }
   __syncthreads();
 }
 
@@ -64,41 +243,79 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   const float* s = cs + (int64_t)m * ld;
   const int32_t* c = ci + (int64_t)m * ld;
 
-  // --- the best entry of each of this thread's blocks (t + 1024 j), and the x row into LDS
-  double srt[BPT];
+  // --- the best entry of each of this thread's blocks (t + 1024 j), and the x row into LDS. A
+  // block's rank among blocks needs only its best score and the block index: blocks hold
+  // consecutive token ranges, so the lower block holds the lower token on equal scores.
+  // every load is issued before any is used (clamped indices; unused values are dropped)
+  float bs[BPT];
 #pragma unroll
   for (int j = 0; j < BPT; ++j) {
     const int b = tid + kSrThreads * j;
-    float v = -__builtin_inff();
-    int32_t t = -1;
-    if (b < nblk) {
-      v = s[(int64_t)b * kc];
-      t = c[(int64_t)b * kc];
-    }
-    srt[j] = token_key(v, t);
+    bs[j] = s[(int64_t)(b < nblk ? b : nblk - 1) * kc];
   }
   const uint16_t* xr = x + (int64_t)m * K;
-  for (int u = tid; u < K / 8; u += kSrThreads)
-    *reinterpret_cast<u32x4*>(xl + 8 * u) = ld16(xr + 8 * u);
-
-  // --- the R best blocks, by their best entry
-  wave_sort_f64<BPT>(srt);
-  merge_waves(L, srt[0], kSrWaves);
-
-  // --- every entry of those blocks (thread t: entry t % kc of block rank t / kc), ranked. A
-  // block's key holds the token of its best entry, and block b holds tokens 64 b .. 64 b + 63.
-  const int nsel = R * kc;
-  double ek[1] = {0.0};
-  if (tid < nsel) {
-    const double bkey = L.top[tid / kc];
-    if (bkey > 0.0) {
-      const int64_t at = (int64_t)(token_key_token(bkey) / kBlockN) * kc + tid % kc;
-      ek[0] = token_key(s[at], c[at]);
+  constexpr int kXU = 2;  // 16-byte units of x per thread per round (K <= 16384)
+  for (int u0 = 0; u0 < K / 8; u0 += kXU * kSrThreads) {
+    u32x4 xv[kXU];
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      const int u = u0 + tid + i * kSrThreads;
+      xv[i] = ld16(xr + 8 * (u < K / 8 ? u : 0));
+    }
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) {
+      const int u = u0 + tid + i * kSrThreads;
+      if (u < K / 8) *reinterpret_cast<u32x4*>(xl + 8 * u) = xv[i];
     }
   }
-  const int nw = nsel <= 64 ? 1 : (nsel <= 128 ? 2 : (nsel <= 256 ? 4 : 8));
-  if (wave < nw) wave_sort_f64<1>(ek);
-  merge_waves(L, ek[0], nw);  // its first barrier follows every read of L.top above
+  uint64_t srt[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = tid + kSrThreads * j;
+    srt[j] = b < nblk ? __builtin_bit_cast(uint64_t, token_key(bs[j], b)) : 0ull;
+  }
+
+  // --- the R best blocks, by their best entry
+  select_top<BPT>(L, srt, R, 0ull);
+
+  // --- every entry of those blocks (thread t: entry t % kc of block rank t / kc), ranked. The
+  // best entry of a block is valid whenever the block has a real column; a caller's list whose
+  // best entry has index < 0 makes the block ranking redo itself with the entries' tokens.
+  const int nsel = R * kc;
+  uint64_t ek[1] = {0ull};
+  bool bad = false;
+  auto gather_entries = [&](bool by_token) {
+    const double bkey = tid < nsel ? L.top[tid / kc] : 0.0;
+    const int t = token_key_token(bkey);  // -1 when there is no block
+    const int blk = t < 0 ? 0 : (by_token ? t / kBlockN : t);
+    const int64_t at = (int64_t)blk * kc + (tid < nsel ? tid % kc : 0);
+    const int32_t tok = c[at];
+    const float sc = s[at];
+    const bool use = t >= 0;
+    bad = bad || (use && tid % kc == 0 && tok < 0);
+    ek[0] = use ? __builtin_bit_cast(uint64_t, token_key(sc, tok)) : 0ull;
+  };
+  gather_entries(false);
+  // The R block maxima are R distinct entries at or above the R-th block's score with that
+  // block's last token, which bounds the R-th best entry from below. select_top rewrites L.top
+  // only after barriers that follow every read of it here.
+  uint64_t lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
+  if (lower_e != 0) {
+    const uint32_t last = (uint32_t)token_key_token(L.top[R - 1]) * kBlockN + (kBlockN - 1);
+    lower_e = (lower_e & ~0xFFFFFull) | (0xFFFFFu - last);
+  }
+  const bool redo = __syncthreads_or(bad);
+  if (redo) {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int b = tid + kSrThreads * j;
+      srt[j] = b < nblk ? __builtin_bit_cast(uint64_t, token_key(s[(int64_t)b * kc], c[(int64_t)b * kc])) : 0ull;
+    }
+    select_top<BPT>(L, srt, R, 0ull);
+    gather_entries(true);
+    lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
+  }
+  select_top<1>(L, ek, R, lower_e);
   if (tid < R) L.sel[tid] = token_key_token(L.top[tid]);
   __syncthreads();
 
