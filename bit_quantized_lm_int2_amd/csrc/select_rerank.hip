@@ -82,7 +82,7 @@ __device__ __forceinline__ void wave_append(SrLds& L, uint64_t key, bool take, i
 template <int BPT>
 __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shift_out, uint64_t* prefix_out) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint64_t mx = 0;
 #pragma unroll
   for (int j = 0; j < BPT; ++j) mx = k[j] > mx ? k[j] : mx;
@@ -105,17 +105,21 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
   uint64_t prefix = mx & kLow & ~((1ull << shift) - 1);
   while (true) {
     shift -= 4;
-    uint32_t mine = 0;  // lane d < 16: this wave's count of digit d
+    // lane d < 16: this wave's count of digit d, from five ballots per key slot (candidates and
+    // the four digit bits): d selects each bit's mask or its complement
+    uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       const uint64_t kl = k[j] & kLow;
       const bool cand = k[j] != 0 && (kl >> (shift + 4)) == (prefix >> (shift + 4));
       const int dig = (int)(kl >> shift) & 15;
+      uint64_t sel = __builtin_amdgcn_ballot_w64(cand);
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const uint32_t c = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(cand && dig == d));
-        mine += lane == d ? c : 0u;
+      for (int bit = 0; bit < 4; ++bit) {
+        const uint64_t b = __builtin_amdgcn_ballot_w64(((dig >> bit) & 1) != 0);
+        sel &= ((lane >> bit) & 1) != 0 ? b : ~b;
       }
+      mine += (uint32_t)__builtin_popcountll(sel);
     }
     if (lane < 16) L.cnt[wave][lane] = mine;
     __syncthreads();
@@ -164,7 +168,7 @@ template <int BPT>
 __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
   constexpr int kCap = 128;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
   if (lower != 0) __syncthreads();
   if (lower == 0) {
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   extern __shared__ __align__(16) uint8_t smem[];
   SrLds& L = *reinterpret_cast<SrLds*>(smem);
   uint16_t* xl = reinterpret_cast<uint16_t*>(smem + kSrLdsHead);
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld = (int64_t)nblk * kc;
   const float* s = cs + (int64_t)m * ld;
   const int32_t* c = ci + (int64_t)m * ld;
