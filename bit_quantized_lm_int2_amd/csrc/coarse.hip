@@ -211,21 +211,26 @@ __device__ __forceinline__ uint64_t block_key(float v, int col_in_block) {
   return ((uint64_t)ordered_key(v) << 32) | (uint64_t)(63 - col_in_block);
 }
 
-// Block top-kc of up to 16 rows whose 64 keys sit in ck[m][64] (unique keys): each lane counts
-// the keys of its row that beat its own; a rank below kc is the lane's output slot.
+// Block top-kc of M rows whose 64 keys sit in ck[m][64] (unique keys): a key's rank is the number
+// of its row's keys that beat it, and a rank below kc is its output slot. Every wave takes 16
+// keys of each row, four lanes per key (lane = 4 i + q compares key 16 wave + i with keys
+// 16 q .. 16 q + 15), and the four partial counts are summed across the quad.
 __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, int N, int kc, int64_t ld,
                                             float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int m = wave; m < M; m += kCoarseThreads / kWave) {
+  const int q = lane & 3, i = wave * 16 + (lane >> 2);
+  for (int m = 0; m < M; ++m) {
     const uint64_t* row = ck + m * kBlockN;
-    const uint64_t mine = row[lane];
+    const uint64_t mine = row[i];
     int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < kBlockN; j += 2) {
-      const uint64_t a = row[j], c = row[j + 1];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const uint64_t a = row[16 * q + j], c = row[16 * q + j + 1];
       rank += (a > mine) + (c > mine);
     }
-    if (rank < kc) {
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    if (q == 0 && rank < kc) {
       const int tok = b * kBlockN + 63 - (int)(mine & 63u);
       const bool ok = tok < N;
       const int64_t at = (int64_t)m * ld + (int64_t)b * kc + rank;
