@@ -22,13 +22,17 @@ Order of the steps (names follow the page):
   rerank        exact dot of x with the selected bf16 weight rows                 (_rerank_exact)
   finalize      argmax, or the top-k of the reranked tokens                       (module docstring;
                                                                                    _apply_head_int2)
+  logits_row    the drop-in row: coarse bf16 row (or -inf), exact scores written
+                back, embedding bias, head dtype                                  (_apply_head_int2)
 Readings of points the page leaves open (each is also listed with the design notes):
   * ties in the block emit go to the lower column; selection and top-k order by score
     descending, then token index ascending; the final argmax takes the lower token index;
   * argmax is taken over the R exact scores;
   * a block with fewer than KCAND real columns (vocab tail) pads with (-inf, -1), and such
     entries are never selected;
-  * K must be a multiple of 4 * G, so that every quarter holds whole groups.
+  * K must be a multiple of 4 * G, so that every quarter holds whole groups;
+  * the exact scores are written back into the row for an argmax caller as well as for a top-k
+    caller (whose row is -inf elsewhere).
 """
 from __future__ import annotations
 
@@ -329,3 +333,50 @@ def storage_bytes(N: int, K: int, G: int = GROUP) -> dict:
     scales = N * (K // G) * 2
     return dict(packed=packed, S=scales, ZS=scales, int2_total=packed + 2 * scales,
                 bf16_weight=N * K * 2)
+
+
+# ----------------------------------------------------------------------------------------------
+# NEXT f1: the drop-in logits row
+# radiance_drafthead.py, _apply_head_int2: the coarse logits are a bf16 row Y [M, N]. A top-k
+# caller's row is first set to -inf everywhere; the R reranked tokens' entries are then
+# overwritten by their exact scores rounded to bf16 (for both callers: the reading that the
+# write-back belongs to every caller with an exact weight). The embedding bias is added next, with
+# torch's type promotion (bf16 + bf16 stays bf16, bf16 + fp16 or fp32 becomes fp32), and the row
+# is cast to the head dtype.
+# ----------------------------------------------------------------------------------------------
+LOGIT_DTYPES = ("bf16", "fp16", "fp32")
+
+
+def logits_row(y_bits: np.ndarray, sel: np.ndarray, exact: np.ndarray, topk_only: bool,
+               bias: np.ndarray | None = None, bias_dtype: str | None = None,
+               out_dtype: str = "bf16") -> np.ndarray:
+    """The drop-in output [M, N]: uint16 bits for bf16/fp16 heads, float32 for fp32 heads.
+
+    y_bits bf16 bits [M, N]; sel int32 [M, R] (distinct tokens per row, -1 = none); exact
+    float32 [M, R]; bias [N] given as uint16 bits (bf16), float16 or float32 per bias_dtype.
+    """
+    assert out_dtype in LOGIT_DTYPES and (bias is None) == (bias_dtype is None)
+    M, N = y_bits.shape
+    # the row before the bias: coarse bf16 values, or -inf for a top-k caller
+    y = np.full((M, N), -np.inf, dtype=np.float32) if topk_only else bf16_to_f32(y_bits)
+    e = bf16_to_f32(f32_to_bf16(np.asarray(exact, dtype=np.float32)))  # ex.to(bfloat16)
+    for m in range(M):
+        for j in range(sel.shape[1]):
+            if sel[m, j] >= 0:
+                y[m, sel[m, j]] = e[m, j]
+    # the bias, then the row's dtype after promotion
+    if bias is None:
+        r, rtype = y, "bf16"
+    elif bias_dtype == "bf16":
+        r, rtype = bf16_to_f32(f32_to_bf16((y + bf16_to_f32(bias)[None, :]).astype(np.float32))), "bf16"
+    elif bias_dtype == "fp16":
+        r, rtype = (y + np.asarray(bias, dtype=np.float16).astype(np.float32)[None, :]).astype(np.float32), "fp32"
+    else:
+        assert bias_dtype == "fp32"
+        r, rtype = (y + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32), "fp32"
+    # the cast to the head dtype (a no-op when the dtypes agree)
+    if out_dtype == "fp32":
+        return r.astype(np.float32)
+    if out_dtype == "bf16":
+        return f32_to_bf16(r)  # exact when the row already holds bf16 values
+    return r.astype(np.float16).view(np.uint16)

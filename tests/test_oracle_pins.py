@@ -428,3 +428,75 @@ def test_shape_rule():
     for K in (0, 256, 640, 5000):
         with pytest.raises(ValueError):
             oracle.check_shape(K)
+
+
+# ---------------------------------------------------------------------------------------------
+# Drop-in logits row (radiance_drafthead.py, _apply_head_int2: write-back of the exact scores,
+# embedding bias, head dtype).
+# ---------------------------------------------------------------------------------------------
+def _bf(vals):
+    return oracle.f32_to_bf16(np.asarray(vals, dtype=np.float32)).reshape(1, -1)
+
+
+def test_logits_row_hand_example():
+    """Worked by hand: y = [1, 2, -3, 0.5], tokens 2 and 0 reranked to 7.25 and 0.1."""
+    y = _bf([1.0, 2.0, -3.0, 0.5])
+    sel = np.array([[2, 0]], np.int32)
+    ex = np.array([[7.25, 0.1]], np.float32)
+    b01 = 0.10009765625                        # bf16(0.1) = 0x3DCD
+    out = oracle.bf16_to_f32(oracle.logits_row(y, sel, ex, topk_only=False))
+    assert out.tolist() == [[b01, 2.0, 7.25, 0.5]]
+    out = oracle.bf16_to_f32(oracle.logits_row(y, sel, ex, topk_only=True))
+    assert out.tolist() == [[b01, -math.inf, 7.25, -math.inf]]
+    # bf16 bias: each sum is rounded back to bf16 (0.6000977 -> 0.6015625; 2 + 2^-8 -> 2)
+    bias = _bf([0.5, 2.0 ** -8, 1.0, -0.5])[0]
+    out = oracle.bf16_to_f32(oracle.logits_row(y, sel, ex, False, bias, "bf16"))
+    assert out.tolist() == [[0.6015625, 2.0, 8.25, 0.0]]
+    # fp32 bias: the row becomes fp32 and keeps the exact sums
+    out = oracle.logits_row(y, sel, ex, False, np.array([0.5, 2.0 ** -8, 1.0, -0.5], np.float32), "fp32", "fp32")
+    assert out.tolist() == [[b01 + 0.5, 2.0 + 2.0 ** -8, 8.25, 0.0]]
+
+
+def test_logits_row_rounding_ties():
+    """Half-way sums round to the even neighbour: bf16 at 1 + 2^-8 and 1 + 3*2^-8 (spacing 2^-7),
+    fp16 at 1 + 3*2^-11 (spacing 2^-10)."""
+    sel = np.full((1, 1), -1, np.int32)
+    ex = np.zeros((1, 1), np.float32)
+    y = _bf([1.0, 1.0078125])
+    out = oracle.bf16_to_f32(oracle.logits_row(y, sel, ex, False, _bf([2.0 ** -8, 2.0 ** -8])[0], "bf16"))
+    assert out.tolist() == [[1.0, 1.015625]]
+    y = _bf([1.0, 1.0])
+    out = oracle.logits_row(y, sel, ex, False, np.array([3 * 2.0 ** -11, 2.0 ** -11], np.float16), "fp16", "fp16")
+    assert out.view(np.float16).astype(np.float64).tolist() == [[1.0 + 2.0 ** -9, 1.0]]
+
+
+@pytest.mark.parametrize("topk_only", [False, True])
+@pytest.mark.parametrize("bias_dtype", [None, "bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+def test_logits_row_matches_eager_torch_steps(topk_only, bias_dtype, out_dtype):
+    """The page's steps as eager torch CPU ops (fill, scatter of ex.to(bf16), + bias with torch's
+    type promotion, .to(head dtype)) on random rows."""
+    g = np.random.default_rng(5)
+    M, N, R = 3, 257, 7
+    y_bits = oracle.f32_to_bf16(g.normal(0, 4, (M, N)).astype(np.float32))
+    sel = np.stack([g.choice(N, R, replace=False) for _ in range(M)]).astype(np.int32)
+    sel[1, -2:] = -1
+    ex = g.normal(0, 8, (M, R)).astype(np.float32)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+    bias_np, bias_t = None, None
+    if bias_dtype is not None:
+        b = g.normal(0, 2, N).astype(np.float32)
+        bias_t = torch.from_numpy(b).to(tdt[bias_dtype])
+        bias_np = oracle.f32_to_bf16(b) if bias_dtype == "bf16" else b.astype(np.float16 if bias_dtype == "fp16" else np.float32)
+    got = oracle.logits_row(y_bits, sel, ex, topk_only, bias_np, bias_dtype, out_dtype)
+    y = torch.from_numpy(y_bits.astype(np.int16)).view(torch.bfloat16).clone()
+    if topk_only:
+        y.fill_(float("-inf"))
+    for m in range(M):
+        ok = sel[m] >= 0
+        y[m].scatter_(0, torch.from_numpy(sel[m][ok]).long(), torch.from_numpy(ex[m][ok]).to(torch.bfloat16))
+    if bias_t is not None:
+        y = y + bias_t
+    y = y.to(tdt[out_dtype])
+    want = y.view(torch.int16).numpy().view(np.uint16) if out_dtype != "fp32" else y.numpy()
+    assert got.dtype == want.dtype and np.array_equal(got, want)
