@@ -17,6 +17,7 @@ import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
+           "logits",
            "GROUP",
            "BLOCK_N"]
 
@@ -47,7 +48,9 @@ _SIGNATURES = {
                                 _P], _INT),
     "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
                   _I64, _P], _INT),
+    "i2h_logits": ([_P, _I64, _I64, _P, _P, _INT, _INT, _P, _INT, _P, _INT, _P], _INT),
 }
+_DTYPE_CODES = {None: 0, torch.bfloat16: 1, torch.float16: 2, torch.float32: 3}
 
 
 class I2HError(RuntimeError):
@@ -329,3 +332,46 @@ def head(x, packed, S, ZS, W, kcand: int = 8, R: int = 32, k: int = 1, want_y: b
                                       kcand, R, k, _ptr(oi), _ptr(ov), _ptr(y), _ptr(workspace),
                                       workspace.numel(), _stream(x)))
     return (oi, ov, y) if want_y else (oi, ov)
+
+
+def logits(y, sel, exact, topk_only: bool = False, bias: torch.Tensor | None = None,
+           out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None) -> torch.Tensor:
+    """The drop-in logits row [M, N] of out_dtype: the coarse bf16 row y (or -inf everywhere when
+    topk_only; y may then be None), the exact scores written back at the sel tokens, plus the
+    embedding bias (bf16, fp16 or fp32 [N]) and the cast to out_dtype. out may be y itself
+    (bf16)."""
+    _need(sel, "sel", torch.int32, 2)
+    _need(exact, "exact", torch.float32, 2)
+    M, R = sel.shape
+    _shape(exact, "exact", (M, R))
+    _dense(sel, "sel")
+    _dense(exact, "exact")
+    if y is not None:
+        _need(y, "y", torch.bfloat16, 2)
+        _dense(y, "y")
+        if y.shape[0] != M:
+            raise ValueError("y and sel must have the same rows")
+        N = y.shape[1]
+    elif not topk_only:
+        raise ValueError("y is needed unless topk_only")
+    elif bias is not None:
+        N = bias.shape[0]
+    elif out is not None:
+        N = out.shape[1]
+    else:
+        raise ValueError("with y None, give bias or out so that N is known")
+    if out_dtype not in (torch.bfloat16, torch.float16, torch.float32):
+        raise ValueError("out_dtype must be bfloat16, float16 or float32")
+    if bias is not None:
+        if bias.dtype not in (torch.bfloat16, torch.float16, torch.float32) or tuple(bias.shape) != (N,):
+            raise ValueError(f"bias must be a [{N}] bfloat16, float16 or float32 tensor")
+        _dense(bias, "bias")
+    dev = sel.device
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=dev)
+    elif out.dtype != out_dtype or tuple(out.shape) != (M, N) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous [{M}, {N}] {out_dtype} tensor")
+    _check("i2h_logits", lib().i2h_logits(_ptr(y), M, N, _ptr(sel), _ptr(exact), R, int(bool(topk_only)),
+                                          _ptr(bias), _DTYPE_CODES[None if bias is None else bias.dtype], _ptr(out),
+                                          _DTYPE_CODES[out_dtype], _stream(sel)))
+    return out

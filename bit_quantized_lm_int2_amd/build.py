@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libi2h.so")
 ARCH = os.environ.get("I2H_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pack.hip", "coarse.hip", "coarse_tile.hip", "select.hip", "select_rerank.hip", "rerank.hip", "head.hip"]
+SOURCES = ["pack.hip", "coarse.hip", "coarse_tile.hip", "select.hip", "select_rerank.hip", "rerank.hip", "head.hip",
+           "logits.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -49,6 +49,12 @@ extern "C" {
 #define I2H_MAX_R 1024
 #define I2H_MAX_NBLK 8192       /* N <= 524288 for the candidate selection */
 
+/* Element types of the drop-in logits row (i2h_logits). */
+#define I2H_DTYPE_NONE 0        /* no embedding bias */
+#define I2H_DTYPE_BF16 1
+#define I2H_DTYPE_F16 2
+#define I2H_DTYPE_F32 3
+
 /* Library version (major * 10000 + minor * 100 + patch). */
 I2H_API int i2h_version(void);
 
@@ -176,6 +182,25 @@ I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const 
                      const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
                      int kcand, int R, int k, int32_t* out_idx, float* out_val, uint16_t* y,
                      void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * The drop-in logits row (radiance_drafthead.py, _apply_head_int2, after the exact rerank):
+ *   row     = topk_only ? -inf : y[m, :]            (y: the coarse bf16 row from i2h_coarse_topk)
+ *   row[sel[m, j]] = bf16(exact[m, j])               for every sel[m, j] in [0, N)
+ *   out[m, :] = cast_out(row + bias)                 with torch's type promotion: a bf16 bias
+ *             rounds the fp32 sum back to bf16; an fp16 or fp32 bias gives the fp32 sum; no bias
+ *             keeps the bf16 row; the cast to out_dtype rounds to nearest-even.
+ *   y       bf16 [M, N] (row stride N), 16-byte aligned; may be NULL when topk_only.
+ *   sel     int32 [M, R], exact fp32 [M, R] (from i2h_select_rerank_topk or i2h_select +
+ *           i2h_rerank); a row's tokens must be distinct (as those calls give them).
+ *   bias    [N] of bias_dtype (I2H_DTYPE_NONE with bias NULL for none), naturally aligned.
+ *   out     [M, N] of out_dtype (BF16 / F16: uint16 bits; F32), 16-byte aligned. out may be y
+ *           itself when out_dtype is I2H_DTYPE_BF16 (the row pass reads each entry before it
+ *           writes it, and the write-back runs after it in stream order).
+ * Two kernel launches on `stream`. Limits: 1 <= R <= 1024.
+ */
+I2H_API int i2h_logits(const uint16_t* y, int64_t M, int64_t N, const int32_t* sel, const float* exact, int R,
+                       int topk_only, const void* bias, int bias_dtype, void* out, int out_dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -362,7 +362,7 @@ def logits_row(y_bits: np.ndarray, sel: np.ndarray, exact: np.ndarray, topk_only
     e = bf16_to_f32(f32_to_bf16(np.asarray(exact, dtype=np.float32)))  # ex.to(bfloat16)
     for m in range(M):
         for j in range(sel.shape[1]):
-            if sel[m, j] >= 0:
+            if 0 <= sel[m, j] < N:  # -1 (none) and tokens past the row are skipped
                 y[m, sel[m, j]] = e[m, j]
     # the bias, then the row's dtype after promotion
     if bias is None:

@@ -27,7 +27,7 @@ def test_header_declares_the_entry_points():
     want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
-            "i2h_select_rerank_topk"}
+            "i2h_select_rerank_topk", "i2h_logits"}
     assert names == want
 
 
@@ -168,3 +168,22 @@ def test_select_rerank_rejects_before_launch():
     assert f(P, P, 1, 1940, 8, 32, P, P, 5120, 124160, 5120, 33, None, None, P, P, None) == LIMIT  # k > R
     assert f(P, P, 1, 4097, 8, 32, P, P, 5120, 262145, 5120, 1, None, None, P, P, None) == LIMIT  # N too large
     assert f(P, P, 1, 1940, 8, 32, P, P, 5124, 124160, 5120, 1, None, None, P, P, None) == ALIGN  # ldw % 8
+
+
+def test_logits_rejects_before_launch():
+    f = i2h.lib().i2h_logits
+    BF, F16, F32 = 1, 2, 3
+    # y, M, N, sel, exact, R, topk_only, bias, bias_dtype, out, out_dtype, stream
+    assert f(None, 1, 124160, P, P, 32, 0, None, 0, P, BF, None) == ARG        # y needed for an argmax caller
+    assert f(P, 1, 124160, P, P, 32, 0, None, 0, None, BF, None) == ARG        # no out
+    assert f(P, 1, 124160, P, P, 32, 0, None, BF, P, BF, None) == ARG          # bias dtype without bias
+    assert f(P, 1, 124160, P, P, 32, 0, P, 0, P, BF, None) == ARG              # bias without dtype
+    assert f(P, 1, 124160, P, P, 32, 0, None, 0, P, 0, None) == ARG            # no out dtype
+    assert f(P, 1, 124160, P, P, 32, 0, None, 0, P, 4, None) == ARG
+    assert f(P, 0, 124160, P, P, 32, 0, None, 0, P, BF, None) == SHAPE
+    assert f(P, 1, 0, P, P, 32, 0, None, 0, P, BF, None) == SHAPE
+    assert f(P, 1, 124160, P, P, 0, 0, None, 0, P, BF, None) == LIMIT
+    assert f(P, 1, 124160, P, P, 1025, 0, None, 0, P, BF, None) == LIMIT
+    assert f(P + 2, 1, 124160, P, P, 32, 0, None, 0, P, BF, None) == ALIGN     # y not 16-byte aligned
+    assert f(P, 1, 124160, P, P, 32, 0, None, 0, P + 8, F32, None) == ALIGN    # out not 16-byte aligned
+    assert f(P, 1, 124160, P, P, 32, 0, ODD, F32, P, BF, None) == ALIGN        # fp32 bias misaligned

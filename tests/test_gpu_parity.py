@@ -377,3 +377,59 @@ def test_full_vocab_top16(i2h):
     packed_o = oracle.pack(Wb)
     out = run_and_check(i2h, xb, Wb, k=16, packed_o=packed_o, rows=rows)
     say(f"  top-16 match vs oracle: {out['match']}/{out['places']}")
+
+
+# ---------------------------------------------------------------------------------------------
+# drop-in logits row: bit-exact
+# ---------------------------------------------------------------------------------------------
+_TDT = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
+
+
+def _logits_inputs(M, N, R, seed):
+    g = np.random.default_rng(seed)
+    y_bits = oracle.f32_to_bf16(g.normal(0, 4, (M, N)).astype(np.float32))
+    sel = np.stack([g.choice(N, R, replace=False) for _ in range(M)]).astype(np.int32)
+    sel[0, -3:] = -1                      # fewer than R reranked tokens in row 0
+    if M > 1:
+        sel[1, 0] = N + 7                 # out of range: never written
+    ex = g.normal(0, 8, (M, R)).astype(np.float32)
+    bias = g.normal(0, 2, N).astype(np.float32)
+    return y_bits, sel, ex, bias
+
+
+def _bias_args(bias, bias_dtype):
+    if bias_dtype is None:
+        return None, None
+    t = torch.from_numpy(bias).to(_TDT[bias_dtype])
+    ref = si.bits(t) if bias_dtype == "bf16" else t.numpy()
+    return t.to(DEV), ref
+
+
+@pytest.mark.parametrize("topk_only", [False, True])
+@pytest.mark.parametrize("bias_dtype", [None, "bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16", "fp32"])
+def test_logits_row_bit_exact(i2h, topk_only, bias_dtype, out_dtype):
+    M, N, R = 3, 4133, 32                 # N not a multiple of 8: rows start unaligned in the flat pass
+    y_bits, sel, ex, bias = _logits_inputs(M, N, R, seed=11)
+    bt, bref = _bias_args(bias, bias_dtype)
+    say(f"logits topk={topk_only} bias={bias_dtype} out={out_dtype}")
+    out = i2h.logits(None if topk_only else dev_bf16(y_bits), torch.from_numpy(sel).to(DEV),
+                     torch.from_numpy(ex).to(DEV), topk_only=topk_only, bias=bt, out_dtype=_TDT[out_dtype],
+                     out=torch.empty(M, N, dtype=_TDT[out_dtype], device=DEV))
+    want = oracle.logits_row(y_bits, sel, ex, topk_only, bref, bias_dtype, out_dtype)
+    got = host(out) if out_dtype != "fp16" else out.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert got.dtype == want.dtype and np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("topk_only", [False, True])
+def test_logits_row_full_vocab_in_place(i2h, topk_only):
+    """The draft-slot row (M = 1, N = 124160) and a full-vocab block (M = 4, N = 248320), written
+    over the coarse row itself, with a bf16 bias."""
+    for M, N in ((1, 124160), (4, 248320)):
+        y_bits, sel, ex, bias = _logits_inputs(M, N, 32, seed=12 + M)
+        bt, bref = _bias_args(bias, "bf16")
+        y = dev_bf16(y_bits)
+        out = i2h.logits(y, torch.from_numpy(sel).to(DEV), torch.from_numpy(ex).to(DEV), topk_only=topk_only,
+                         bias=bt, out=y)
+        assert out.data_ptr() == y.data_ptr()
+        assert np.array_equal(host(out), oracle.logits_row(y_bits, sel, ex, topk_only, bref, "bf16", "bf16"))
