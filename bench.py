@@ -17,6 +17,9 @@ Prints one JSON line. `value` is the head's algorithmic HBM bytes per call divid
 measured time per call (GB/s); `us_per_call` is the same time. `roofline` covers the coarse
 kernel, the dominant one, timed with HIP events on the launch stream over the timed region.
 `cpu_baseline` times the oracle (test infrastructure, CPU) on the same workload.
+`dropin_logits` times the drop-in logits row at the same M: coarse pass with its bf16 row, the
+fused tail with its selection and exact scores, and i2h_logits writing the exact scores back
+(argmax caller, in place) or over a -inf row (top-k caller), per call and the write-back alone.
 """
 from __future__ import annotations
 
@@ -120,6 +123,15 @@ class Head:
                       P(self.oi), P(self.ov), s)
         self.a_head = [(P(x), M, P(p), P(S), P(Z), P(W), W.stride(0), N, K, KC, R, 1, P(self.oi), P(self.ov),
                         None, P(self.ws), ws_n, s) for (p, S, Z) in copies]
+        # the drop-in logits row: coarse with its bf16 row, the tail with its selection and exact
+        # scores, then the write-back in place (argmax caller) or over -inf (top-k caller)
+        self.y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        self.a_coarse_y = [(P(x), xs_arg, M, P(p), P(S), P(Z), N, K, KC, P(self.cs), P(self.ci), P(self.y), s)
+                           for (p, S, Z) in copies]
+        self.a_srr_sel = (P(self.cs), P(self.ci), M, nblk, KC, R, P(x), P(W), W.stride(0), N, K, 1, P(self.sel),
+                          P(self.ex), P(self.oi), P(self.ov), s)
+        self.a_logits = {topk: (None if topk else P(self.y), M, N, P(self.sel), P(self.ex), R, int(topk), None, 0,
+                                P(self.y), 1, s) for topk in (False, True)}
 
     def step(self, i, ev0=None, ev1=None):
         L = self.lib
@@ -142,6 +154,27 @@ class Head:
         for i in range(n):
             if L.i2h_coarse_topk(*self.a_coarse[(first + i) % len(self.a_coarse)]):
                 raise RuntimeError("libi2h coarse launch failed")
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    def dropin(self, i, topk=False):
+        L = self.lib
+        st = 0 if self.own_sums else L.i2h_xsum(*self.a_xsum)
+        coarse = self.a_coarse if topk else self.a_coarse_y  # a top-k caller needs no coarse row
+        st |= L.i2h_coarse_topk(*coarse[i % len(coarse)])
+        st |= L.i2h_select_rerank_topk(*self.a_srr_sel)
+        st |= L.i2h_logits(*self.a_logits[topk])
+        if st:
+            raise RuntimeError(f"libi2h status {st}")
+
+    def logits_only(self, torch, n, topk=False):
+        """Mean time of n back-to-back i2h_logits calls (row pass + write-back) by HIP events."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            if self.lib.i2h_logits(*self.a_logits[topk]):
+                raise RuntimeError("libi2h logits launch failed")
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / n
@@ -270,6 +303,19 @@ def main():
         torch.cuda.synchronize()
         return h, dt, coarse_ms, dt_fused
 
+    def measure_dropin(h, steps, warmup):
+        """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
+        res = {}
+        for topk in (False, True):
+            d, _ = time_steps(torch, lambda i, t=topk: h.dropin(i, t), steps, warmup)
+            h.logits_only(torch, warmup, topk)
+            lu = h.logits_only(torch, steps, topk)
+            name = "topk" if topk else "argmax"
+            res[f"{name}_us_per_call"] = round(d * 1e6, 2)
+            res[f"{name}_logits_us"] = round(lu, 2)
+        torch.cuda.synchronize()
+        return res
+
     log(f"[bench] timing M={M}: {args.warmup} warmup + {args.steps} steps")
     h, dt, coarse_ms, dt_fused = measure(M, args.steps, args.warmup)
     hb = head_bytes(M, N, K, own_sums=h.own_sums)
@@ -277,6 +323,9 @@ def main():
     coarse_us = coarse_ms * 1e3
     achieved = hb["coarse"] / (coarse_us * 1e-6) / 1e9
     traffic = traffic_for(M)
+    log(f"[bench] timing the drop-in logits row at M={M}")
+    dropin = measure_dropin(h, args.steps, args.warmup)
+    dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
 
     bands = []
     if not args.no_bands:
@@ -352,6 +401,7 @@ def main():
                      "algorithmic_bytes": hb["coarse"]},
         "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
                  "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},
+        "dropin_logits": dropin,
         **result,
         "bands": bands,
         "cpu_baseline": cpu,

@@ -6,9 +6,9 @@
 // bias is added with torch's type promotion (bf16 + bf16 rounds the fp32 sum back to bf16,
 // bf16 + fp16 or fp32 gives fp32) and the row is cast to the head dtype.
 //
-// Two launches on the caller's stream: an elementwise pass over [M, N] (8 entries per thread,
-// HBM-bound), then one thread per (row, reranked token) that overwrites that entry with the same
-// finishing arithmetic applied to the exact score.
+// One launch: each workgroup writes a chunk of one row (8 entries per thread) and then overwrites
+// the reranked tokens that fall in that chunk, with the same finishing arithmetic applied to the
+// exact score.
 #include <hip/hip_fp16.h>
 
 #include "device_util.h"
@@ -43,62 +43,53 @@ __device__ __forceinline__ void finish(float v, int64_t n, const void* __restric
   }
 }
 
-template <int BDT, int ODT>
-__global__ __launch_bounds__(kLogitsThreads) void logits_rows_kernel(const uint16_t* __restrict__ y, int64_t total,
-                                                                     int64_t N, const void* __restrict__ bias,
-                                                                     void* __restrict__ out) {
-  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
-  const int64_t i0 = ((int64_t)blockIdx.x * kLogitsThreads + threadIdx.x) * 8;
-  if (i0 >= total) return;
-  uint32_t w[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};  // -inf: the top-k caller's row
-  if (y != nullptr) {
-    if (i0 + 8 <= total) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(y + i0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = v[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (i0 + e < total) w[e >> 1] = (w[e >> 1] & ~(0xffffu << (16 * (e & 1)))) | ((uint32_t)y[i0 + e] << (16 * (e & 1)));
-    }
-  }
-  int64_t n = i0 % N;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (i0 + e < total) {
-      const float v = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      finish<BDT, ODT>(v, n, bias, out, i0 + e);
-    }
-    if (++n == N) n = 0;
-  }
-}
+// One workgroup per (row m, chunk of kChunk columns): the row pass over its columns (8 per
+// thread), a barrier, then the threads t < R write back the reranked tokens that fall in the
+// chunk, so every write-back lands after the row pass wrote the same entry.
+constexpr int kChunk = 8 * kLogitsThreads;
 
 template <int BDT, int ODT>
-__global__ __launch_bounds__(kLogitsThreads) void logits_writeback_kernel(const int32_t* __restrict__ sel,
-                                                                          const float* __restrict__ exact, int64_t M,
-                                                                          int R, int64_t N, const void* __restrict__ bias,
-                                                                          void* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * kLogitsThreads + threadIdx.x;
-  if (t >= M * R) return;
-  const int64_t m = t / R;
-  const int32_t n = sel[t];
-  if (n < 0 || n >= N) return;
-  const float v = __uint_as_float(f32_to_bf16_rne(exact[t]) << 16);  // the exact score as bf16
-  finish<BDT, ODT>(v, n, bias, out, m * N + n);
+__global__ __launch_bounds__(kLogitsThreads) void logits_kernel(const uint16_t* __restrict__ y, int64_t N,
+                                                                const int32_t* __restrict__ sel,
+                                                                const float* __restrict__ exact, int R,
+                                                                const void* __restrict__ bias, void* __restrict__ out) {
+  typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+  const int64_t m = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * kChunk;
+  const int64_t n0 = c0 + 8 * threadIdx.x;
+  const int64_t row = m * N;
+  if (n0 < N) {
+    uint32_t w[4] = {0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u};  // -inf: the top-k caller's row
+    if (y != nullptr) {
+      if (n0 + 8 <= N && (N & 7) == 0) {  // 16-byte aligned: every row starts on a multiple of 8
+        const u32x4 v = *reinterpret_cast<const u32x4*>(y + row + n0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = v[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n0 + e < N) w[e >> 1] = (w[e >> 1] & ~(0xffffu << (16 * (e & 1)))) | ((uint32_t)y[row + n0 + e] << (16 * (e & 1)));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (n0 + e < N) finish<BDT, ODT>((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), n0 + e, bias, out, row + n0 + e);
+  }
+  __syncthreads();  // the row pass of this chunk is done (workgroup-scope release/acquire)
+  for (int t = threadIdx.x; t < R; t += kLogitsThreads) {
+    const int32_t n = sel[m * R + t];
+    if (n >= c0 && n < c0 + kChunk && n < N) {
+      const float v = __uint_as_float(f32_to_bf16_rne(exact[m * R + t]) << 16);  // the exact score as bf16
+      finish<BDT, ODT>(v, n, bias, out, row + n);
+    }
+  }
 }
 
 template <int BDT, int ODT>
 int launch_logits(const uint16_t* y, int64_t M, int64_t N, const int32_t* sel, const float* exact, int R,
                   const void* bias, void* out, hipStream_t s) {
-  const int64_t total = M * N;
-  const int64_t blocks = (total + 8 * kLogitsThreads - 1) / (8 * kLogitsThreads);
-  hipLaunchKernelGGL((logits_rows_kernel<BDT, ODT>), dim3((unsigned)blocks), dim3(kLogitsThreads), 0, s, y, total, N,
-                     bias, out);
-  int st = check_launch();
-  if (st != I2H_OK) return st;
-  const int64_t wb = (M * R + kLogitsThreads - 1) / kLogitsThreads;
-  hipLaunchKernelGGL((logits_writeback_kernel<BDT, ODT>), dim3((unsigned)wb), dim3(kLogitsThreads), 0, s, sel, exact,
-                     M, R, N, bias, out);
+  const dim3 grid((unsigned)((N + kChunk - 1) / kChunk), (unsigned)M);
+  hipLaunchKernelGGL((logits_kernel<BDT, ODT>), grid, dim3(kLogitsThreads), 0, s, y, N, sel, exact, R, bias, out);
   return check_launch();
 }
 
@@ -124,7 +115,7 @@ extern "C" int i2h_logits(const uint16_t* y, int64_t M, int64_t N, const int32_t
   if (bias_dtype < I2H_DTYPE_NONE || bias_dtype > I2H_DTYPE_F32 || (bias_dtype == I2H_DTYPE_NONE) != (bias == nullptr))
     return I2H_ERR_ARG;
   if (out_dtype < I2H_DTYPE_BF16 || out_dtype > I2H_DTYPE_F32) return I2H_ERR_ARG;
-  if (M < 1 || N < 1 || M > ((int64_t)1 << 40) / N) return I2H_ERR_SHAPE;
+  if (M < 1 || N < 1 || M > 65535 || N > ((int64_t)1 << 40)) return I2H_ERR_SHAPE;
   if (R < 1 || R > I2H_MAX_R) return I2H_ERR_LIMIT;
   if ((y && !aligned(y, 16)) || !aligned(out, 16) || !aligned(sel, 4) || !aligned(exact, 4) ||
       (bias && !aligned(bias, dtype_bytes(bias_dtype))))

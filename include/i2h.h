@@ -195,9 +195,9 @@ I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const 
  *           i2h_rerank); a row's tokens must be distinct (as those calls give them).
  *   bias    [N] of bias_dtype (I2H_DTYPE_NONE with bias NULL for none), naturally aligned.
  *   out     [M, N] of out_dtype (BF16 / F16: uint16 bits; F32), 16-byte aligned. out may be y
- *           itself when out_dtype is I2H_DTYPE_BF16 (the row pass reads each entry before it
- *           writes it, and the write-back runs after it in stream order).
- * Two kernel launches on `stream`. Limits: 1 <= R <= 1024.
+ *           itself when out_dtype is I2H_DTYPE_BF16 (each entry is read before it is written,
+ *           and the write-back of a token follows the row pass over it).
+ * One kernel launch on `stream`. Limits: 1 <= M <= 65535, 1 <= R <= 1024.
  */
 I2H_API int i2h_logits(const uint16_t* y, int64_t M, int64_t N, const int32_t* sel, const float* exact, int R,
                        int topk_only, const void* bias, int bias_dtype, void* out, int out_dtype, void* stream);
