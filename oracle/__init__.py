@@ -8,11 +8,13 @@ values fixed by the page or by mathematics (closed forms, exact-grid constructio
 on small inputs, invariants and byte counts the page prints).
 """
 from .int2_head import (BLOCK_N, GROUP, bf16_to_f32, block_emit, check_shape, coarse_logits,
-                        dequantize, exact_logits, f32_to_bf16, finalize, group_sums, head, logits_row, pack,
+                        dequantize, exact_logits, f32_to_bf16, finalize, fp8_e4m3_decode, fp8_rows_f32,
+                        group_sums, head, logits_row, pack, pack_fp8, quantize_fp8, rerank_exact_fp8,
                         pack_quarter_split, premultiplied_scales, quantize, rerank_exact,
                         select_top_r, storage_bytes, unpack_quarter_split)
 
 __all__ = ["BLOCK_N", "GROUP", "bf16_to_f32", "block_emit", "check_shape", "coarse_logits",
-           "dequantize", "exact_logits", "f32_to_bf16", "finalize", "group_sums", "head", "logits_row", "pack",
+           "dequantize", "exact_logits", "f32_to_bf16", "finalize", "fp8_e4m3_decode", "fp8_rows_f32",
+           "group_sums", "head", "logits_row", "pack", "pack_fp8", "quantize_fp8", "rerank_exact_fp8",
            "pack_quarter_split", "premultiplied_scales", "quantize", "rerank_exact",
            "select_top_r", "storage_bytes", "unpack_quarter_split"]

@@ -103,7 +103,12 @@ def quantize(W_bits: np.ndarray, G: int = GROUP):
       zp = clamp(round(-lo / sc), 0, 3)       round half to even
       q  = clamp(round(w / sc + zp), 0, 3)    fp32 divide, fp32 add, round half to even
     """
-    N, K = W_bits.shape
+    return _quantize_rows(lambda a, b: bf16_to_f32(W_bits[a:b]), W_bits.shape, G)
+
+
+def _quantize_rows(rows, shape, G: int = GROUP):
+    """The quantiser of quantize() over fp32 rows [a, b) that rows(a, b) returns."""
+    N, K = shape
     if K % G:
         raise ValueError("K must be a multiple of G")
     q = np.empty((N, K), dtype=np.uint8)
@@ -113,7 +118,7 @@ def quantize(W_bits: np.ndarray, G: int = GROUP):
     floor = np.float32(1e-8)
 
     def run(a: int, b: int) -> None:
-        w = bf16_to_f32(W_bits[a:b]).reshape(b - a, K // G, G)
+        w = rows(a, b).astype(np.float32).reshape(b - a, K // G, G)
         lo = w.min(axis=2)
         hi = w.max(axis=2)
         sc = (hi - lo) / three
@@ -380,3 +385,51 @@ def logits_row(y_bits: np.ndarray, sel: np.ndarray, exact: np.ndarray, topk_only
     if out_dtype == "bf16":
         return f32_to_bf16(r)  # exact when the row already holds bf16 values
     return r.astype(np.float16).view(np.uint16)
+
+
+
+# ----------------------------------------------------------------------------------------------
+# NEXT f4: an FP8 e4m3 head with a per-row fp32 scale as the weight source
+# radiance_drafthead.py, _rerank_exact (FP8 branch): a byte b decodes by bit arithmetic as
+# sign (bit 7), exponent field e = bits 3-6, mantissa m = bits 0-2: m * 2^-9 when e = 0, else
+# (1 + m/8) * 2^(e - 7); the weight is that value times the row's fp32 scale, an fp32 product.
+# _quantize_head_now: the int2 head of such a weight quantises the same fp32 rows.
+# ----------------------------------------------------------------------------------------------
+def fp8_e4m3_decode(b: np.ndarray) -> np.ndarray:
+    """fp64 values of e4m3 bytes by the page's bit formula (exact; 0x7F decodes to 480)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((b & 128) != 0, -mag, mag)
+
+
+def fp8_rows_f32(W8: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """fp32 [rows, K]: decode(W8) * scale[row], one fp32 multiply (the decode is exact in fp32)."""
+    return (fp8_e4m3_decode(W8).astype(np.float32) * np.asarray(scale, np.float32)[:, None]).astype(np.float32)
+
+
+def quantize_fp8(W8: np.ndarray, scale: np.ndarray, G: int = GROUP):
+    """quantize() over the fp32 rows of an FP8 head (W8 uint8 [N, K], scale fp32 [N])."""
+    return _quantize_rows(lambda a, b: fp8_rows_f32(W8[a:b], scale[a:b]), W8.shape, G)
+
+
+def pack_fp8(W8: np.ndarray, scale: np.ndarray, G: int = GROUP):
+    """The stored int2 head of an FP8 head: (packed uint8 [N, K/4], S bits, ZS bits)."""
+    check_shape(W8.shape[1], G)
+    q, sc, zp = quantize_fp8(W8, scale, G)
+    S, ZS = premultiplied_scales(sc, zp)
+    return pack_quarter_split(q), S, ZS
+
+
+def rerank_exact_fp8(x_bits: np.ndarray, W8: np.ndarray, scale: np.ndarray, sel: np.ndarray) -> np.ndarray:
+    """e fp64 [M, R]: x against the fp32 rows of the FP8 head (products exact in fp64); -inf
+    where sel is -1."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    M, R = sel.shape
+    e = np.full((M, R), -np.inf)
+    for m in range(M):
+        ok = sel[m] >= 0
+        t = sel[m][ok]
+        e[m, ok] = fp8_rows_f32(W8[t], scale[t]).astype(np.float64) @ x[m]
+    return e

@@ -55,6 +55,16 @@ def _gen(seed: int) -> torch.Generator:
     return torch.Generator(device="cpu").manual_seed(int(seed))
 
 
+def gen_weight_fp8(N: int, K: int, seed: int = SEED_W, rowscale_seed: int = SEED_ROWSCALE):
+    """A per-channel FP8 head of the same weights: (e4m3 bytes uint8 [N, K], scale fp32 [N]),
+    scale = max |w| / 448 per row and the bytes torch's round-to-nearest cast of w / scale, on the
+    CPU (the storage of a compressed-tensors FP8 lm_head)."""
+    w = gen_weight(N, K, seed, rowscale_seed).float()
+    scale = (w.abs().amax(dim=1) / 448.0).clamp(min=1e-12)
+    w8 = (w / scale[:, None]).to(torch.float8_e4m3fn)
+    return w8.view(torch.uint8), scale.float()
+
+
 def gen_weight(N: int, K: int, seed: int = SEED_W, rowscale_seed: int = SEED_ROWSCALE) -> torch.Tensor:
     """bf16 [N, K] head weight (rows are vocab tokens), on the CPU."""
     u = torch.randn(N, generator=_gen(rowscale_seed), dtype=torch.float32)

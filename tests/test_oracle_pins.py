@@ -500,3 +500,57 @@ def test_logits_row_matches_eager_torch_steps(topk_only, bias_dtype, out_dtype):
     y = y.to(tdt[out_dtype])
     want = y.view(torch.int16).numpy().view(np.uint16) if out_dtype != "fp32" else y.numpy()
     assert got.dtype == want.dtype and np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 e4m3 weight source (radiance_drafthead.py, _rerank_exact FP8 branch; _quantize_head_now)
+# ---------------------------------------------------------------------------------------------
+def test_fp8_decode_hand_values():
+    """1.0 = 0x38, the smallest subnormal 2^-9 = 0x01, the smallest normal 2^-6 = 0x08, the
+    largest finite 448 = 0x7E, -1.0 = 0xB8; the page's formula reads 0x7F (a NaN code of e4m3fn)
+    as 480."""
+    got = oracle.fp8_e4m3_decode(np.array([0x38, 0x01, 0x08, 0x7E, 0xB8, 0x00, 0x7F], np.uint8))
+    assert got.tolist() == [1.0, 2.0 ** -9, 2.0 ** -6, 448.0, -1.0, 0.0, 480.0]
+
+
+def test_fp8_decode_matches_torch_e4m3fn():
+    """Every byte except the two NaN codes against torch's float8_e4m3fn -> float32 conversion."""
+    b = np.arange(256, dtype=np.uint8)
+    ok = (b & 0x7F) != 0x7F
+    t = torch.from_numpy(b.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    assert np.array_equal(oracle.fp8_e4m3_decode(b)[ok], t[ok])
+
+
+def test_fp8_rerank_against_fsum():
+    K, N = 1024, 200
+    x = si.bits(si.gen_x(2, K, outliers=8, seed=15))
+    W8, sc = si.gen_weight_fp8(N, K, seed=83)
+    sel = si.gen_rows(2, 11, N, seed=16).numpy()
+    sel[0, 2] = -1
+    e = oracle.rerank_exact_fp8(x, W8.numpy(), sc.numpy(), sel)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    rows = (W8.view(torch.float8_e4m3fn).float() * sc[:, None]).numpy().astype(np.float64)  # torch fp32 ops
+    for m in range(2):
+        for j in range(11):
+            if sel[m, j] < 0:
+                assert e[m, j] == -np.inf
+                continue
+            prods = xf[m] * rows[sel[m, j]]
+            assert abs(e[m, j] - math.fsum(prods)) <= K * 2.0 ** -52 * np.abs(prods).sum()
+
+
+def test_fp8_quantize_matches_eager_fp32_ops():
+    """Cross-check: the page's quantiser as eager torch fp32 ops on the FP8 head's fp32 rows
+    (torch's e4m3fn decode times the row scale)."""
+    W8, scale = si.gen_weight_fp8(300, 1024, seed=84)
+    w = (W8.view(torch.float8_e4m3fn).float() * scale[:, None]).reshape(300, 8, 128)
+    lo, hi = w.amin(2), w.amax(2)
+    sc = ((hi - lo) / 3).clamp(min=1e-8)
+    zp = torch.round(-lo / sc).clamp(0, 3)
+    qt = torch.round(w / sc[:, :, None] + zp[:, :, None]).clamp(0, 3).to(torch.uint8).reshape(300, 1024)
+    S = (4.0 * sc).to(torch.bfloat16)
+    ZS = (4.0 * sc + zp * sc).to(torch.bfloat16)
+    q, sco, zpo = oracle.quantize_fp8(W8.numpy(), scale.numpy())
+    So, ZSo = oracle.premultiplied_scales(sco, zpo)
+    assert np.array_equal(q, qt.numpy())
+    assert np.array_equal(So, si.bits(S)) and np.array_equal(ZSo, si.bits(ZS))
