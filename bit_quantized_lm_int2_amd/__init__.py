@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
-           "logits",
+           "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8",
            "GROUP",
            "BLOCK_N"]
 
@@ -49,6 +49,10 @@ _SIGNATURES = {
     "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
                   _I64, _P], _INT),
     "i2h_logits": ([_P, _I64, _I64, _P, _P, _INT, _INT, _P, _INT, _P, _INT, _P], _INT),
+    "i2h_pack_fp8": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
+    "i2h_rerank_fp8": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P, _INT, _P, _P], _INT),
+    "i2h_select_rerank_topk_fp8": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P,
+                                    _P, _P], _INT),
 }
 _DTYPE_CODES = {None: 0, torch.bfloat16: 1, torch.float16: 2, torch.float32: 3}
 
@@ -375,3 +379,79 @@ def logits(y, sel, exact, topk_only: bool = False, bias: torch.Tensor | None = N
                                           _ptr(bias), _DTYPE_CODES[None if bias is None else bias.dtype], _ptr(out),
                                           _DTYPE_CODES[out_dtype], _stream(sel)))
     return out
+
+
+def _fp8_head(W8, wscale):
+    _need(W8, "W8", torch.uint8, 2)
+    _need(wscale, "wscale", torch.float32, 1)
+    _dense(wscale, "wscale")
+    if wscale.shape[0] != W8.shape[0]:
+        raise ValueError("wscale must have one entry per row of W8")
+    if W8.stride(1) != 1:
+        raise ValueError("W8 rows must be contiguous")
+
+
+def pack_fp8(W8: torch.Tensor, wscale: torch.Tensor, out=None):
+    """pack() for an FP8 head: W8 uint8 e4m3 codes [N, K] with a per-row fp32 scale [N]."""
+    _fp8_head(W8, wscale)
+    N, K = W8.shape
+    if out is None:
+        packed = torch.empty(N, K // 4, dtype=torch.uint8, device=W8.device)
+        S = torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=W8.device)
+        ZS = torch.empty_like(S)
+    else:
+        packed, S, ZS = out
+    _shape(packed, "packed", (N, K // 4))
+    _shape(S, "S", (N, K // GROUP))
+    _shape(ZS, "ZS", (N, K // GROUP))
+    for t, nm in ((packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    _check("i2h_pack_fp8", lib().i2h_pack_fp8(_ptr(W8), _ptr(wscale), W8.stride(0), N, K, _ptr(packed), _ptr(S),
+                                              _ptr(ZS), _stream(W8)))
+    return packed, S, ZS
+
+
+def rerank_fp8(x, W8, wscale, sel) -> torch.Tensor:
+    """rerank() against an FP8 head (W8 uint8 [N, K], wscale fp32 [N])."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(sel, "sel", torch.int32, 2)
+    _fp8_head(W8, wscale)
+    _dense(x, "x")
+    _dense(sel, "sel")
+    M, K = x.shape
+    R = sel.shape[1]
+    _shape(sel, "sel", (M, R))
+    if W8.shape[1] != K:
+        raise ValueError("W8 must have K columns")
+    ex = torch.empty(M, R, dtype=torch.float32, device=x.device)
+    _check("i2h_rerank_fp8", lib().i2h_rerank_fp8(_ptr(x), M, _ptr(W8), W8.stride(0), W8.shape[0], K, _ptr(wscale),
+                                                  _ptr(sel), R, _ptr(ex), _stream(x)))
+    return ex
+
+
+def select_rerank_topk_fp8(cand_score, cand_idx, kcand: int, R: int, x, W8, wscale, k: int = 1,
+                           want_sel: bool = False):
+    """select_rerank_topk() with the exact scores against an FP8 head."""
+    _need(cand_score, "cand_score", torch.float32, 2)
+    _need(cand_idx, "cand_idx", torch.int32, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    _fp8_head(W8, wscale)
+    for t, n in ((cand_score, "cand_score"), (cand_idx, "cand_idx"), (x, "x")):
+        _dense(t, n)
+    M, ncand = cand_score.shape
+    _shape(cand_idx, "cand_idx", (M, ncand))
+    K = x.shape[1]
+    if ncand % kcand:
+        raise ValueError("candidate count is not a multiple of kcand")
+    if W8.shape[1] != K:
+        raise ValueError("W8 must have K columns")
+    dev = x.device
+    oi = torch.empty(M, k, dtype=torch.int32, device=dev)
+    ov = torch.empty(M, k, dtype=torch.float32, device=dev)
+    sel = torch.empty(M, R, dtype=torch.int32, device=dev) if want_sel else None
+    ex = torch.empty(M, R, dtype=torch.float32, device=dev) if want_sel else None
+    _check("i2h_select_rerank_topk_fp8",
+           lib().i2h_select_rerank_topk_fp8(_ptr(cand_score), _ptr(cand_idx), M, ncand // kcand, kcand, R, _ptr(x),
+                                            _ptr(W8), _ptr(wscale), W8.stride(0), W8.shape[0], K, k, _ptr(sel),
+                                            _ptr(ex), _ptr(oi), _ptr(ov), _stream(x)))
+    return (oi, ov, sel, ex) if want_sel else (oi, ov)

@@ -14,6 +14,7 @@
 // any multiply-add from being fused. It is also built without NaN semantics (min / max need no
 // quieting): W must be finite.
 #include "device_util.h"
+#include "fp8.h"
 #include "host_util.h"
 
 #pragma clang fp contract(off)
@@ -86,9 +87,14 @@ constexpr int kPackWaves = 4;
 // quarter t; two permlane swap rounds (rows t ^ 1, then t ^ 2) OR the four quarters together,
 // shifting each field into bits 2t on the way, and leave lane (t, g, p) with bytes
 // 32 t + 8 p .. +7, which it stores. Lane p = 0 of each (t, g) writes its group's S and ZS.
+// FP8: the weight is an FP8 head (e4m3 bytes Wv with a per-row fp32 scale); each weight is the
+// decoded byte times the row's scale (one fp32 product, as the page's quantiser sees it). Those
+// fp32 weights have full 24-bit significands, for which the exhaustive check of quot_rn (over
+// bf16 numerators) says nothing, so their codes use the IEEE division.
+template <bool FP8>
 __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
-    const uint16_t* __restrict__ W, int64_t ldw, int N, int K, uint8_t* __restrict__ packed,
-    uint16_t* __restrict__ S, uint16_t* __restrict__ ZS) {
+    const void* __restrict__ Wv, const float* __restrict__ wscale, int64_t ldw, int N, int K,
+    uint8_t* __restrict__ packed, uint16_t* __restrict__ S, uint16_t* __restrict__ ZS) {
   typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = lane >> 4, g = (lane >> 2) & 3, p = lane & 3;
@@ -105,11 +111,24 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
   const int dn = ustep / NG, dgb = ustep - dn * NG;
   int u = 4 * q0 + g;
   int n = u / NG, gb = u - n * NG;
+  float vs = 0.f;  // the row scale of the loaded weights (FP8)
   auto load = [&](u32x4 (&v)[4], int un, int ugb) {
     const int nc = un < N ? un : N - 1;  // past the last unit: a valid row, never stored
-    const uint16_t* src = W + (int64_t)nc * ldw + t * Q + ugb * kGroup + 8 * p;
+    const int64_t off = (int64_t)nc * ldw + t * Q + ugb * kGroup + 8 * p;  // in weights
+    if constexpr (FP8) {
+      typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+      const uint8_t* src = static_cast<const uint8_t*>(Wv) + off;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+      for (int c = 0; c < 4; ++c) {
+        const u32x2 b = *reinterpret_cast<const u32x2*>(src + 32 * c);
+        v[c] = u32x4{b[0], b[1], 0u, 0u};
+      }
+      vs = wscale[nc];
+    } else {
+      const uint16_t* src = static_cast<const uint16_t*>(Wv) + off;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const u32x4*>(src + 32 * c);
+    }
   };
   u32x4 v[4];
   load(v, n, gb);
@@ -117,10 +136,15 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
     float w[32];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      if constexpr (FP8) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w[8 * c + 2 * e] = bf16_lo(v[c][e]);
-        w[8 * c + 2 * e + 1] = bf16_hi(v[c][e]);
+        for (int e = 0; e < 8; ++e) w[8 * c + e] = __fmul_rn(fp8_e4m3_value(byte_of(v[c][0], v[c][1], e)), vs);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[8 * c + 2 * e] = bf16_lo(v[c][e]);
+          w[8 * c + 2 * e + 1] = bf16_hi(v[c][e]);
+        }
       }
     }
     const int cu = u, cn = n, cgb = gb;
@@ -141,22 +165,28 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
     lo = quad_min(lo);
     hi = quad_max(hi);
     const float sc = fmaxf(div3_rn(__fadd_rn(hi, -lo)), 1e-8f);
-    // The page's codes clamp(rint(fl(fl(w / sc) + zp)), 0, 3), with each quotient from quot_rn.
-    // The rounding to an integer is left to the byte conversion below (clamping to [0, 3] first
-    // gives the same code).
-    // Groups whose quotients could overflow, or whose 1 / sc could leave the normal range, take
-    // the IEEE division throughout (never met by a real head).
-    const bool wide = !(sc < 0x1p100f) || !(fmaxf(hi, -lo) < 0x1p100f);
-    const float y = __fdiv_rn(1.0f, sc);
-    float zp = clamp03(__builtin_rintf(quot_rn(-lo, sc, y)));
-    float q[32];
+    float zp, q[32];
+    if constexpr (FP8) {
+      zp = clamp03(rintf(__fdiv_rn(-lo, sc)));
 #pragma unroll
-    for (int e = 0; e < 32; ++e) q[e] = clamp03(__fadd_rn(quot_rn(w[e], sc, y), zp));
-    if (__builtin_amdgcn_ballot_w64(wide) != 0ull) {
-      if (wide) {
-        zp = clamp03(rintf(__fdiv_rn(-lo, sc)));
+      for (int e = 0; e < 32; ++e) q[e] = clamp03(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
+    } else {
+      // The page's codes clamp(rint(fl(fl(w / sc) + zp)), 0, 3), with each quotient from quot_rn.
+      // The rounding to an integer is left to the byte conversion below (clamping to [0, 3] first
+      // gives the same code).
+      // Groups whose quotients could overflow, or whose 1 / sc could leave the normal range, take
+      // the IEEE division throughout (never met by a real head).
+      const bool wide = !(sc < 0x1p100f) || !(fmaxf(hi, -lo) < 0x1p100f);
+      const float y = __fdiv_rn(1.0f, sc);
+      zp = clamp03(__builtin_rintf(quot_rn(-lo, sc, y)));
 #pragma unroll
-        for (int e = 0; e < 32; ++e) q[e] = clamp03(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
+      for (int e = 0; e < 32; ++e) q[e] = clamp03(__fadd_rn(quot_rn(w[e], sc, y), zp));
+      if (__builtin_amdgcn_ballot_w64(wide) != 0ull) {
+        if (wide) {
+          zp = clamp03(rintf(__fdiv_rn(-lo, sc)));
+#pragma unroll
+          for (int e = 0; e < 32; ++e) q[e] = clamp03(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
+        }
       }
     }
     // codes as bytes: v_cvt_pk_u8_f32 rounds to nearest with ties to even (as rint does) and
@@ -212,12 +242,15 @@ extern "C" int i2h_sizes(int64_t N, int64_t K, int64_t* packed_bytes, int64_t* s
   return I2H_OK;
 }
 
-extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
-                        uint16_t* S, uint16_t* ZS, void* stream) {
-  using namespace i2h;
-  if (!W || !packed || !S || !ZS) return I2H_ERR_ARG;
+namespace i2h {
+namespace {
+template <bool FP8>
+int pack_launch(const void* W, const float* wscale, int64_t ldw, int64_t N, int64_t K, uint8_t* packed, uint16_t* S,
+                uint16_t* ZS, hipStream_t stream) {
+  if (!W || !packed || !S || !ZS || (FP8 && !wscale)) return I2H_ERR_ARG;
   if (N < 1 || check_k(K) != I2H_OK || ldw < K) return I2H_ERR_SHAPE;
-  if (!aligned(W, 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 16) || !aligned(ZS, 16))
+  if (!aligned(W, FP8 ? 8 : 16) || ldw % 8 != 0 || !aligned(packed, 16) || !aligned(S, 16) || !aligned(ZS, 16) ||
+      (FP8 && !aligned(wscale, 4)))
     return I2H_ERR_ALIGN;
   // units (row, 128-byte span) are counted in 32 bits, with room for the grid stride
   if (N * (K / 512) > (int64_t)1 << 30) return I2H_ERR_SHAPE;
@@ -225,7 +258,19 @@ extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, ui
   const int64_t per_wg = (int64_t)kPackWaves * I2H_PACK_STEPS;
   int64_t grid = (quads + per_wg - 1) / per_wg;
   grid = grid < 1 ? 1 : (grid > I2H_PACK_MAX_WG ? I2H_PACK_MAX_WG : grid);
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)grid), dim3(kPackWaves * kWave), 0, (hipStream_t)stream, W,
-                     ldw, (int)N, (int)K, packed, S, ZS);
+  hipLaunchKernelGGL(pack_kernel<FP8>, dim3((unsigned)grid), dim3(kPackWaves * kWave), 0, stream, W, wscale, ldw,
+                     (int)N, (int)K, packed, S, ZS);
   return check_launch();
+}
+}  // namespace
+}  // namespace i2h
+
+extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
+                        uint16_t* S, uint16_t* ZS, void* stream) {
+  return i2h::pack_launch<false>(W, nullptr, ldw, N, K, packed, S, ZS, (hipStream_t)stream);
+}
+
+extern "C" int i2h_pack_fp8(const uint8_t* W8, const float* wscale, int64_t ldw, int64_t N, int64_t K,
+                            uint8_t* packed, uint16_t* S, uint16_t* ZS, void* stream) {
+  return i2h::pack_launch<true>(W8, wscale, ldw, N, K, packed, S, ZS, (hipStream_t)stream);
 }

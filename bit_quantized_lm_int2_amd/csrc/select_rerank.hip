@@ -16,6 +16,7 @@
 // The exact dot products use the same lane mapping and summation order as rerank.hip, so both
 // paths give the same bits.
 #include "dequant.h"
+#include "fp8.h"
 #include "host_util.h"
 #include "wave_rank.h"
 
@@ -233,11 +234,12 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
   __syncthreads();
 }
 
-template <int BPT>
+// FP8: the weight rows are e4m3 bytes (Wv) with a per-row fp32 scale (wscale); else bf16 rows.
+template <int BPT, bool FP8>
 __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     const float* __restrict__ cs, const int32_t* __restrict__ ci, int nblk, int kc, int R,
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W, int64_t ldw, int N, int K, int k,
-    int32_t* __restrict__ sel_out, float* __restrict__ ex_out, int32_t* __restrict__ oi,
+    const uint16_t* __restrict__ x, const void* __restrict__ Wv, const float* __restrict__ wscale, int64_t ldw,
+    int N, int K, int k, int32_t* __restrict__ sel_out, float* __restrict__ ex_out, int32_t* __restrict__ oi,
     float* __restrict__ ov) {
   extern __shared__ __align__(16) uint8_t smem[];
   SrLds& L = *reinterpret_cast<SrLds*>(smem);
@@ -330,27 +332,60 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     const int j1 = j0 + kSrWaves;
     const int n0 = L.sel[j0], n1 = j1 < R ? L.sel[j1] : -1;
     const bool v0 = n0 >= 0 && n0 < N, v1 = n1 >= 0 && n1 < N;
-    const uint16_t* w0 = W + (int64_t)(v0 ? n0 : 0) * ldw + 8 * lane;
-    const uint16_t* w1 = W + (int64_t)(v1 ? n1 : 0) * ldw + 8 * lane;
     float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
-    for (int i0 = 0; i0 < steps; i0 += kSrChunk) {
-      u32x4 r0[kSrChunk], r1[kSrChunk];
+    if constexpr (FP8) {
+      // 8 weights per lane per 512-k step: an 8-byte load of e4m3 codes, each weight decoded and
+      // scaled in fp32 (the order of rerank_fp8_kernel)
+      typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+      const uint8_t* W8 = static_cast<const uint8_t*>(Wv);
+      const uint8_t* w0 = W8 + (int64_t)(v0 ? n0 : 0) * ldw + 8 * lane;
+      const uint8_t* w1 = W8 + (int64_t)(v1 ? n1 : 0) * ldw + 8 * lane;
+      const float sc0 = wscale[v0 ? n0 : 0], sc1 = wscale[v1 ? n1 : 0];
+      for (int i0 = 0; i0 < steps; i0 += kSrChunk) {
+        u32x2 r0[kSrChunk], r1[kSrChunk];
 #pragma unroll
-      for (int i = 0; i < kSrChunk; ++i) {
-        const bool in = i0 + i < steps;
-        r0[i] = in && v0 ? ld16(w0 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
-        r1[i] = in && v1 ? ld16(w1 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kSrChunk; ++i) {
+          const bool in = i0 + i < steps;
+          r0[i] = in && v0 ? *reinterpret_cast<const u32x2*>(w0 + 512 * (i0 + i)) : u32x2{0u, 0u};
+          r1[i] = in && v1 ? *reinterpret_cast<const u32x2*>(w1 + 512 * (i0 + i)) : u32x2{0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < kSrChunk; ++i) {
+          if (i0 + i < steps) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a00 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e)), sc0), a00);
+              a01 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e + 1)), sc0), a01);
+              a10 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e)), sc1), a10);
+              a11 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e + 1)), sc1), a11);
+            }
+          }
+        }
       }
+    } else {
+      const uint16_t* W = static_cast<const uint16_t*>(Wv);
+      const uint16_t* w0 = W + (int64_t)(v0 ? n0 : 0) * ldw + 8 * lane;
+      const uint16_t* w1 = W + (int64_t)(v1 ? n1 : 0) * ldw + 8 * lane;
+      for (int i0 = 0; i0 < steps; i0 += kSrChunk) {
+        u32x4 r0[kSrChunk], r1[kSrChunk];
 #pragma unroll
-      for (int i = 0; i < kSrChunk; ++i) {
-        if (i0 + i < steps) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
+        for (int i = 0; i < kSrChunk; ++i) {
+          const bool in = i0 + i < steps;
+          r0[i] = in && v0 ? ld16(w0 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
+          r1[i] = in && v1 ? ld16(w1 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a00 = fmaf(bf16_lo(xv[e]), bf16_lo(r0[i][e]), a00);
-            a01 = fmaf(bf16_hi(xv[e]), bf16_hi(r0[i][e]), a01);
-            a10 = fmaf(bf16_lo(xv[e]), bf16_lo(r1[i][e]), a10);
-            a11 = fmaf(bf16_hi(xv[e]), bf16_hi(r1[i][e]), a11);
+        for (int i = 0; i < kSrChunk; ++i) {
+          if (i0 + i < steps) {
+            const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a00 = fmaf(bf16_lo(xv[e]), bf16_lo(r0[i][e]), a00);
+              a01 = fmaf(bf16_hi(xv[e]), bf16_hi(r0[i][e]), a01);
+              a10 = fmaf(bf16_lo(xv[e]), bf16_lo(r1[i][e]), a10);
+              a11 = fmaf(bf16_hi(xv[e]), bf16_hi(r1[i][e]), a11);
+            }
           }
         }
       }
@@ -390,28 +425,39 @@ bool select_rerank_supported(int64_t nblk, int kc, int R, int64_t N, int64_t K) 
          N >= 1 && N <= (int64_t)1 << 19 && check_k(K) == I2H_OK;
 }
 
-int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
-                         const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
-                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s) {
-  if (!cand_score || !cand_idx || !x || !W || !out_idx || !out_val) return I2H_ERR_ARG;
+namespace {
+template <bool FP8>
+int select_rerank_launch_t(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
+                           const uint16_t* x, const void* W, const float* wscale, int64_t ldw, int64_t N, int64_t K,
+                           int k, int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s) {
+  if (!cand_score || !cand_idx || !x || !W || !out_idx || !out_val || (FP8 && !wscale)) return I2H_ERR_ARG;
   if (M < 1 || M > (1 << 30) || nblk != nblk_of(N) || ldw < K) return I2H_ERR_SHAPE;
   if (!select_rerank_supported(nblk, kc, R, N, K)) return I2H_ERR_LIMIT;
   if (k < 1 || k > R) return I2H_ERR_LIMIT;
-  if (!aligned(cand_score, 4) || !aligned(cand_idx, 4) || !aligned(x, 16) || !aligned(W, 16) || ldw % 8 != 0 ||
-      !aligned(out_idx, 4) || !aligned(out_val, 4) || (sel && !aligned(sel, 4)) || (exact && !aligned(exact, 4)))
+  if (!aligned(cand_score, 4) || !aligned(cand_idx, 4) || !aligned(x, 16) || !aligned(W, FP8 ? 8 : 16) ||
+      ldw % 8 != 0 || (FP8 && !aligned(wscale, 4)) || !aligned(out_idx, 4) || !aligned(out_val, 4) ||
+      (sel && !aligned(sel, 4)) || (exact && !aligned(exact, 4)))
     return I2H_ERR_ALIGN;
   const size_t lds = kSrLdsHead + (size_t)K * 2;
   const dim3 grid((unsigned)M), block(kSrThreads);
   if (nblk <= kSrThreads)
-    hipLaunchKernelGGL(select_rerank_kernel<1>, grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x, W,
-                       ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+    hipLaunchKernelGGL((select_rerank_kernel<1, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
   else if (nblk <= 2 * kSrThreads)
-    hipLaunchKernelGGL(select_rerank_kernel<2>, grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x, W,
-                       ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+    hipLaunchKernelGGL((select_rerank_kernel<2, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
   else
-    hipLaunchKernelGGL(select_rerank_kernel<4>, grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x, W,
-                       ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+    hipLaunchKernelGGL((select_rerank_kernel<4, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
   return check_launch();
+}
+}  // namespace
+
+int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
+                         const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
+                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s) {
+  return select_rerank_launch_t<false>(cand_score, cand_idx, M, nblk, kc, R, x, W, nullptr, ldw, N, K, k, sel, exact,
+                                       out_idx, out_val, s);
 }
 
 }  // namespace i2h
@@ -422,4 +468,12 @@ extern "C" int i2h_select_rerank_topk(const float* cand_score, const int32_t* ca
                                       void* stream) {
   return i2h::select_rerank_launch(cand_score, cand_idx, M, nblk, kcand, R, x, W, ldw, N, K, k, sel, exact, out_idx,
                                    out_val, (hipStream_t)stream);
+}
+
+extern "C" int i2h_select_rerank_topk_fp8(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
+                                          int kcand, int R, const uint16_t* x, const uint8_t* W8, const float* wscale,
+                                          int64_t ldw, int64_t N, int64_t K, int k, int32_t* sel, float* exact,
+                                          int32_t* out_idx, float* out_val, void* stream) {
+  return i2h::select_rerank_launch_t<true>(cand_score, cand_idx, M, nblk, kcand, R, x, W8, wscale, ldw, N, K, k, sel,
+                                           exact, out_idx, out_val, (hipStream_t)stream);
 }

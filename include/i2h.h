@@ -86,6 +86,19 @@ I2H_API int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8
                      uint16_t* S, uint16_t* ZS, void* stream);
 
 /*
+ * i2h_pack for an FP8 head (radiance_drafthead.py, _quantize_head_now with a compressed-tensors
+ * per-channel FP8 lm_head): the weight is w[n, k] = decode(W8[n, k]) * wscale[n] in fp32, decode
+ * being the e4m3 bit formula of _rerank_exact (sign bit 7; exponent field e = bits 3-6, mantissa
+ * m = bits 0-2; m * 2^-9 when e = 0, else (1 + m/8) * 2^(e - 7)), and the rest is i2h_pack's
+ * quantiser on those fp32 rows, bit-exact against eager fp32 ops.
+ *   W8      uint8 e4m3 codes [N, K], row stride ldw bytes (>= K, multiple of 8), 8-byte aligned.
+ *   wscale  fp32 [N] per-row scale.
+ *   packed, S, ZS as in i2h_pack. Limits as in i2h_pack.
+ */
+I2H_API int i2h_pack_fp8(const uint8_t* W8, const float* wscale, int64_t ldw, int64_t N, int64_t K,
+                         uint8_t* packed, uint16_t* S, uint16_t* ZS, void* stream);
+
+/*
  * Per-group sums of x (radiance_drafthead.py, _apply_head_int2: the fp32 group sums the coarse
  * kernel uses for the zero point and the dequant bias).
  *   x   bf16 [M, K] (row stride K);  xs  fp32 [M, K/128]: xs[m, g] = sum of x[m, 128g .. 128g+127].
@@ -154,6 +167,15 @@ I2H_API int i2h_rerank_topk(const uint16_t* x, int64_t M, const uint16_t* W, int
                             float* out_val, void* stream);
 
 /*
+ * i2h_rerank against an FP8 head (radiance_drafthead.py, _rerank_exact, FP8 branch):
+ *   exact[m, j] = sum_k x[m,k] * fl32(decode(W8[sel[m,j], k]) * wscale[sel[m,j]])
+ * accumulated in fp32 (decode as in i2h_pack_fp8). W8 uint8 [N, K] with row stride ldw bytes
+ * (multiple of 8), 8-byte aligned; wscale fp32 [N]. A sel entry outside [0, N) gives -inf.
+ */
+I2H_API int i2h_rerank_fp8(const uint16_t* x, int64_t M, const uint8_t* W8, int64_t ldw, int64_t N, int64_t K,
+                           const float* wscale, const int32_t* sel, int R, float* exact, void* stream);
+
+/*
  * i2h_select, i2h_rerank and i2h_finalize in one kernel, one workgroup per row
  * (radiance_drafthead.py, _apply_head_int2 and _rerank_exact): the R best block candidates of each
  * row, their exact scores against the bf16 weight rows, and the k best of those. Same arguments,
@@ -168,6 +190,16 @@ I2H_API int i2h_select_rerank_topk(const float* cand_score, const int32_t* cand_
                                    int kcand, int R, const uint16_t* x, const uint16_t* W, int64_t ldw,
                                    int64_t N, int64_t K, int k, int32_t* sel, float* exact, int32_t* out_idx,
                                    float* out_val, void* stream);
+
+/*
+ * i2h_select_rerank_topk with the exact scores against an FP8 head (as i2h_rerank_fp8): same
+ * arguments, with W8/wscale in place of W; bit-identical to i2h_select + i2h_rerank_fp8 +
+ * i2h_finalize. Same limits.
+ */
+I2H_API int i2h_select_rerank_topk_fp8(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
+                                       int kcand, int R, const uint16_t* x, const uint8_t* W8, const float* wscale,
+                                       int64_t ldw, int64_t N, int64_t K, int k, int32_t* sel, float* exact,
+                                       int32_t* out_idx, float* out_val, void* stream);
 
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);

@@ -27,7 +27,8 @@ def test_header_declares_the_entry_points():
     want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
-            "i2h_select_rerank_topk", "i2h_logits"}
+            "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
+            "i2h_select_rerank_topk_fp8"}
     assert names == want
 
 
@@ -187,3 +188,21 @@ def test_logits_rejects_before_launch():
     assert f(P + 2, 1, 124160, P, P, 32, 0, None, 0, P, BF, None) == ALIGN     # y not 16-byte aligned
     assert f(P, 1, 124160, P, P, 32, 0, None, 0, P + 8, F32, None) == ALIGN    # out not 16-byte aligned
     assert f(P, 1, 124160, P, P, 32, 0, ODD, F32, P, BF, None) == ALIGN        # fp32 bias misaligned
+
+
+def test_fp8_entry_points_reject_before_launch():
+    lib = i2h.lib()
+    # W8, wscale, ldw, N, K, packed, S, ZS, stream
+    assert lib.i2h_pack_fp8(P, None, 5120, 100, 5120, P, P, P, None) == ARG        # no scale
+    assert lib.i2h_pack_fp8(P, P, 5120, 100, 5000, P, P, P, None) == SHAPE         # K % 512
+    assert lib.i2h_pack_fp8(P + 4, P, 5120, 100, 5120, P, P, P, None) == ALIGN     # W8 not 8-byte aligned
+    assert lib.i2h_pack_fp8(P, P + 2, 5120, 100, 5120, P, P, P, None) == ALIGN     # scale misaligned
+    # x, M, W8, ldw, N, K, wscale, sel, R, exact, stream
+    assert lib.i2h_rerank_fp8(P, 1, P, 5120, 100, 5120, None, P, 32, P, None) == ARG
+    assert lib.i2h_rerank_fp8(P, 1, P, 5120, 100, 5120, P, P, 0, P, None) == LIMIT
+    assert lib.i2h_rerank_fp8(P, 1, P, 5124, 100, 5120, P, P, 32, P, None) == ALIGN  # ldw % 8
+    f = lib.i2h_select_rerank_topk_fp8
+    # cand_score, cand_idx, M, nblk, kcand, R, x, W8, wscale, ldw, N, K, k, sel, exact, out_idx, out_val, stream
+    assert f(P, P, 1, 1940, 8, 32, P, P, None, 5120, 124160, 5120, 1, None, None, P, P, None) == ARG
+    assert f(P, P, 1, 1940, 8, 65, P, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == LIMIT
+    assert f(P, P, 1, 1940, 8, 32, P, P + 4, P, 5120, 124160, 5120, 1, None, None, P, P, None) == ALIGN

@@ -433,3 +433,84 @@ def test_logits_row_full_vocab_in_place(i2h, topk_only):
                          bias=bt, out=y)
         assert out.data_ptr() == y.data_ptr()
         assert np.array_equal(host(out), oracle.logits_row(y_bits, sel, ex, topk_only, bref, "bf16", "bf16"))
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 e4m3 per-row-scale weight source: pack bit-exact; rerank within the fp32 accumulation bound
+# ---------------------------------------------------------------------------------------------
+def _fp8_degenerate_rows(K):
+    return np.stack([np.zeros(K, np.uint8),                                  # all zero
+                     np.full(K, 0x38, np.uint8),                             # constant 1.0
+                     (np.arange(K) % 8 + 0x38).astype(np.uint8),             # all positive
+                     (np.arange(K) % 5 + 0xB8).astype(np.uint8),             # all negative
+                     np.where(np.arange(K) % 2 == 0, 0x7E, 0xFE).astype(np.uint8),  # +-448
+                     np.where(np.arange(K) % 3 == 0, 0x01, 0x81).astype(np.uint8)])  # subnormal codes
+
+
+@pytest.mark.parametrize("N,K", [(1000, 1024), (37, 5120)])
+def test_pack_fp8_bit_exact(i2h, N, K):
+    say(f"pack_fp8 N={N} K={K}")
+    W8, scale = si.gen_weight_fp8(N, K, seed=200 + N)
+    W8 = np.concatenate([W8.numpy(), _fp8_degenerate_rows(K)])
+    scale = np.concatenate([scale.numpy(), np.array([1.0, 0.5, 2.0 ** -10, 3.0, 1e-3, 7.0], np.float32)])
+    p, S, ZS = i2h.pack_fp8(torch.from_numpy(W8).to(DEV), torch.from_numpy(scale).to(DEV))
+    po, So, ZSo = oracle.pack_fp8(W8, scale)
+    assert np.array_equal(host(p), po)
+    assert np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+
+
+def test_pack_fp8_strided_rows(i2h):
+    K = 1024
+    W8, scale = si.gen_weight_fp8(300, K + 64, seed=9)
+    Wd = W8.to(DEV)[:, 24:24 + K]   # row stride K + 64 bytes, 24-byte offset (8-byte aligned)
+    p, S, ZS = i2h.pack_fp8(Wd, scale.to(DEV))
+    po, So, ZSo = oracle.pack_fp8(W8.numpy()[:, 24:24 + K], scale.numpy())
+    assert np.array_equal(host(p), po) and np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+
+
+def _fp8_rerank_check(ex_g, x_bits, W8, scale, sel):
+    """GPU fp32 dots against the fp64 dots of the same fp32 rows: within the fp32 accumulation
+    bound K * 2^-23 * sum |x w|."""
+    e = oracle.rerank_exact_fp8(x_bits, W8, scale, sel)
+    ok = sel >= 0
+    assert np.all(np.isneginf(ex_g[~ok]))
+    xf = np.abs(oracle.bf16_to_f32(x_bits).astype(np.float64))
+    for m, j in zip(*np.nonzero(ok)):
+        row = np.abs(oracle.fp8_rows_f32(W8[sel[m, j]][None], scale[sel[m, j]][None])[0].astype(np.float64))
+        bound = x_bits.shape[1] * 2.0 ** -23 * float(xf[m] @ row)
+        assert abs(float(ex_g[m, j]) - e[m, j]) <= bound, (m, j)
+
+
+def test_rerank_fp8(i2h):
+    M, N, K, R = 3, 2000, 5120, 32
+    x = si.gen_x(M, K, outliers=8, seed=31)
+    W8, scale = si.gen_weight_fp8(N, K, seed=32)
+    sel = si.gen_rows(M, R, N, seed=33).numpy()
+    sel[0, 5] = -1
+    sel[2, 7] = N + 3
+    ex = i2h.rerank_fp8(x.to(DEV), W8.to(DEV), scale.to(DEV), torch.from_numpy(sel).to(DEV))
+    sel_o = np.where(sel < N, sel, -1)
+    _fp8_rerank_check(host(ex), si.bits(x), W8.numpy(), scale.numpy(), sel_o)
+
+
+@pytest.mark.parametrize("M,N,kc,R,k", [(2, 124160, 8, 32, 1), (3, 5000, 8, 32, 16)])
+def test_select_rerank_fused_fp8(i2h, M, N, kc, R, k):
+    """The fused FP8 tail against select + rerank_fp8 + finalize (bit for bit) and the oracle."""
+    K = 5120
+    say(f"select_rerank_fp8 M={M} N={N}")
+    sc = si.gen_scores(M, N, seed=N + 5).numpy()
+    cs, ci = oracle.block_emit(sc.astype(np.float64), kc)
+    want_sel = oracle.select_top_r(cs, ci, R)
+    cs_d, ci_d = torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV)
+    x = si.gen_x(M, K, outliers=8, seed=34)
+    W8, scale = si.gen_weight_fp8(N, K, seed=35)
+    xd, W8d, sd = x.to(DEV), W8.to(DEV), scale.to(DEV)
+    sel = i2h.select(cs_d, ci_d, kc, R)
+    ex = i2h.rerank_fp8(xd, W8d, sd, sel)
+    oi, ov = i2h.finalize(ex, sel, k)
+    fi, fv, fsel, fex = i2h.select_rerank_topk_fp8(cs_d, ci_d, kc, R, xd, W8d, sd, k, want_sel=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fsel), want_sel)
+    assert torch.equal(fsel, sel) and torch.equal(fex, ex), "fused FP8 selection / exact scores differ"
+    assert torch.equal(fi, oi) and torch.equal(fv, ov), "fused FP8 top-k differs"
+    _fp8_rerank_check(host(fex), si.bits(x), W8.numpy(), scale.numpy(), host(fsel))
