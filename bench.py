@@ -20,6 +20,8 @@ kernel, the dominant one, timed with HIP events on the launch stream over the ti
 `dropin_logits` times the drop-in logits row at the same M: coarse pass with its bf16 row, the
 fused tail with its selection and exact scores, and i2h_logits writing the exact scores back
 (argmax caller, in place) or over a -inf row (top-k caller), per call and the write-back alone.
+`fp8_source` times the same weights as an FP8 e4m3 per-row-scale head: its load-time pack, and the
+fused tail reranking against the FP8 rows beside the bf16 one (back-to-back launches).
 """
 from __future__ import annotations
 
@@ -303,6 +305,48 @@ def main():
         torch.cuda.synchronize()
         return h, dt, coarse_ms, dt_fused
 
+    def measure_fp8(h, steps, warmup):
+        """The FP8 e4m3 per-row-scale source (the same weights in FP8): its load-time pack, and the
+        fused tail (selection, exact rerank against the FP8 rows, argmax) beside the bf16 one, each
+        timed back to back with HIP events on the candidates of one coarse call."""
+        W8, wsc = si.fp8_head_of(W)
+        pk8 = []
+        p8 = i2h.pack_fp8(W8, wsc)
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            i2h.pack_fp8(W8, wsc, out=p8)
+            b.record()
+            torch.cuda.synchronize()
+            pk8.append(a.elapsed_time(b) * 1e3)
+        h.step(0)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        a_fp8 = (P(h.cs), P(h.ci), M, (N + 63) // 64, KC, R, P(h.x), P(W8), P(wsc), W8.stride(0), N, K, 1, None,
+                 None, P(h.oi), P(h.ov), h.stream)
+
+        def tail_us(fn, args_):
+            for _ in range(warmup):
+                fn(*args_)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                if fn(*args_):
+                    raise RuntimeError("libi2h tail launch failed")
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / steps
+
+        L = h.lib
+        res = dict(pack_us=round(float(np.median(pk8)), 1),
+                   pack_bytes=N * K + 4 * N + N * K // 4 + 2 * N * (K // 128) * 2,
+                   tail_fp8_us=round(tail_us(L.i2h_select_rerank_topk_fp8, a_fp8), 2),
+                   tail_bf16_us=round(tail_us(L.i2h_select_rerank_topk, h.a_srr), 2))
+        res["pack_gbps"] = round(res["pack_bytes"] / (res["pack_us"] * 1e-6) / 1e9, 1)
+        del W8, wsc, p8
+        torch.cuda.synchronize()
+        return res
+
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
         res = {}
@@ -323,6 +367,8 @@ def main():
     coarse_us = coarse_ms * 1e3
     achieved = hb["coarse"] / (coarse_us * 1e-6) / 1e9
     traffic = traffic_for(M)
+    log(f"[bench] FP8 weight source at M={M}: pack and fused tail")
+    fp8 = measure_fp8(h, args.steps, args.warmup)
     log(f"[bench] timing the drop-in logits row at M={M}")
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
@@ -402,6 +448,7 @@ def main():
         "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
                  "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},
         "dropin_logits": dropin,
+        "fp8_source": fp8,
         **result,
         "bands": bands,
         "cpu_baseline": cpu,

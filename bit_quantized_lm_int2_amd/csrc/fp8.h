@@ -9,10 +9,12 @@
 
 namespace i2h {
 
+// The 7 low bits placed at bits 20-26 of an fp32 read as 2^(e - 127) (1 + m/8) for e > 0 and as
+// the subnormal m * 2^-129 for e = 0; times 2^120 (exact: a power-of-two scaling, fp32 denormals
+// kept) that is the formula's value, 0x7F included. The sign bit goes to bit 31.
 __device__ __forceinline__ float fp8_e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  const float mag = e != 0u ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (b & 0x80u) ? -mag : mag;
+  const uint32_t bits = ((b & 0x7fu) << 20) | ((b & 0x80u) << 24);
+  return __uint_as_float(bits) * 0x1p120f;
 }
 
 // Byte i (0..7) of two dwords.

@@ -55,14 +55,19 @@ def _gen(seed: int) -> torch.Generator:
     return torch.Generator(device="cpu").manual_seed(int(seed))
 
 
-def gen_weight_fp8(N: int, K: int, seed: int = SEED_W, rowscale_seed: int = SEED_ROWSCALE):
-    """A per-channel FP8 head of the same weights: (e4m3 bytes uint8 [N, K], scale fp32 [N]),
-    scale = max |w| / 448 per row and the bytes torch's round-to-nearest cast of w / scale, on the
-    CPU (the storage of a compressed-tensors FP8 lm_head)."""
-    w = gen_weight(N, K, seed, rowscale_seed).float()
-    scale = (w.abs().amax(dim=1) / 448.0).clamp(min=1e-12)
-    w8 = (w / scale[:, None]).to(torch.float8_e4m3fn)
+def fp8_head_of(w: torch.Tensor):
+    """The per-channel FP8 form of a head w [N, K] (any float dtype, any device): (e4m3 bytes
+    uint8 [N, K], scale fp32 [N]) with scale = max |w| / 448 per row and the bytes torch's
+    round-to-nearest cast of w / scale (the storage of a compressed-tensors FP8 lm_head)."""
+    wf = w.float()
+    scale = (wf.abs().amax(dim=1) / 448.0).clamp(min=1e-12)
+    w8 = (wf / scale[:, None]).to(torch.float8_e4m3fn)
     return w8.view(torch.uint8), scale.float()
+
+
+def gen_weight_fp8(N: int, K: int, seed: int = SEED_W, rowscale_seed: int = SEED_ROWSCALE):
+    """fp8_head_of(gen_weight(N, K)), on the CPU."""
+    return fp8_head_of(gen_weight(N, K, seed, rowscale_seed))
 
 
 def gen_weight(N: int, K: int, seed: int = SEED_W, rowscale_seed: int = SEED_ROWSCALE) -> torch.Tensor:

@@ -10,6 +10,11 @@
  *     the roundings while no intermediate overflows or underflows, so b in [1, 2) and a in [1, 2)
  *     cover every normal case.
  *
+ *  3. The e4m3 decode of the FP8 weight source (radiance_drafthead.py, _rerank_exact: sign bit
+ *     7, exponent field e = bits 3-6, mantissa m = bits 0-2, value m * 2^-9 for e = 0 else
+ *     (1 + m/8) * 2^(e - 7)) equals the fp32 whose bits are (b & 0x7F) << 20 | (b & 0x80) << 24
+ *     times 2^120, for all 256 codes.
+ *
  * The references are IEEE division in fp32 (1) and fp64 division rounded to fp32 (2); the
  * latter is exact here because a / b (an 8-bit by 24-bit quotient) never lies within 2^-49 of
  * an fp32 rounding midpoint. Build: cc -O2 -ffp-contract=off [-fopenmp] pack_arith_check.c -lm
@@ -51,7 +56,16 @@ int main(void) {
       ++n_quot;
     }
   }
+  unsigned bad_fp8 = 0;
+  for (uint32_t b = 0; b < 256; ++b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const double mag = e == 0 ? m * ldexp(1.0, -9) : (1.0 + m / 8.0) * ldexp(1.0, (int)e - 7);
+    const double ref = (b & 0x80u) ? -mag : mag;
+    const float got = from_bits(((b & 0x7fu) << 20) | ((b & 0x80u) << 24)) * 0x1p120f;
+    bad_fp8 += (double)got != ref;
+  }
+  printf("fp8 checked 256 mismatches %u\n", bad_fp8);
   printf("div3 checked %llu mismatches %llu\n", n_div3, bad_div3);
   printf("quot checked %llu mismatches %llu\n", n_quot, bad_quot);
-  return (bad_div3 || bad_quot || n_div3 != 0x7F800000ull || n_quot != (128ull << 23)) ? 1 : 0;
+  return (bad_fp8 || bad_div3 || bad_quot || n_div3 != 0x7F800000ull || n_quot != (128ull << 23)) ? 1 : 0;
 }

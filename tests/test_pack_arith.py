@@ -1,4 +1,5 @@
-"""Exhaustive host checks of the fp32 identities behind the packer's exact arithmetic.
+"""Exhaustive host checks of the fp32 identities behind the packer's exact arithmetic and the
+FP8 decode.
 
 radiance_drafthead.py, _quantize_head_now: the scale is (hi - lo) / 3 and the codes come from
 w / sc, each an IEEE fp32 division. The packer forms the first with an FMA-corrected product by
@@ -32,6 +33,7 @@ def test_exhaustive_division_identities():
             cmd.remove("-fopenmp")
             subprocess.run(cmd, check=True, capture_output=True)
         p = subprocess.run([exe], capture_output=True, text=True, timeout=600)
+    assert "fp8 checked 256 mismatches 0" in p.stdout, p.stdout
     assert "div3 checked 2139095040 mismatches 0" in p.stdout, p.stdout
     assert "quot checked 1073741824 mismatches 0" in p.stdout, p.stdout
     assert p.returncode == 0
