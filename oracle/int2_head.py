@@ -106,15 +106,16 @@ def quantize(W_bits: np.ndarray, G: int = GROUP):
     return _quantize_rows(lambda a, b: bf16_to_f32(W_bits[a:b]), W_bits.shape, G)
 
 
-def _quantize_rows(rows, shape, G: int = GROUP):
-    """The quantiser of quantize() over fp32 rows [a, b) that rows(a, b) returns."""
+def _quantize_rows(rows, shape, G: int = GROUP, levels: int = 3):
+    """The quantiser of quantize() over fp32 rows [a, b) that rows(a, b) returns, with codes
+    0..levels (3 for 2 bits, 15 for 4 bits)."""
     N, K = shape
     if K % G:
         raise ValueError("K must be a multiple of G")
     q = np.empty((N, K), dtype=np.uint8)
     sc_all = np.empty((N, K // G), dtype=np.float32)
     zp_all = np.empty((N, K // G), dtype=np.float32)
-    three = np.float32(3.0)
+    three = np.float32(levels)
     floor = np.float32(1e-8)
 
     def run(a: int, b: int) -> None:
@@ -433,3 +434,88 @@ def rerank_exact_fp8(x_bits: np.ndarray, W8: np.ndarray, scale: np.ndarray, sel:
         t = sel[m][ok]
         e[m, ok] = fp8_rows_f32(W8[t], scale[t]).astype(np.float64) @ x[m]
     return e
+
+
+
+# ----------------------------------------------------------------------------------------------
+# NEXT f3: the int4 head (the page's comparison point, used at KCAND = 1)
+# radiance_drafthead.py, _quantize_head_now (BITS = 4 branch) and the module docstring: the same
+# asymmetric min/max quantiser with codes 0..15; byte j of a packed row holds the codes of k = j
+# (bits 0-3) and K/2 + j (bits 4-7); the bit-pattern dequant reads 1 + v/16, so S = bf16(16 sc)
+# and ZS = bf16(16 sc + zp sc). The page prints no 4-bit kernel: its coarse logits follow from the
+# same fold, c = sum_g S P - xs ZS with P = sum_k x (1 + v/16).
+# Reading: K must be a multiple of 2 * G (each half of a row holds whole groups), the page's own
+# check for this layout.
+# ----------------------------------------------------------------------------------------------
+def check_shape4(K: int, G: int = GROUP) -> None:
+    if K <= 0 or K % (2 * G):
+        raise ValueError(f"K = {K} must be a positive multiple of {2 * G} for the int4 head")
+
+
+def quantize4(W_bits: np.ndarray, G: int = GROUP):
+    """quantize() with codes 0..15: q uint8 [N, K], sc, zp fp32 [N, K/G]."""
+    return _quantize_rows(lambda a, b: bf16_to_f32(W_bits[a:b]), W_bits.shape, G, levels=15)
+
+
+def premultiplied_scales4(sc: np.ndarray, zp: np.ndarray):
+    """S = bf16(16 sc), ZS = bf16(16 sc + zp sc) (fp32 products and sum, then bf16)."""
+    sixteen = np.float32(16.0)
+    s16 = (sixteen * sc).astype(np.float32)
+    zs = (s16 + (zp * sc).astype(np.float32)).astype(np.float32)
+    return f32_to_bf16(s16), f32_to_bf16(zs)
+
+
+def pack_half_split(q: np.ndarray) -> np.ndarray:
+    """uint8 [N, K/2]: byte j = q[j] | q[K/2 + j] << 4."""
+    N, K = q.shape
+    H = K // 2
+    q = q.astype(np.uint8)
+    return (q[:, :H] | (q[:, H:] << 4)).astype(np.uint8)
+
+
+def unpack_half_split(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_half_split: v uint8 [N, K]."""
+    return np.concatenate([packed & np.uint8(15), packed >> np.uint8(4)], axis=1).astype(np.uint8)
+
+
+def pack4(W_bits: np.ndarray, G: int = GROUP):
+    """The stored int4 head: (packed uint8 [N, K/2], S bits [N, K/G], ZS bits [N, K/G])."""
+    check_shape4(W_bits.shape[1], G)
+    q, sc, zp = quantize4(W_bits, G)
+    S, ZS = premultiplied_scales4(sc, zp)
+    return pack_half_split(q), S, ZS
+
+
+def dequantize4(packed: np.ndarray, S_bits: np.ndarray, ZS_bits: np.ndarray, G: int = GROUP) -> np.ndarray:
+    """fp64 [N, K]: S (1 + v/16) - ZS per group (exact)."""
+    v = unpack_half_split(packed).astype(np.float64)
+    s = np.repeat(bf16_to_f32(S_bits).astype(np.float64), G, axis=1)
+    zs = np.repeat(bf16_to_f32(ZS_bits).astype(np.float64), G, axis=1)
+    return s * (1.0 + v / 16.0) - zs
+
+
+def coarse_logits4(x_bits: np.ndarray, packed: np.ndarray, S_bits: np.ndarray, ZS_bits: np.ndarray,
+                   G: int = GROUP) -> np.ndarray:
+    """c fp64 [M, N] = x @ dequantize4(...)^T."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    N = packed.shape[0]
+    c = np.empty((x.shape[0], N), dtype=np.float64)
+
+    def run(a: int, b: int) -> None:
+        c[:, a:b] = x @ dequantize4(packed[a:b], S_bits[a:b], ZS_bits[a:b], G).T
+
+    _map_chunks(run, N)
+    return c
+
+
+def head4(x_bits: np.ndarray, W_bits: np.ndarray, packed: np.ndarray, S_bits: np.ndarray,
+          ZS_bits: np.ndarray, kcand: int = 1, R: int = 32, k: int = 1, G: int = GROUP,
+          block_n: int = BLOCK_N) -> dict:
+    """One call of the int4 head: coarse over the int4 copy, then the same emit, selection, exact
+    rerank and finalize as head()."""
+    c = coarse_logits4(x_bits, packed, S_bits, ZS_bits, G)
+    cs, ci = block_emit(c, kcand, block_n)
+    sel = select_top_r(cs, ci, R)
+    e = rerank_exact(x_bits, W_bits, sel)
+    oi, ov = finalize(e, sel, k)
+    return dict(coarse=c, cand_score=cs, cand_idx=ci, sel=sel, exact=e, idx=oi, val=ov)

@@ -554,3 +554,78 @@ def test_fp8_quantize_matches_eager_fp32_ops():
     So, ZSo = oracle.premultiplied_scales(sco, zpo)
     assert np.array_equal(q, qt.numpy())
     assert np.array_equal(So, si.bits(S)) and np.array_equal(ZSo, si.bits(ZS))
+
+
+# ---------------------------------------------------------------------------------------------
+# int4 head (radiance_drafthead.py, _quantize_head_now BITS = 4: codes 0..15, half-split bytes,
+# bias 16)
+# ---------------------------------------------------------------------------------------------
+def test_pack_half_split_worked_example():
+    """By hand: K = 8, q = [1 2 15 0 | 3 4 5 6]: byte j = q[j] | q[4 + j] << 4."""
+    q = np.array([[1, 2, 15, 0, 3, 4, 5, 6]], np.uint8)
+    assert oracle.pack_half_split(q).tolist() == [[0x31, 0x42, 0x5F, 0x60]]
+    assert np.array_equal(oracle.unpack_half_split(oracle.pack_half_split(q)), q)
+
+
+def test_pack_half_split_round_trip_random():
+    q = np.random.default_rng(3).integers(0, 16, (7, 512)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_half_split(oracle.pack_half_split(q)), q)
+
+
+def grid_head4(N, K, seed):
+    """W whose every group is sc * (q - zp) with sc a power of two, q in 0..15 with 0 and 15
+    present, zp in 0..15: exact in bf16, so the 4-bit quantiser must recover q, zp and sc."""
+    rng = np.random.default_rng(seed)
+    G = 128
+    ng = K // G
+    q = rng.integers(0, 16, size=(N, K)).astype(np.int64)
+    qg = q.reshape(N, ng, G)
+    qg[:, :, 0] = 0
+    qg[:, :, 1] = 15
+    zp = rng.integers(0, 16, size=(N, ng))
+    e = rng.integers(-14, -6, size=(N, ng))
+    sc = np.ldexp(1.0, e)
+    w = (sc[:, :, None] * (qg - zp[:, :, None])).reshape(N, K)
+    Wb = oracle.f32_to_bf16(w.astype(np.float32))
+    assert np.array_equal(oracle.bf16_to_f32(Wb).astype(np.float64), w)
+    return Wb, q.reshape(N, K), zp, sc
+
+
+def test_int4_exact_grid_head_recovers_codes_and_logits():
+    N, K = 150, 1024
+    Wb, q, zp, sc = grid_head4(N, K, 5)
+    q4, sc4, zp4 = oracle.quantize4(Wb)
+    assert np.array_equal(q4, q) and np.array_equal(zp4, zp) and np.array_equal(sc4.astype(np.float64), sc)
+    p, S, ZS = oracle.pack4(Wb)
+    assert np.array_equal(oracle.bf16_to_f32(S).astype(np.float64), 16 * sc)
+    assert np.array_equal(oracle.bf16_to_f32(ZS).astype(np.float64), (16 + zp) * sc)
+    # the bias-16 fold reproduces the weight exactly, so the coarse logits are the exact ones
+    assert np.array_equal(oracle.dequantize4(p, S, ZS), oracle.bf16_to_f32(Wb).astype(np.float64))
+    x = si.bits(si.gen_x(3, K, outliers=4, seed=41))
+    assert np.allclose(oracle.coarse_logits4(x, p, S, ZS), oracle.exact_logits(x, Wb), rtol=0, atol=1e-9)
+
+
+def test_int4_quantize_matches_eager_fp32_ops():
+    """Cross-check: the page's 4-bit quantiser and bias-16 premultiply as eager torch fp32 ops."""
+    W = si.gen_weight(200, 1024, seed=87)
+    w = W.float().reshape(200, 8, 128)
+    lo, hi = w.amin(2), w.amax(2)
+    sc = ((hi - lo) / 15).clamp(min=1e-8)
+    zp = torch.round(-lo / sc).clamp(0, 15)
+    qt = torch.round(w / sc[:, :, None] + zp[:, :, None]).clamp(0, 15).to(torch.uint8).reshape(200, 1024)
+    S = (16.0 * sc).to(torch.bfloat16)
+    ZS = (16.0 * sc + zp * sc).to(torch.bfloat16)
+    q, sco, zpo = oracle.quantize4(si.bits(W))
+    So, ZSo = oracle.premultiplied_scales4(sco, zpo)
+    assert np.array_equal(q, qt.numpy())
+    assert np.array_equal(So, si.bits(S)) and np.array_equal(ZSo, si.bits(ZS))
+    packed = (qt[:, :512] | (qt[:, 512:] << 4)).numpy()
+    assert np.array_equal(oracle.pack_half_split(q), packed)
+
+
+def test_int4_shape_rule():
+    oracle.check_shape4(256)
+    oracle.check_shape4(5120)
+    for bad in (0, 128, 384, 5000):
+        with pytest.raises(ValueError):
+            oracle.check_shape4(bad)
