@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
-           "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8",
+           "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8", "pack4", "coarse4_topk",
            "GROUP",
            "BLOCK_N"]
 
@@ -50,6 +50,8 @@ _SIGNATURES = {
                   _I64, _P], _INT),
     "i2h_logits": ([_P, _I64, _I64, _P, _P, _INT, _INT, _P, _INT, _P, _INT, _P], _INT),
     "i2h_pack_fp8": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
+    "i2h_pack4": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
+    "i2h_coarse4_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P], _INT),
     "i2h_rerank_fp8": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P, _INT, _P, _P], _INT),
     "i2h_select_rerank_topk_fp8": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P,
                                     _P, _P], _INT),
@@ -455,3 +457,45 @@ def select_rerank_topk_fp8(cand_score, cand_idx, kcand: int, R: int, x, W8, wsca
                                             _ptr(W8), _ptr(wscale), W8.stride(0), W8.shape[0], K, k, _ptr(sel),
                                             _ptr(ex), _ptr(oi), _ptr(ov), _stream(x)))
     return (oi, ov, sel, ex) if want_sel else (oi, ov)
+
+
+def pack4(W: torch.Tensor, out=None):
+    """The int4 head of a bf16 head W [N, K]: (packed4 u8 [N, K/2], S bf16 [N, K/128], ZS)."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    if out is None:
+        packed = torch.empty(N, K // 2, dtype=torch.uint8, device=W.device)
+        S = torch.empty(N, K // GROUP, dtype=torch.bfloat16, device=W.device)
+        ZS = torch.empty_like(S)
+    else:
+        packed, S, ZS = out
+    _shape(packed, "packed4", (N, K // 2))
+    _shape(S, "S", (N, K // GROUP))
+    _shape(ZS, "ZS", (N, K // GROUP))
+    for t, nm in ((packed, "packed4"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    _check("i2h_pack4", lib().i2h_pack4(_ptr(W), _rows(W, "W"), N, K, _ptr(packed), _ptr(S), _ptr(ZS), _stream(W)))
+    return packed, S, ZS
+
+
+def coarse4_topk(x, xs, packed4, S, ZS, kcand: int = 1, want_y: bool = False):
+    """(cand_score fp32 [M, NBLK*kcand], cand_idx int32 [M, NBLK*kcand][, y bf16 [M, N]]) of the
+    int4 head; xs from xsum(x)."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(packed4, "packed4", torch.uint8, 2)
+    _need(xs, "xs", torch.float32, 2)
+    for t, nm in ((x, "x"), (xs, "xs"), (packed4, "packed4"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    M, K = x.shape
+    N = packed4.shape[0]
+    _shape(packed4, "packed4", (N, K // 2))
+    _shape(S, "S", (N, K // GROUP))
+    _shape(ZS, "ZS", (N, K // GROUP))
+    _shape(xs, "xs", (M, K // GROUP))
+    nblk = (N + BLOCK_N - 1) // BLOCK_N
+    cs = torch.empty(M, nblk * kcand, dtype=torch.float32, device=x.device)
+    ci = torch.empty(M, nblk * kcand, dtype=torch.int32, device=x.device)
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=x.device) if want_y else None
+    _check("i2h_coarse4_topk", lib().i2h_coarse4_topk(_ptr(x), _ptr(xs), M, _ptr(packed4), _ptr(S), _ptr(ZS), N, K,
+                                                      kcand, _ptr(cs), _ptr(ci), _ptr(y), _stream(x)))
+    return (cs, ci, y) if want_y else (cs, ci)

@@ -1,0 +1,215 @@
+// Coarse logits and block candidates of the int4 head.
+//
+// radiance_drafthead.py (the module docstring's bit-pattern dequant, bias fold and accumulator
+// scaling, written for the 4-bit layout of _quantize_head_now): byte j of a packed row [K/2]
+// holds the codes of k = j (bits 0-3) and K/2 + j (bits 4-7); the bf16 pattern 0x3F80 | v << 3
+// reads as 1 + v/16, and with S = 16 sc, ZS = 16 sc + zp sc each group contributes
+// S * sum_k x (1 + v/16) - xs * ZS. The page prints no 4-bit kernel; this is the 2-bit coarse
+// kernel's structure with the half-split layout: a 128-byte span of a row feeds group gb of the
+// first half and group KG/2 + gb of the second, each through 4 MFMAs (16x16x32 bf16) per m-tile.
+//
+// One 4-wave workgroup per 64-column block; lane (col = l & 15, h = l >> 4) streams bytes
+// 32 h .. 32 h + 31 of each span of its row, x comes from L2 (this path is not tuned for
+// bandwidth), and the emit ranks the block's columns with a wave bitonic sort (any kcand <= 64).
+#include "dequant.h"
+#include "host_util.h"
+
+namespace i2h {
+namespace {
+
+constexpr int kC4Threads = 256;
+
+// Bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3], so that one mask takes the nibbles of b0 and b1 (then b2
+// and b3) into the two bf16 halves of a dword.
+__device__ __forceinline__ uint32_t pair_bytes4(uint32_t d) { return __builtin_amdgcn_perm(d, d, 0x03010200u); }
+
+// Eight weights of half HALF as bf16 1 + v/16 in natural k order; d0/d1 are byte-paired dwords.
+template <int HALF>
+__device__ __forceinline__ bf16x8 dequant4x8(uint32_t d0, uint32_t d1) {
+  constexpr uint32_t kMask = 0x00780078u, kOne = 0x3F803F80u;
+  u32x4 r;
+  if constexpr (HALF == 0) {
+    r[0] = ((d0 << 3) & kMask) | kOne;
+    r[1] = ((d0 >> 5) & kMask) | kOne;
+    r[2] = ((d1 << 3) & kMask) | kOne;
+    r[3] = ((d1 >> 5) & kMask) | kOne;
+  } else {
+    r[0] = ((d0 >> 1) & kMask) | kOne;
+    r[1] = ((d0 >> 9) & kMask) | kOne;
+    r[2] = ((d1 >> 1) & kMask) | kOne;
+    r[3] = ((d1 >> 9) & kMask) | kOne;
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <int MT, int HALF>
+__device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8], const uint16_t* xq, int M, int K,
+                                      int col, float sv, float zv, const float* xsg, int h) {
+  f32x4 p[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) p[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bf16x8 b = dequant4x8<HALF>(dw[2 * s], dw[2 * s + 1]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + col;
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (m < M) a = ld16(xq + (int64_t)m * K + 8 * s);
+      p[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, p[mt], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(xsg + mt * 16 + 4 * h);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = fmaf(sv, p[mt][r], acc[mt][r]);
+      acc[mt][r] = fmaf(-xv[r], zv, a);
+    }
+  }
+}
+
+// Descending bitonic sort across the wave of (value, column); better = larger value, then lower
+// column. Afterwards lane r holds the r-th best.
+__device__ __forceinline__ void wave_sort_vc(float& v, int& c, int lane) {
+#pragma unroll
+  for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float ov = __shfl_xor(v, stride);
+      const int oc = __shfl_xor(c, stride);
+      const bool lower = (lane & stride) == 0;
+      const bool desc = (lane & size) == 0;
+      const bool other_better = (ov > v) || (ov == v && oc < c);
+      if ((lower == desc) == other_better) {
+        v = ov;
+        c = oc;
+      }
+    }
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ xs,
+                                                             int M, const uint8_t* __restrict__ packed,
+                                                             const uint16_t* __restrict__ S,
+                                                             const uint16_t* __restrict__ ZS, int N, int K, int kc,
+                                                             int nblk, float* __restrict__ cand_score,
+                                                             int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+  constexpr int MR = 16 * MT;
+  extern __shared__ float smem[];
+  const int H = K >> 1, NS = H / kGroup, KG = K / kGroup;
+  float* xsT = smem;             // [KG][MR]: xs transposed, zero past row M
+  float* cbuf = smem + KG * MR;  // [MR][64]: the block's logits for the emit
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, h = lane >> 4;
+  const int b = blockIdx.x;
+  const int n = b * kBlockN + wave * 16 + col;
+  const bool nvalid = n < N;
+  const int nr = nvalid ? n : 0;
+
+  for (int i = tid; i < KG * MR; i += kC4Threads) {
+    const int g = i / MR, m = i - g * MR;
+    xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
+  }
+  __syncthreads();
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* prow = packed + (int64_t)nr * H + 32 * h;
+  const uint16_t* srow = S + (int64_t)nr * KG;
+  const uint16_t* zrow = ZS + (int64_t)nr * KG;
+  const uint16_t* xh = x + 32 * h;
+  for (int gb = 0; gb < NS; ++gb) {
+    const u32x4 p0 = ld16(prow + gb * kGroup);  // rows past N read row 0 and are never stored
+    const u32x4 p1 = ld16(prow + gb * kGroup + 16);
+    uint32_t dw[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dw[i] = pair_bytes4(p0[i]);
+      dw[4 + i] = pair_bytes4(p1[i]);
+    }
+    const uint16_t* xg = xh + gb * kGroup;
+    const int g0 = gb, g1 = KG / 2 + gb;
+    half4<MT, 0>(acc, dw, xg, M, K, col, bf16_lo(srow[g0]), bf16_lo(zrow[g0]), xsT + g0 * MR, h);
+    half4<MT, 1>(acc, dw, xg + H, M, K, col, bf16_lo(srow[g1]), bf16_lo(zrow[g1]), xsT + g1 * MR, h);
+  }
+
+  // acc[mt][r] is c[m = 16 mt + 4 h + r][n]
+  if (y != nullptr && nvalid) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mt * 16 + 4 * h + r;
+        if (m < M) y[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(acc[mt][r]);
+      }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      cbuf[(mt * 16 + 4 * h + r) * kBlockN + wave * 16 + col] = nvalid ? acc[mt][r] : -__builtin_inff();
+  __syncthreads();
+
+  const int64_t ld = (int64_t)nblk * kc;
+  for (int m = wave; m < M; m += kC4Threads / kWave) {
+    float v = cbuf[m * kBlockN + lane];
+    int c = lane;
+    wave_sort_vc(v, c, lane);
+    if (lane < kc) {
+      const int tok = b * kBlockN + c;
+      const bool ok = tok < N;
+      const int64_t at = (int64_t)m * ld + (int64_t)b * kc + lane;
+      cand_score[at] = ok ? v : -__builtin_inff();
+      cand_idx[at] = ok ? tok : -1;
+    }
+  }
+}
+
+template <int MT>
+void launch4(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S, const uint16_t* ZS,
+             int N, int K, int kc, int nblk, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+  const size_t lds = ((size_t)(K / kGroup) * 16 * MT + (size_t)16 * MT * kBlockN) * sizeof(float);
+  hipLaunchKernelGGL((coarse4_kernel<MT>), dim3((unsigned)nblk), dim3(kC4Threads), lds, s, x, xs, M, packed, S, ZS, N,
+                     K, kc, nblk, cs, ci, y);
+}
+
+}  // namespace
+}  // namespace i2h
+
+extern "C" int i2h_coarse4_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                                const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
+                                float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream) {
+  using namespace i2h;
+  if (!x || !xs || !packed || !S || !ZS || !cand_score || !cand_idx) return I2H_ERR_ARG;
+  if (M < 1 || N < 1 || N > ((int64_t)1 << 31) - 64 || K <= 0 || K % (2 * I2H_GROUP) != 0 || K > I2H_MAX_K)
+    return I2H_ERR_SHAPE;
+  if (kcand < 1 || kcand > I2H_MAX_KCAND) return I2H_ERR_LIMIT;
+  if (!aligned(x, 16) || !aligned(xs, 16) || !aligned(packed, 16) || !aligned(S, 2) || !aligned(ZS, 2) ||
+      !aligned(cand_score, 4) || !aligned(cand_idx, 4) || (y && !aligned(y, 2)))
+    return I2H_ERR_ALIGN;
+  const int64_t nblk = nblk_of(N);
+  const int64_t KG = K / I2H_GROUP, ld = nblk * kcand;
+  const hipStream_t s = (hipStream_t)stream;
+  // rows in chunks of at most 64 (one launch each)
+  for (int64_t m0 = 0; m0 < M; m0 += 64) {
+    const int mc = (int)(M - m0 < 64 ? M - m0 : 64);
+    const uint16_t* xm = x + m0 * K;
+    const float* xsm = xs + m0 * KG;
+    float* csm = cand_score + m0 * ld;
+    int32_t* cim = cand_idx + m0 * ld;
+    uint16_t* ym = y ? y + m0 * N : nullptr;
+    if (mc <= 16)
+      launch4<1>(xm, xsm, mc, packed, S, ZS, (int)N, (int)K, kcand, (int)nblk, csm, cim, ym, s);
+    else if (mc <= 32)
+      launch4<2>(xm, xsm, mc, packed, S, ZS, (int)N, (int)K, kcand, (int)nblk, csm, cim, ym, s);
+    else
+      launch4<4>(xm, xsm, mc, packed, S, ZS, (int)N, (int)K, kcand, (int)nblk, csm, cim, ym, s);
+    const int st = check_launch();
+    if (st != I2H_OK) return st;
+  }
+  return I2H_OK;
+}

@@ -231,6 +231,87 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The int4 head (radiance_drafthead.py, _quantize_head_now with BITS = 4): codes 0..15, byte j of
+// a packed row [K/2 bytes] holds k = j (bits 0-3) and K/2 + j (bits 4-7); S = bf16(16 sc),
+// ZS = bf16(16 sc + zp sc). Same exact arithmetic as pack_kernel (bf16 numerators, quot_rn).
+//
+// A unit is (row n, span gb): packed bytes 128 gb .. +127 of the row, i.e. group gb of the first
+// half and group KG/2 + gb of the second. One wave per unit; lane l = 32 t + i (half t) holds the
+// 4 weights k = t K/2 + 128 gb + 4 i .. +3; a half's min / max is a 32-lane reduction (DPP row
+// rotations, then the permlane16 swap); lanes i and 32 + i combine their nibbles with the
+// permlane32 swap and lanes 0..31 write 4 bytes each.
+// ---------------------------------------------------------------------------------------------
+template <int S>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + S, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float half_min(float v) {  // over the 32 lanes of a half-wave
+  v = fminf(v, row_ror<1>(v));
+  v = fminf(v, row_ror<2>(v));
+  v = fminf(v, row_ror<4>(v));
+  v = fminf(v, row_ror<8>(v));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fminf(v, __uint_as_float((threadIdx.x & 16) ? p[0] : p[1]));
+}
+__device__ __forceinline__ float half_max(float v) {
+  v = fmaxf(v, row_ror<1>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<8>(v));
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, __uint_as_float((threadIdx.x & 16) ? p[0] : p[1]));
+}
+__device__ __forceinline__ float clamp15(float v) { return fminf(fmaxf(v, 0.0f), 15.0f); }
+
+__global__ __launch_bounds__(kPackWaves * kWave) void pack4_kernel(const uint16_t* __restrict__ W, int64_t ldw, int N,
+                                                                    int K, uint8_t* __restrict__ packed,
+                                                                    uint16_t* __restrict__ S, uint16_t* __restrict__ ZS) {
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = lane >> 5, i = lane & 31;
+  const int H = K >> 1, NS = H / kGroup, KG = K / kGroup;
+  const int64_t units = (int64_t)N * NS;
+  const int64_t wstep = (int64_t)gridDim.x * kPackWaves;
+  for (int64_t u = (int64_t)blockIdx.x * kPackWaves + (threadIdx.x >> 6); u < units; u += wstep) {
+    const int64_t n = u / NS;
+    const int gb = (int)(u - n * NS);
+    const u32x2 v = *reinterpret_cast<const u32x2*>(W + n * ldw + t * H + gb * kGroup + 4 * i);
+    const float w[4] = {bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+    const float lo = half_min(fminf(fminf(w[0], w[1]), fminf(w[2], w[3])));
+    const float hi = half_max(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])));
+    const float sc = fmaxf(__fdiv_rn(__fadd_rn(hi, -lo), 15.0f), 1e-8f);
+    const bool wide = !(sc < 0x1p100f) || !(fmaxf(hi, -lo) < 0x1p100f);
+    const float y = __fdiv_rn(1.0f, sc);
+    float zp = clamp15(__builtin_rintf(quot_rn(-lo, sc, y)));
+    float q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = clamp15(__fadd_rn(quot_rn(w[e], sc, y), zp));
+    if (__builtin_amdgcn_ballot_w64(wide) != 0ull) {
+      if (wide) {
+        zp = clamp15(rintf(__fdiv_rn(-lo, sc)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] = clamp15(rintf(__fadd_rn(__fdiv_rn(w[e], sc), zp)));
+      }
+    }
+    // codes as bytes (v_cvt_pk_u8_f32: nearest, ties to even), the second half's shifted by 4
+    uint32_t b = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b = __builtin_amdgcn_cvt_pk_u8_f32(q[e], e, b);
+    b <<= 4 * t;
+    const auto pr = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    b |= (lane & 32) ? pr[0] : pr[1];
+    if (t == 0) *reinterpret_cast<uint32_t*>(packed + n * H + gb * kGroup + 4 * i) = b;
+    if (i == 0) {
+      const float s16 = __fmul_rn(16.0f, sc);
+      const float zs = __fadd_rn(s16, __fmul_rn(zp, sc));
+      const int64_t at = n * KG + t * (KG / 2) + gb;
+      S[at] = (uint16_t)bf16_bits_rne(s16);
+      ZS[at] = (uint16_t)bf16_bits_rne(zs);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace i2h
 
@@ -273,4 +354,19 @@ extern "C" int i2h_pack(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, ui
 extern "C" int i2h_pack_fp8(const uint8_t* W8, const float* wscale, int64_t ldw, int64_t N, int64_t K,
                             uint8_t* packed, uint16_t* S, uint16_t* ZS, void* stream) {
   return i2h::pack_launch<true>(W8, wscale, ldw, N, K, packed, S, ZS, (hipStream_t)stream);
+}
+
+extern "C" int i2h_pack4(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed, uint16_t* S,
+                         uint16_t* ZS, void* stream) {
+  using namespace i2h;
+  if (!W || !packed || !S || !ZS) return I2H_ERR_ARG;
+  if (N < 1 || K <= 0 || K % (2 * I2H_GROUP) != 0 || K > I2H_MAX_K || ldw < K) return I2H_ERR_SHAPE;
+  if (!aligned(W, 8) || ldw % 4 != 0 || !aligned(packed, 16) || !aligned(S, 2) || !aligned(ZS, 2))
+    return I2H_ERR_ALIGN;
+  if (N > (int64_t)1 << 31) return I2H_ERR_SHAPE;
+  const int64_t units = N * (K / 256);
+  const int64_t grid = (units + kPackWaves * 4 - 1) / (kPackWaves * 4);
+  hipLaunchKernelGGL(pack4_kernel, dim3((unsigned)(grid < 65536 ? grid : 65536)), dim3(kPackWaves * kWave), 0,
+                     (hipStream_t)stream, W, ldw, (int)N, (int)K, packed, S, ZS);
+  return check_launch();
 }

@@ -102,6 +102,7 @@ I2H_API int i2h_pack_fp8(const uint8_t* W8, const float* wscale, int64_t ldw, in
  * Per-group sums of x (radiance_drafthead.py, _apply_head_int2: the fp32 group sums the coarse
  * kernel uses for the zero point and the dequant bias).
  *   x   bf16 [M, K] (row stride K);  xs  fp32 [M, K/128]: xs[m, g] = sum of x[m, 128g .. 128g+127].
+ * K a multiple of 128 up to I2H_MAX_K.
  */
 I2H_API int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void* stream);
 
@@ -200,6 +201,30 @@ I2H_API int i2h_select_rerank_topk_fp8(const float* cand_score, const int32_t* c
                                        int kcand, int R, const uint16_t* x, const uint8_t* W8, const float* wscale,
                                        int64_t ldw, int64_t N, int64_t K, int k, int32_t* sel, float* exact,
                                        int32_t* out_idx, float* out_val, void* stream);
+
+/*
+ * The int4 head (radiance_drafthead.py, _quantize_head_now with BITS = 4, the page's comparison
+ * point, used with kcand = 1): codes 0..15 from the same asymmetric min/max quantiser per group of
+ * 128 k (sc = max((hi - lo)/15, 1e-8), zp = clamp(round(-lo/sc), 0, 15), q = clamp(round(w/sc +
+ * zp), 0, 15), IEEE fp32, bit-exact against eager fp32 ops);
+ *   packed4 u8 [N, K/2]: byte j holds q[j] (bits 0-3) and q[K/2 + j] (bits 4-7);
+ *   S, ZS   bf16 [N, K/128]: S = bf16(16 sc), ZS = bf16(16 sc + zp sc).
+ * W bf16 [N, K], row stride ldw (>= K, multiple of 4), 8-byte aligned; packed4 16-byte aligned.
+ * Limits: K a multiple of 256 up to I2H_MAX_K (the exact rerank after it needs a multiple of 512).
+ */
+I2H_API int i2h_pack4(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed4, uint16_t* S,
+                      uint16_t* ZS, void* stream);
+
+/*
+ * Coarse logits and block candidates of the int4 head (the fold of the page's bit-pattern
+ * dequant at bias 16): c[m, n] = sum over groups g of S[n,g] * sum_{k in g} x[m,k] (1 + v/16)
+ * - xs[m,g] ZS[n,g], accumulated in fp32; the block top-kcand, y and the layouts as in
+ * i2h_coarse_topk. xs from i2h_xsum is required. Limits: M >= 1, 1 <= kcand <= 64, K a
+ * multiple of 256. Not tuned for bandwidth (x is read from L2 per block).
+ */
+I2H_API int i2h_coarse4_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed4,
+                             const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
+                             float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream);
 
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);

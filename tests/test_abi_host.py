@@ -28,7 +28,7 @@ def test_header_declares_the_entry_points():
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
             "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
-            "i2h_select_rerank_topk_fp8"}
+            "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk"}
     assert names == want
 
 
@@ -206,3 +206,19 @@ def test_fp8_entry_points_reject_before_launch():
     assert f(P, P, 1, 1940, 8, 32, P, P, None, 5120, 124160, 5120, 1, None, None, P, P, None) == ARG
     assert f(P, P, 1, 1940, 8, 65, P, P, P, 5120, 124160, 5120, 1, None, None, P, P, None) == LIMIT
     assert f(P, P, 1, 1940, 8, 32, P, P + 4, P, 5120, 124160, 5120, 1, None, None, P, P, None) == ALIGN
+
+
+def test_int4_entry_points_reject_before_launch():
+    lib = i2h.lib()
+    # W, ldw, N, K, packed4, S, ZS, stream
+    assert lib.i2h_pack4(None, 5120, 100, 5120, P, P, P, None) == ARG
+    assert lib.i2h_pack4(P, 5120, 100, 5000, P, P, P, None) == SHAPE        # K % 256
+    assert lib.i2h_pack4(P, 5120, 100, 5376, P, P, P, None) == SHAPE        # ldw < K
+    assert lib.i2h_pack4(P + 4, 5120, 100, 5120, P, P, P, None) == ALIGN    # W not 8-byte aligned
+    # x, xs, M, packed4, S, ZS, N, K, kcand, cand_score, cand_idx, y, stream
+    f = lib.i2h_coarse4_topk
+    assert f(P, None, 1, P, P, P, 124160, 5120, 1, P, P, None, None) == ARG  # xs required
+    assert f(P, P, 1, P, P, P, 124160, 5000, 1, P, P, None, None) == SHAPE
+    assert f(P, P, 1, P, P, P, 124160, 5120, 0, P, P, None, None) == LIMIT
+    assert f(P, P, 1, P, P, P, 124160, 5120, 65, P, P, None, None) == LIMIT
+    assert f(P + 8, P, 1, P, P, P, 124160, 5120, 1, P, P, None, None) == ALIGN

@@ -514,3 +514,43 @@ def test_select_rerank_fused_fp8(i2h, M, N, kc, R, k):
     assert torch.equal(fsel, sel) and torch.equal(fex, ex), "fused FP8 selection / exact scores differ"
     assert torch.equal(fi, oi) and torch.equal(fv, ov), "fused FP8 top-k differs"
     _fp8_rerank_check(host(fex), si.bits(x), W8.numpy(), scale.numpy(), host(fsel))
+
+
+# ---------------------------------------------------------------------------------------------
+# int4 head (KCAND = 1, the page's comparison point): pack bit-exact; coarse and head as the
+# int2 head's parity rules
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,K", [(1000, 1024), (37, 5120), (5, 256)])
+def test_pack4_bit_exact(i2h, N, K):
+    say(f"pack4 N={N} K={K}")
+    W = si.bits(si.gen_weight(N, K, seed=300 + N))
+    W = np.concatenate([W, degenerate_rows(K)])
+    p, S, ZS = i2h.pack4(dev_bf16(W))
+    po, So, ZSo = oracle.pack4(W)
+    assert np.array_equal(host(p), po)
+    assert np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+
+
+def run_and_check4(i2h, xb, Wb, kc=1, R=32, k=1):
+    x, W = dev_bf16(xb), dev_bf16(Wb)
+    p, S, ZS = i2h.pack4(W)
+    po, So, ZSo = oracle.pack4(Wb)
+    assert np.array_equal(host(p), po) and np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+    xs = i2h.xsum(x)
+    cs, ci, y = i2h.coarse4_topk(x, xs, p, S, ZS, kcand=kc, want_y=True)
+    oi, ov, sel, ex = i2h.select_rerank_topk(cs, ci, kc, R, x, W, k, want_sel=True)
+    torch.cuda.synchronize()
+    g = dict(cs=cs, ci=ci, y=y, sel=sel, ex=ex, oi=oi, ov=ov)
+    res = oracle.head4(xb, Wb, po, So, ZSo, kcand=kc, R=R, k=k)
+    rows = np.arange(xb.shape[0])
+    return check_path(g, res, rows, xb, Wb, kc, k, "int4 head")
+
+
+@pytest.mark.parametrize("M,N,K,kc,R,k", [(1, 4096, 512, 1, 32, 1), (3, 4133, 5120, 1, 32, 1),
+                                          (20, 2000, 1024, 8, 32, 16), (40, 1000, 512, 4, 16, 4),
+                                          (1, 124160, 5120, 1, 32, 1)])
+def test_int4_head_parity(i2h, M, N, K, kc, R, k):
+    say(f"int4 head M={M} N={N} K={K} kc={kc} R={R} k={k}")
+    xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=M + K + 1))
+    Wb = si.bits(si.gen_weight(N, K, seed=N + K + 1))
+    run_and_check4(i2h, xb, Wb, kc=kc, R=R, k=k)
