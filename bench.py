@@ -22,6 +22,9 @@ fused tail with its selection and exact scores, and i2h_logits writing the exact
 (argmax caller, in place) or over a -inf row (top-k caller), per call and the write-back alone.
 `fp8_source` times the same weights as an FP8 e4m3 per-row-scale head: its load-time pack, and the
 fused tail reranking against the FP8 rows beside the bf16 one (back-to-back launches).
+`int4_head` times the int4 head on the same weights at KCAND = 1 (pack; xsum + int4 coarse +
+fused tail per call; the int4 coarse kernel alone, 6-copy rotation) and, with the CPU baseline,
+how often its argmax equals the dense bf16 argmax on the match rows (beside the int2 head's).
 """
 from __future__ import annotations
 
@@ -347,6 +350,61 @@ def main():
         torch.cuda.synchronize()
         return res
 
+    def measure_int4(h, steps, warmup):
+        """The int4 head (the page's comparison point) on the same weights at KCAND = 1: its pack,
+        and per call xsum + int4 coarse + the fused tail, with the coarse kernel alone timed back
+        to back on cold copies; argmax agreement with the int2 head's GPU call on the match rows."""
+        p4 = i2h.pack4(W)
+        pk4 = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            i2h.pack4(W, out=p4)
+            b.record()
+            torch.cuda.synchronize()
+            pk4.append(a.elapsed_time(b) * 1e3)
+        cps = [p4] + [(p4[0].clone(), p4[1].clone(), p4[2].clone()) for _ in range(5)]
+        nblk = (N + 63) // 64
+        x = h.x
+        xs = torch.empty(M, K // 128, dtype=torch.float32, device=x.device)
+        cs = torch.empty(M, nblk, dtype=torch.float32, device=x.device)
+        ci = torch.empty(M, nblk, dtype=torch.int32, device=x.device)
+        oi = torch.empty(M, 1, dtype=torch.int32, device=x.device)
+        ov = torch.empty(M, 1, dtype=torch.float32, device=x.device)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        L = h.lib
+        a_c = [(P(x), P(xs), M, P(p), P(S), P(Z), N, K, 1, P(cs), P(ci), None, h.stream) for (p, S, Z) in cps]
+        a_t = (P(cs), P(ci), M, nblk, 1, R, P(x), P(W), W.stride(0), N, K, 1, None, None, P(oi), P(ov), h.stream)
+
+        def call(i):
+            st = L.i2h_xsum(P(x), M, K, P(xs), h.stream)
+            st |= L.i2h_coarse4_topk(*a_c[i % len(a_c)])
+            st |= L.i2h_select_rerank_topk(*a_t)
+            if st:
+                raise RuntimeError(f"libi2h status {st}")
+
+        d, _ = time_steps(torch, call, steps, warmup)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            L.i2h_coarse4_topk(*a_c[i % len(a_c)])
+        ev1.record()
+        torch.cuda.synchronize()
+        c_us = ev0.elapsed_time(ev1) * 1e3 / steps
+        cbytes = N * K // 2 + 4 * N * (K // 128) + M * K * 2 + M * (K // 128) * 4 + M * nblk * 8
+        argmax4 = []
+        for r in range(args.match_rows):
+            xr = x_all[r:r + 1].contiguous()
+            c4s, c4i = i2h.coarse4_topk(xr, i2h.xsum(xr), *p4, kcand=1)
+            i4, _ = i2h.select_rerank_topk(c4s, c4i, 1, R, xr, W, 1)
+            argmax4.append(int(i4.item()))
+        del cps, p4
+        torch.cuda.synchronize()
+        return dict(kcand=1, us_per_call=round(d * 1e6, 2), coarse_us=round(c_us, 2), coarse_bytes=cbytes,
+                    coarse_gbps=round(cbytes / (c_us * 1e-6) / 1e9, 1),
+                    coarse_hbm_frac=round(cbytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    pack_us=round(float(np.median(pk4)), 1), argmax_rows=argmax4)
+
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
         res = {}
@@ -369,6 +427,8 @@ def main():
     traffic = traffic_for(M)
     log(f"[bench] FP8 weight source at M={M}: pack and fused tail")
     fp8 = measure_fp8(h, args.steps, args.warmup)
+    log(f"[bench] int4 head at M={M}, KCAND=1: pack, coarse and per call")
+    int4 = measure_int4(h, args.steps, args.warmup)
     log(f"[bench] timing the drop-in logits row at M={M}")
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
@@ -413,8 +473,11 @@ def main():
         match = sum(int(a == b) for a, b in zip(got, want))
         ex = oracle.exact_logits(xb, Wb)
         recall = sum(int(a == b) for a, b in zip(want, ex.argmax(1)))
+        dense = ex.argmax(1)
         result = dict(argmax_match_pct=round(100.0 * match / len(want), 2), argmax_rows=len(want),
                       recall_vs_dense_bf16_pct=round(100.0 * recall / len(want), 2))
+        int4["recall_vs_dense_bf16_pct"] = round(
+            100.0 * sum(int(a == b) for a, b in zip(int4["argmax_rows"], dense)) / len(want), 2)
         assert int(r1["idx"][0, 0]) == want[0]
         cpu = dict(value=round(hb["total"] / cpu_s / 1e9, 4), unit="GB/s", us_per_call=round(cpu_s * 1e6, 1),
                    cores=threads, kind="oracle",
@@ -449,6 +512,7 @@ def main():
                  "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},
         "dropin_logits": dropin,
         "fp8_source": fp8,
+        "int4_head": {k_: v_ for k_, v_ in int4.items() if k_ != "argmax_rows"},
         **result,
         "bands": bands,
         "cpu_baseline": cpu,

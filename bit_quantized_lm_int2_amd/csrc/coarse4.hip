@@ -9,8 +9,9 @@
 // first half and group KG/2 + gb of the second, each through 4 MFMAs (16x16x32 bf16) per m-tile.
 //
 // One 4-wave workgroup per 64-column block; lane (col = l & 15, h = l >> 4) streams bytes
-// 32 h .. 32 h + 31 of each span of its row, x comes from L2 (this path is not tuned for
-// bandwidth), and the emit ranks the block's columns with a wave bitonic sort (any kcand <= 64).
+// 32 h .. 32 h + 31 of each span of its row, kC4Pf spans ahead (with its x fragments when one
+// m-tile covers the rows; x comes from L2), and the emit ranks the block's columns with a wave
+// bitonic sort (any kcand <= 64).
 #include "dequant.h"
 #include "host_util.h"
 
@@ -18,6 +19,10 @@ namespace i2h {
 namespace {
 
 constexpr int kC4Threads = 256;
+#ifndef I2H_C4_PF
+#define I2H_C4_PF 1
+#endif
+constexpr int kC4Pf = I2H_C4_PF;  // spans of packed bytes (and x) in flight per lane
 
 // Bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3], so that one mask takes the nibbles of b0 and b1 (then b2
 // and b3) into the two bf16 halves of a dword.
@@ -42,9 +47,12 @@ __device__ __forceinline__ bf16x8 dequant4x8(uint32_t d0, uint32_t d1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// One half of one span: 4 MFMAs per m-tile, then the group's scale and zero. xa[s] (MT == 1) holds
+// the x fragment of slice s already loaded; otherwise x is read here.
 template <int MT, int HALF>
-__device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8], const uint16_t* xq, int M, int K,
-                                      int col, float sv, float zv, const float* xsg, int h) {
+__device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8], const u32x4* xa,
+                                      const uint16_t* xq, int M, int K, int col, float sv, float zv,
+                                      const float* xsg, int h) {
   f32x4 p[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) p[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -53,9 +61,13 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
     const bf16x8 b = dequant4x8<HALF>(dw[2 * s], dw[2 * s + 1]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = mt * 16 + col;
-      u32x4 a = {0u, 0u, 0u, 0u};
-      if (m < M) a = ld16(xq + (int64_t)m * K + 8 * s);
+      u32x4 a;
+      if constexpr (MT == 1) {
+        a = xa[s];
+      } else {
+        const int m = mt * 16 + col;
+        a = m < M ? ld16(xq + (int64_t)m * K + 8 * s) : u32x4{0u, 0u, 0u, 0u};
+      }
       p[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), b, p[mt], 0, 0, 0);
     }
   }
@@ -122,19 +134,58 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   const uint16_t* srow = S + (int64_t)nr * KG;
   const uint16_t* zrow = ZS + (int64_t)nr * KG;
   const uint16_t* xh = x + 32 * h;
-  for (int gb = 0; gb < NS; ++gb) {
-    const u32x4 p0 = ld16(prow + gb * kGroup);  // rows past N read row 0 and are never stored
-    const u32x4 p1 = ld16(prow + gb * kGroup + 16);
+  // a ring of kC4Pf spans in flight: the packed bytes and the two groups' S / ZS (rows past N
+  // read row 0, never stored) and, for one m-tile, the lane's x fragments of both halves (rows
+  // past M read row 0, unused)
+  constexpr int kXF = MT == 1 ? 8 : 1;
+  const int xrow = MT == 1 ? (col < M ? col : 0) : 0;
+  struct Slot {
+    u32x4 p0, p1;
+    u32x4 xa[kXF];
+    uint32_t s0, z0, s1, z1;  // the two groups' S and ZS bits
+  };
+  auto fetch = [&](Slot& sl, int gb) {
+    sl.p0 = ld16(prow + gb * kGroup);
+    sl.p1 = ld16(prow + gb * kGroup + 16);
+    sl.s0 = srow[gb];
+    sl.z0 = zrow[gb];
+    sl.s1 = srow[KG / 2 + gb];
+    sl.z1 = zrow[KG / 2 + gb];
+    if constexpr (MT == 1) {
+      const uint16_t* xq = xh + (int64_t)xrow * K + gb * kGroup;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sl.xa[s] = ld16(xq + 8 * s);
+        sl.xa[4 + s] = ld16(xq + H + 8 * s);
+      }
+    }
+  };
+  auto body = [&](const Slot& sl, int gb) {
     uint32_t dw[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      dw[i] = pair_bytes4(p0[i]);
-      dw[4 + i] = pair_bytes4(p1[i]);
+      dw[i] = pair_bytes4(sl.p0[i]);
+      dw[4 + i] = pair_bytes4(sl.p1[i]);
     }
     const uint16_t* xg = xh + gb * kGroup;
     const int g0 = gb, g1 = KG / 2 + gb;
-    half4<MT, 0>(acc, dw, xg, M, K, col, bf16_lo(srow[g0]), bf16_lo(zrow[g0]), xsT + g0 * MR, h);
-    half4<MT, 1>(acc, dw, xg + H, M, K, col, bf16_lo(srow[g1]), bf16_lo(zrow[g1]), xsT + g1 * MR, h);
+    half4<MT, 0>(acc, dw, sl.xa, xg, M, K, col, bf16_lo(sl.s0), bf16_lo(sl.z0), xsT + g0 * MR, h);
+    half4<MT, 1>(acc, dw, sl.xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(sl.s1), bf16_lo(sl.z1),
+                 xsT + g1 * MR, h);
+  };
+  Slot ring[kC4Pf];
+#pragma unroll
+  for (int q = 0; q < kC4Pf; ++q) fetch(ring[q], q < NS ? q : NS - 1);
+  for (int gb0 = 0; gb0 < NS; gb0 += kC4Pf) {
+#pragma unroll
+    for (int q = 0; q < kC4Pf; ++q) {
+      const int gb = gb0 + q;
+      if (gb < NS) {
+        body(ring[q], gb);
+        const int nx = gb + kC4Pf;
+        fetch(ring[q], nx < NS ? nx : NS - 1);
+      }
+    }
   }
 
   // acc[mt][r] is c[m = 16 mt + 4 h + r][n]
