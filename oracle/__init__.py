@@ -13,7 +13,9 @@ from .int2_head import (BLOCK_N, GROUP, bf16_to_f32, block_emit, check_shape, co
                         premultiplied_scales4, quantize4, quantize_fp8, rerank_exact_fp8, coarse_logits4,
                         dequantize4, unpack_half_split, check_shape4,
                         pack_quarter_split, premultiplied_scales, quantize, rerank_exact,
-                        select_top_r, storage_bytes, unpack_quarter_split)
+                        select_top_r, storage_bytes, unpack_quarter_split,
+                        pack_contiguous4, unpack_contiguous4, pack_variant, coarse_logits_contiguous4,
+                        dequantize_tile, coarse_logits_tile, select_tokens)
 
 __all__ = ["BLOCK_N", "GROUP", "bf16_to_f32", "block_emit", "check_shape", "coarse_logits",
            "dequantize", "exact_logits", "f32_to_bf16", "finalize", "fp8_e4m3_decode", "fp8_rows_f32",
@@ -21,4 +23,6 @@ __all__ = ["BLOCK_N", "GROUP", "bf16_to_f32", "block_emit", "check_shape", "coar
            "premultiplied_scales4", "quantize4", "quantize_fp8", "rerank_exact_fp8", "coarse_logits4",
            "dequantize4", "unpack_half_split", "check_shape4",
            "pack_quarter_split", "premultiplied_scales", "quantize", "rerank_exact",
-           "select_top_r", "storage_bytes", "unpack_quarter_split"]
+           "select_top_r", "storage_bytes", "unpack_quarter_split",
+           "pack_contiguous4", "unpack_contiguous4", "pack_variant", "coarse_logits_contiguous4",
+           "dequantize_tile", "coarse_logits_tile", "select_tokens"]

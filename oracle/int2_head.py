@@ -519,3 +519,95 @@ def head4(x_bits: np.ndarray, W_bits: np.ndarray, packed: np.ndarray, S_bits: np
     e = rerank_exact(x_bits, W_bits, sel)
     oi, ov = finalize(e, sel, k)
     return dict(coarse=c, cand_score=cs, cand_idx=ci, sel=sel, exact=e, idx=oi, val=ov)
+
+
+# ----------------------------------------------------------------------------------------------
+# f2: the variants the design is measured against
+# radiance_drafthead.py, module docstring (group 128 against 64; quarter-split against a
+# contiguous-4 byte layout; the scale applied to the accumulator against a dequantised weight
+# tile) and _emit (candidates from block maxima against a top-k over the whole coarse row).
+# Group 64 is quantize / pack / coarse_logits with G = 64; the rest follows.
+# ----------------------------------------------------------------------------------------------
+def pack_contiguous4(q: np.ndarray) -> np.ndarray:
+    """uint8 [N, K/4]: byte j = q[4j] | q[4j+1] << 2 | q[4j+2] << 4 | q[4j+3] << 6."""
+    q = q.astype(np.uint8)
+    return (q[:, 0::4] | (q[:, 1::4] << 2) | (q[:, 2::4] << 4) | (q[:, 3::4] << 6)).astype(np.uint8)
+
+
+def unpack_contiguous4(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_contiguous4: v uint8 [N, K] with v[n, 4j + t] = (byte j >> 2t) & 3."""
+    N, Q = packed.shape
+    v = np.empty((N, 4 * Q), dtype=np.uint8)
+    for t in range(4):
+        v[:, t::4] = (packed >> np.uint8(2 * t)) & np.uint8(3)
+    return v
+
+
+def pack_variant(W_bits: np.ndarray, G: int = GROUP, layout: str = "quarter"):
+    """(packed, S, ZS) of the same quantiser at group G in the quarter-split or contiguous-4 layout."""
+    check_shape(W_bits.shape[1], G)
+    q, sc, zp = quantize(W_bits, G)
+    S, ZS = premultiplied_scales(sc, zp)
+    packed = pack_quarter_split(q) if layout == "quarter" else pack_contiguous4(q)
+    return packed, S, ZS
+
+
+def coarse_logits_contiguous4(x_bits: np.ndarray, packed: np.ndarray, S_bits: np.ndarray,
+                              ZS_bits: np.ndarray, G: int = GROUP) -> np.ndarray:
+    """c fp64 [M, N] = x @ (S (1 + v/4) - ZS)^T with v read from the contiguous-4 layout."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    N = packed.shape[0]
+    c = np.empty((x.shape[0], N), dtype=np.float64)
+
+    def run(a: int, b: int) -> None:
+        v = unpack_contiguous4(packed[a:b]).astype(np.float64)
+        s = np.repeat(bf16_to_f32(S_bits[a:b]).astype(np.float64), G, axis=1)
+        zs = np.repeat(bf16_to_f32(ZS_bits[a:b]).astype(np.float64), G, axis=1)
+        c[:, a:b] = x @ (s * (1.0 + v / 4.0) - zs).T
+
+    _map_chunks(run, N)
+    return c
+
+
+def dequantize_tile(packed: np.ndarray, S_bits: np.ndarray, ZS_bits: np.ndarray,
+                    G: int = GROUP) -> np.ndarray:
+    """bf16 bits [N, K] of the dequantised weight tile: fl32(fl32(S (1 + v/4)) - ZS), then bf16.
+
+    The product is exact in fp32 (8-bit S times a 3-bit 1 + v/4); the difference rounds once in
+    fp32 and the tile is rounded to bf16 for the bf16 dot, so the scale reaches the weight and
+    not the accumulator."""
+    v = unpack_quarter_split(packed)
+    d = (np.float32(1.0) + v.astype(np.float32) / np.float32(4.0)).astype(np.float32)
+    s = np.repeat(bf16_to_f32(S_bits), G, axis=1).astype(np.float32)
+    zs = np.repeat(bf16_to_f32(ZS_bits), G, axis=1).astype(np.float32)
+    w = (s * d).astype(np.float32)
+    w = (w - zs).astype(np.float32)
+    return f32_to_bf16(w)
+
+
+def coarse_logits_tile(x_bits: np.ndarray, packed: np.ndarray, S_bits: np.ndarray,
+                       ZS_bits: np.ndarray, G: int = GROUP) -> np.ndarray:
+    """c fp64 [M, N] = x @ dequantize_tile(...)^T (no group sums of x)."""
+    x = bf16_to_f32(x_bits).astype(np.float64)
+    N = packed.shape[0]
+    c = np.empty((x.shape[0], N), dtype=np.float64)
+
+    def run(a: int, b: int) -> None:
+        w = bf16_to_f32(dequantize_tile(packed[a:b], S_bits[a:b], ZS_bits[a:b], G)).astype(np.float64)
+        c[:, a:b] = x @ w.T
+
+    _map_chunks(run, N)
+    return c
+
+
+def select_tokens(y_bits: np.ndarray, R: int) -> np.ndarray:
+    """sel int32 [M, R]: the R largest entries of each bf16 coarse row, best first (value
+    descending, index ascending on ties, -0.0 equal to +0.0); -1 past the row's end."""
+    y = bf16_to_f32(y_bits).astype(np.float64) + 0.0  # + 0.0 turns -0.0 into +0.0
+    M, N = y.shape
+    sel = np.full((M, R), -1, dtype=np.int32)
+    cols = np.arange(N)
+    for m in range(M):
+        o = np.lexsort((cols, -y[m]))[:R]
+        sel[m, :len(o)] = o
+    return sel

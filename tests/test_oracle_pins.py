@@ -629,3 +629,129 @@ def test_int4_shape_rule():
     for bad in (0, 128, 384, 5000):
         with pytest.raises(ValueError):
             oracle.check_shape4(bad)
+
+
+# ---------------------------------------------------------------------------------------------
+# The measured alternatives (radiance_drafthead.py, module docstring and _emit): token-level
+# selection, the contiguous-4 layout, the dequantised weight tile, group 64
+# ---------------------------------------------------------------------------------------------
+def brute_top_r(vals, R):
+    """Repeated pick of the best remaining entry in pure Python: the largest value, and of equal
+    values the lowest index (a strict > keeps the earlier one; -0.0 > 0.0 is false)."""
+    left = list(range(len(vals)))
+    out = []
+    while left and len(out) < R:
+        best = left[0]
+        for i in left[1:]:
+            if vals[i] > vals[best]:
+                best = i
+        out.append(best)
+        left.remove(best)
+    return out + [-1] * (R - len(out))
+
+
+def test_select_tokens_brute_force_with_ties():
+    rng = np.random.default_rng(17)
+    pool = np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x4000, 0x7F80, 0xFF80, 0x3F81, 0x0001, 0x8001],
+                    np.uint16)  # +-0, +-1, 2, +-inf, a neighbour of 1, +-the smallest subnormal
+    for N, R in [(1, 1), (5, 8), (37, 5), (200, 32), (64, 64)]:
+        y = pool[rng.integers(0, len(pool), size=(3, N))]
+        sel = oracle.select_tokens(y, R)
+        for m in range(3):
+            assert sel[m].tolist() == brute_top_r([bf(b) for b in y[m]], R)
+
+
+def test_select_tokens_all_equal_and_short_rows():
+    y = np.full((2, 100), 0x3F80, np.uint16)
+    assert oracle.select_tokens(y, 10).tolist() == [list(range(10))] * 2
+    y = np.array([[0x3F80, 0x4000, 0x3F80]], np.uint16)
+    assert oracle.select_tokens(y, 5).tolist() == [[1, 0, 2, -1, -1]]
+
+
+def test_select_tokens_equals_block_path_with_whole_blocks():
+    """With KCAND = BLOCK_N every column is a block candidate, so the block path's selection over
+    the same row must give the same tokens in the same order."""
+    z = np.random.default_rng(5).normal(size=(3, 1000)).astype(np.float32)
+    z[:, 100:140] = z[:, 60:100]  # repeated values across blocks
+    y = oracle.f32_to_bf16(z)
+    c = oracle.bf16_to_f32(y).astype(np.float64)
+    cs, ci = oracle.block_emit(c, 64)
+    for R in (1, 32, 300):
+        assert np.array_equal(oracle.select_top_r(cs, ci, R), oracle.select_tokens(y, R))
+
+
+def test_pack_contiguous4_worked_example():
+    """By hand: K = 8, q = [1 2 3 0 0 3 2 1]: byte j = q[4j] | q[4j+1] << 2 | q[4j+2] << 4 | q[4j+3] << 6."""
+    q = np.array([[1, 2, 3, 0, 0, 3, 2, 1]], np.uint8)
+    assert oracle.pack_contiguous4(q).tolist() == [[0x39, 0x6C]]
+    assert np.array_equal(oracle.unpack_contiguous4(oracle.pack_contiguous4(q)), q)
+
+
+def test_contiguous4_layout_changes_no_value():
+    q = np.random.default_rng(8).integers(0, 4, (9, 1024)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_contiguous4(oracle.pack_contiguous4(q)), q)
+    W = si.gen_weight(40, 1024, seed=21)
+    pq, S, ZS = oracle.pack_variant(si.bits(W), layout="quarter")
+    pc, S2, ZS2 = oracle.pack_variant(si.bits(W), layout="contiguous")
+    assert np.array_equal(S, S2) and np.array_equal(ZS, ZS2)
+    assert np.array_equal(oracle.unpack_contiguous4(pc), oracle.unpack_quarter_split(pq))
+    x = si.bits(si.gen_x(2, 1024, seed=4))
+    assert np.array_equal(oracle.coarse_logits_contiguous4(x, pc, S, ZS), oracle.coarse_logits(x, pq, S, ZS))
+
+
+def test_dequantize_tile_hand_rounding():
+    """By hand, S = bf16 1.0078125 (0x3F81), ZS = 0.5 (0x3F00), one group of K = 4 with codes
+    (3, 1, 0, 2) in a quarter-split byte (3 | 1 << 2 | 0 << 4 | 2 << 6 = 0x87):
+      v = 3: 1.0078125 * 1.75 - 0.5 = 1.263671875 -> 33.75/128 above 1 -> 34 -> 0x3FA2
+      v = 1: 1.0078125 * 1.25 - 0.5 = 0.759765625 = 0.5 (1 + 66.5/128) -> tie, even 66 -> 0x3F42
+      v = 0: 0.5078125 = 0.5 (1 + 2/128) exact -> 0x3F02
+      v = 2: 1.51171875 - 0.5 = 1.01171875 = 1 + 1.5/128 -> tie, even 2 -> 0x3F82"""
+    t = oracle.dequantize_tile(np.array([[0x87]], np.uint8), np.array([[0x3F81]], np.uint16),
+                               np.array([[0x3F00]], np.uint16), G=4)
+    assert [hex(v) for v in t[0]] == ["0x3fa2", "0x3f42", "0x3f02", "0x3f82"]
+
+
+def grid_head_g(N, K, G, seed):
+    """grid_head at any group size G."""
+    rng = np.random.default_rng(seed)
+    ng = K // G
+    q = rng.integers(0, 4, size=(N, K)).astype(np.int64)
+    qg = q.reshape(N, ng, G)
+    qg[:, :, 0] = 0
+    qg[:, :, 1] = 3
+    zp = rng.integers(0, 4, size=(N, ng))
+    sc = np.ldexp(1.0, rng.integers(-12, -3, size=(N, ng)))
+    w = (sc[:, :, None] * (qg - zp[:, :, None])).reshape(N, K)
+    Wb = oracle.f32_to_bf16(w.astype(np.float32))
+    assert np.array_equal(oracle.bf16_to_f32(Wb).astype(np.float64), w)
+    return Wb, q.reshape(N, K), zp, sc
+
+
+def test_dequantize_tile_on_exact_grid_is_the_weight():
+    """On the exact int2 grid S (1 + v/4) - ZS = sc (v - zp) is a bf16 value, so the rounded tile is
+    the weight itself and the tile-scaled logits equal the accumulator-scaled ones."""
+    Wb, q, zp, sc = grid_head_g(60, 1024, 128, 12)
+    packed, S, ZS = oracle.pack(Wb)
+    assert np.array_equal(oracle.dequantize_tile(packed, S, ZS), Wb)
+    x = si.bits(si.gen_x(2, 1024, seed=6))
+    assert np.array_equal(oracle.coarse_logits_tile(x, packed, S, ZS), oracle.coarse_logits(x, packed, S, ZS))
+
+
+def test_group64_exact_grid_head():
+    N, K, G = 80, 1024, 64
+    Wb, q, zp, sc = grid_head_g(N, K, G, 14)
+    qo, sco, zpo = oracle.quantize(Wb, G)
+    assert np.array_equal(qo, q) and np.array_equal(zpo, zp) and np.array_equal(sco, sc)
+    packed, S, ZS = oracle.pack_variant(Wb, G=G)
+    assert S.shape == (N, K // G)
+    assert np.array_equal(oracle.bf16_to_f32(ZS).astype(np.float64), (4 + zp) * sc)
+    x = si.bits(si.gen_x(2, K, seed=10))
+    c = oracle.coarse_logits(x, packed, S, ZS, G)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    wf = oracle.bf16_to_f32(Wb).astype(np.float64)
+    for m in range(2):
+        for n in range(0, N, 7):
+            want = math.fsum(xf[m] * wf[n])
+            assert abs(c[m, n] - want) <= K * 2.0 ** -52 * np.sum(np.abs(xf[m] * wf[n]))
+    with pytest.raises(ValueError):
+        oracle.pack_variant(Wb[:, :128], G=G)  # K = 128 is not four quarters of whole groups
