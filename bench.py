@@ -25,6 +25,9 @@ fused tail reranking against the FP8 rows beside the bf16 one (back-to-back laun
 `int4_head` times the int4 head on the same weights at KCAND = 1 (pack; xsum + int4 coarse +
 fused tail per call; the int4 coarse kernel alone, 6-copy rotation) and, with the CPU baseline,
 how often its argmax equals the dense bf16 argmax on the match rows (beside the int2 head's).
+`ablations.selection` sets the block candidates against a token-level top-R over the whole bf16
+coarse row (i2h_select_tokens, then the exact rerank and argmax): per call, the tail alone and the
+selection alone, with the token-level path's argmax agreement with the dense bf16 argmax.
 """
 from __future__ import annotations
 
@@ -135,6 +138,9 @@ class Head:
                            for (p, S, Z) in copies]
         self.a_srr_sel = (P(self.cs), P(self.ci), M, nblk, KC, R, P(x), P(W), W.stride(0), N, K, 1, P(self.sel),
                           P(self.ex), P(self.oi), P(self.ov), s)
+        # token-level selection over the coarse row (the alternative to block candidates)
+        self.a_seltok = (P(self.y), M, N, R, P(self.sel), s)
+        self.a_rr_sel = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, 1, None, P(self.oi), P(self.ov), s)
         self.a_logits = {topk: (None if topk else P(self.y), M, N, P(self.sel), P(self.ex), R, int(topk), None, 0,
                                 P(self.y), 1, s) for topk in (False, True)}
 
@@ -173,6 +179,17 @@ class Head:
         if st:
             raise RuntimeError(f"libi2h status {st}")
 
+    def token_level(self, i):
+        """One call with token-level selection: coarse with its bf16 row, the top-R of the row,
+        then the exact rerank and argmax of those R tokens."""
+        L = self.lib
+        st = 0 if self.own_sums else L.i2h_xsum(*self.a_xsum)
+        st |= L.i2h_coarse_topk(*self.a_coarse_y[i % len(self.a_coarse_y)])
+        st |= L.i2h_select_tokens(*self.a_seltok)
+        st |= L.i2h_rerank_topk(*self.a_rr_sel)
+        if st:
+            raise RuntimeError(f"libi2h status {st}")
+
     def logits_only(self, torch, n, topk=False):
         """Mean time of n back-to-back i2h_logits calls (row pass + write-back) by HIP events."""
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -188,6 +205,22 @@ class Head:
         st = self.lib.i2h_head(*self.a_head[i % len(self.a_head)])
         if st:
             raise RuntimeError(f"libi2h status {st}")
+
+
+def back_to_back_us(torch, fn, steps, warmup):
+    """Mean µs of `steps` back-to-back calls of fn() (each enqueues launches and returns a
+    libi2h status), by HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        if fn():
+            raise RuntimeError("libi2h launch failed")
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / steps
 
 
 def time_steps(torch, fn, steps, warmup, events=False):
@@ -328,17 +361,7 @@ def main():
                  None, P(h.oi), P(h.ov), h.stream)
 
         def tail_us(fn, args_):
-            for _ in range(warmup):
-                fn(*args_)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for _ in range(steps):
-                if fn(*args_):
-                    raise RuntimeError("libi2h tail launch failed")
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) * 1e3 / steps
+            return back_to_back_us(torch, lambda: fn(*args_), steps, warmup)
 
         L = h.lib
         res = dict(pack_us=round(float(np.median(pk8)), 1),
@@ -405,6 +428,28 @@ def main():
                     coarse_hbm_frac=round(cbytes / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     pack_us=round(float(np.median(pk4)), 1), argmax_rows=argmax4)
 
+    def measure_selection(h, steps, warmup):
+        """Block candidates (the design) against a token-level top-R over the whole coarse row:
+        per call, and the tail alone (selection + exact rerank + argmax) on one call's outputs."""
+        L = h.lib
+        d_tok, _ = time_steps(torch, h.token_level, steps, warmup)
+        h.token_level(0)
+        tail_tok = back_to_back_us(torch, lambda: L.i2h_select_tokens(*h.a_seltok) | L.i2h_rerank_topk(*h.a_rr_sel),
+                                   steps, warmup)
+        sel_tok = back_to_back_us(torch, lambda: L.i2h_select_tokens(*h.a_seltok), steps, warmup)
+        h.step(0)
+        tail_blk = back_to_back_us(torch, lambda: L.i2h_select_rerank_topk(*h.a_srr), steps, warmup)
+        rows = []
+        for r in range(args.match_rows):
+            xr = x_all[r:r + 1].contiguous()
+            _, _, yr = i2h.coarse_topk(xr, None if i2h.coarse_sums_x(1, K) else i2h.xsum(xr), packed, S, ZS,
+                                       kcand=KC, want_y=True)
+            ir, _ = i2h.rerank_topk(xr, W, i2h.select_tokens(yr, R), 1)
+            rows.append(int(ir.item()))
+        torch.cuda.synchronize()
+        return dict(token_level_us_per_call=round(d_tok * 1e6, 2), token_level_tail_us=round(tail_tok, 2),
+                    select_tokens_us=round(sel_tok, 2), block_tail_us=round(tail_blk, 2), argmax_rows=rows)
+
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
         res = {}
@@ -429,6 +474,9 @@ def main():
     fp8 = measure_fp8(h, args.steps, args.warmup)
     log(f"[bench] int4 head at M={M}, KCAND=1: pack, coarse and per call")
     int4 = measure_int4(h, args.steps, args.warmup)
+    log(f"[bench] selection: block candidates against token-level top-{R} at M={M}")
+    selab = measure_selection(h, args.steps, args.warmup)
+    selab["block_us_per_call"] = round(us, 2)
     log(f"[bench] timing the drop-in logits row at M={M}")
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
@@ -476,6 +524,8 @@ def main():
         dense = ex.argmax(1)
         result = dict(argmax_match_pct=round(100.0 * match / len(want), 2), argmax_rows=len(want),
                       recall_vs_dense_bf16_pct=round(100.0 * recall / len(want), 2))
+        selab["token_level_recall_vs_dense_bf16_pct"] = round(
+            100.0 * sum(int(a == b) for a, b in zip(selab["argmax_rows"], dense)) / len(want), 2)
         int4["recall_vs_dense_bf16_pct"] = round(
             100.0 * sum(int(a == b) for a, b in zip(int4["argmax_rows"], dense)) / len(want), 2)
         assert int(r1["idx"][0, 0]) == want[0]
@@ -513,6 +563,7 @@ def main():
         "dropin_logits": dropin,
         "fp8_source": fp8,
         "int4_head": {k_: v_ for k_, v_ in int4.items() if k_ != "argmax_rows"},
+        "ablations": {"selection": {k_: v_ for k_, v_ in selab.items() if k_ != "argmax_rows"}},
         **result,
         "bands": bands,
         "cpu_baseline": cpu,

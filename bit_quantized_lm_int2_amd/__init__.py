@@ -18,7 +18,7 @@ import torch
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
            "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8", "pack4", "coarse4_topk",
-           "GROUP",
+           "select_tokens", "GROUP",
            "BLOCK_N"]
 
 GROUP = 128
@@ -52,6 +52,7 @@ _SIGNATURES = {
     "i2h_pack_fp8": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_pack4": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_coarse4_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P], _INT),
+    "i2h_select_tokens": ([_P, _I64, _I64, _INT, _P, _P], _INT),
     "i2h_rerank_fp8": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P, _INT, _P, _P], _INT),
     "i2h_select_rerank_topk_fp8": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P,
                                     _P, _P], _INT),
@@ -499,3 +500,14 @@ def coarse4_topk(x, xs, packed4, S, ZS, kcand: int = 1, want_y: bool = False):
     _check("i2h_coarse4_topk", lib().i2h_coarse4_topk(_ptr(x), _ptr(xs), M, _ptr(packed4), _ptr(S), _ptr(ZS), N, K,
                                                       kcand, _ptr(cs), _ptr(ci), _ptr(y), _stream(x)))
     return (cs, ci, y) if want_y else (cs, ci)
+
+
+def select_tokens(y, R: int):
+    """sel int32 [M, R]: the R largest entries of each bf16 row of y (value descending, lower
+    index first on ties), -1 past a row's end."""
+    _need(y, "y", torch.bfloat16, 2)
+    _dense(y, "y")
+    M, N = y.shape
+    sel = torch.empty(M, R, dtype=torch.int32, device=y.device)
+    _check("i2h_select_tokens", lib().i2h_select_tokens(_ptr(y), M, N, R, _ptr(sel), _stream(y)))
+    return sel

@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libi2h.so")
 ARCH = os.environ.get("I2H_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pack.hip", "coarse.hip", "coarse_tile.hip", "select.hip", "select_rerank.hip", "rerank.hip", "head.hip",
-           "logits.hip", "coarse4.hip"]
+           "logits.hip", "coarse4.hip", "select_tokens.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -226,6 +226,16 @@ I2H_API int i2h_coarse4_topk(const uint16_t* x, const float* xs, int64_t M, cons
                              const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
                              float* cand_score, int32_t* cand_idx, uint16_t* y, void* stream);
 
+/*
+ * Token-level selection over the coarse row (the alternative to block candidates that the page
+ * measures; radiance_drafthead.py, _emit docstring and the module docstring's note on
+ * selection): sel [M, R] int32 = for each row of y [M, N] bf16 (row-major, row stride N), the
+ * indices of its R largest entries, value descending, lower index first on ties, -0.0 equal to
+ * +0.0; -1 in slots past N. Feed sel to i2h_rerank or i2h_rerank_topk. y finite. Limits:
+ * 1 <= M, N <= 2^31 - 1, 1 <= R <= I2H_MAX_R; y 2-byte and sel 4-byte aligned.
+ */
+I2H_API int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* stream);
+
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);
 

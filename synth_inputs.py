@@ -122,6 +122,15 @@ def gen_rows(M: int, R: int, N: int, seed: int = 12) -> torch.Tensor:
     return torch.stack([torch.randperm(N, generator=g)[:R] for _ in range(M)]).to(torch.int32)
 
 
+def gen_coarse_row(M: int, N: int, seed: int = 13, levels: int = 0) -> torch.Tensor:
+    """bf16 [M, N] rows shaped like coarse logits (3 z, z ~ N(0, 1)); with levels > 0 the values
+    are rounded to multiples of 1/levels first, so many entries tie (and both signed zeros occur)."""
+    z = 3.0 * torch.randn(M, N, generator=_gen(seed), dtype=torch.float32)
+    if levels > 0:
+        z = torch.round(z * levels) / levels
+    return z.to(torch.bfloat16)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw uint16 bit patterns of a bf16 tensor (CPU copy), for the numpy side."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)

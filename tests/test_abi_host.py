@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
             "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
-            "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk"}
+            "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk",
+            "i2h_select_tokens"}
     assert names == want
 
 
@@ -222,3 +223,17 @@ def test_int4_entry_points_reject_before_launch():
     assert f(P, P, 1, P, P, P, 124160, 5120, 0, P, P, None, None) == LIMIT
     assert f(P, P, 1, P, P, P, 124160, 5120, 65, P, P, None, None) == LIMIT
     assert f(P + 8, P, 1, P, P, P, 124160, 5120, 1, P, P, None, None) == ALIGN
+
+
+def test_select_tokens_rejects_before_launch():
+    f = i2h.lib().i2h_select_tokens
+    # y, M, N, R, sel, stream
+    assert f(None, 1, 100, 32, P, None) == ARG
+    assert f(P, 1, 100, 32, None, None) == ARG
+    assert f(P, 0, 100, 32, P, None) == SHAPE
+    assert f(P, 1, 0, 32, P, None) == SHAPE
+    assert f(P, 1, 1 << 31, 32, P, None) == SHAPE
+    assert f(P, 1, 100, 0, P, None) == LIMIT
+    assert f(P, 1, 100, 1025, P, None) == LIMIT
+    assert f(P + 1, 1, 100, 32, P, None) == ALIGN
+    assert f(P, 1, 100, 32, P + 2, None) == ALIGN

@@ -554,3 +554,28 @@ def test_int4_head_parity(i2h, M, N, K, kc, R, k):
     xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=M + K + 1))
     Wb = si.bits(si.gen_weight(N, K, seed=N + K + 1))
     run_and_check4(i2h, xb, Wb, kc=kc, R=R, k=k)
+
+
+# ---------------------------------------------------------------------------------------------
+# token-level selection over the coarse row: bit-exact indices
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,R,levels", [(3, 1000, 32, 0), (2, 37, 64, 0), (4, 4099, 32, 2), (2, 8191, 100, 1),
+                                          (1, 124160, 32, 0), (2, 248320, 1024, 0), (2, 124160, 16, 3),
+                                          (3, 9000, 1024, 1)])
+def test_select_tokens_exact(i2h, M, N, R, levels):
+    say(f"select_tokens M={M} N={N} R={R} levels={levels}")
+    y = si.gen_coarse_row(M, N, seed=300 + N, levels=levels)
+    sel = i2h.select_tokens(y.to(DEV), R)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sel), oracle.select_tokens(si.bits(y), R))
+
+
+def test_select_tokens_all_ties_and_signed_zeros(i2h):
+    say("select_tokens ties")
+    y = np.zeros((3, 20000), np.uint16)
+    y[1, ::2] = 0x8000                       # -0.0 and +0.0 interleaved: all equal
+    y[2] = 0x3F80
+    y[2, 19990:] = 0x4000                    # ten larger entries at the end, then ties
+    sel = i2h.select_tokens(dev_bf16(y), 40)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sel), oracle.select_tokens(y, 40))
