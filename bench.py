@@ -28,6 +28,9 @@ how often its argmax equals the dense bf16 argmax on the match rows (beside the 
 `ablations.selection` sets the block candidates against a token-level top-R over the whole bf16
 coarse row (i2h_select_tokens, then the exact rerank and argmax): per call, the tail alone and the
 selection alone, with the token-level path's argmax agreement with the dense bf16 argmax.
+`ablations.coarse_variants` times one coarse kernel family in four forms that differ in one
+property each (the design: group 128, quarter-split, scale on the accumulator; group 64;
+contiguous-4 bytes; dequantised weight tile) at M = 1 and 16 on cold copies, with each pack.
 """
 from __future__ import annotations
 
@@ -450,6 +453,52 @@ def main():
         return dict(token_level_us_per_call=round(d_tok * 1e6, 2), token_level_tail_us=round(tail_tok, 2),
                     select_tokens_us=round(sel_tok, 2), block_tail_us=round(tail_blk, 2), argmax_rows=rows)
 
+    def measure_variants(steps, warmup):
+        """The design alternatives at the workload shape (one property changed each): each variant's
+        load-time pack, and its coarse kernel alone at M = 1 and 16, back to back over cold copies,
+        with the production coarse kernel's time beside them."""
+        combos = (("design", 128, "quarter", "accumulator"), ("group64", 64, "quarter", "accumulator"),
+                  ("contiguous4", 128, "contiguous", "accumulator"), ("weight_tile", 128, "quarter", "tile"))
+        Pp = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        L = i2h.lib()
+        nblk = (N + 63) // 64
+        res = {}
+        for name, g, lay, sc in combos:
+            pk = i2h.pack_variant(W, g, lay)
+            torch.cuda.synchronize()
+            t = []
+            for _ in range(3):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                i2h.pack_variant(W, g, lay)
+                b.record()
+                torch.cuda.synchronize()
+                t.append(a.elapsed_time(b) * 1e3)
+            cps = [pk] + [tuple(u.clone() for u in pk) for _ in range(COPIES - 1)]
+            r = dict(group=g, layout=lay, scaling=sc, pack_us=round(float(np.median(t)), 1),
+                     weight_bytes=N * K // 4 + 2 * N * (K // g) * 2)
+            for Mv in (1, 16):
+                xv = x_all[:Mv].contiguous()
+                xs = i2h.xsum_group(xv, g) if sc == "accumulator" else None
+                cs = torch.empty(Mv, nblk * KC, dtype=torch.float32, device=dev)
+                ci = torch.empty(Mv, nblk * KC, dtype=torch.int32, device=dev)
+                lay_c, sc_c = (0 if lay == "quarter" else 1), (0 if sc == "accumulator" else 1)
+                args_ = [(Pp(xv), Pp(xs), Mv, Pp(p), Pp(S_), Pp(Z_), N, K, g, lay_c, sc_c, KC, Pp(cs), Pp(ci), stream)
+                         for (p, S_, Z_) in cps]
+                it = iter(range(1 << 30))
+                us = back_to_back_us(torch, lambda: L.i2h_coarse_variant_topk(*args_[next(it) % len(args_)]),
+                                     steps, warmup)
+                r[f"M{Mv}_coarse_us"] = round(us, 2)
+                r[f"M{Mv}_hbm_frac"] = round((r["weight_bytes"] + Mv * K * 2) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            res[name] = r
+            del cps, pk
+            torch.cuda.synchronize()
+        for name in res:
+            for Mv in (1, 16):
+                res[name][f"M{Mv}_vs_design"] = round(res[name][f"M{Mv}_coarse_us"] / res["design"][f"M{Mv}_coarse_us"], 3)
+        return res
+
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
         res = {}
@@ -477,6 +526,8 @@ def main():
     log(f"[bench] selection: block candidates against token-level top-{R} at M={M}")
     selab = measure_selection(h, args.steps, args.warmup)
     selab["block_us_per_call"] = round(us, 2)
+    log("[bench] design alternatives: group 64, contiguous-4 bytes, dequantised weight tile")
+    variants = measure_variants(args.steps, args.warmup)
     log(f"[bench] timing the drop-in logits row at M={M}")
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
@@ -563,7 +614,8 @@ def main():
         "dropin_logits": dropin,
         "fp8_source": fp8,
         "int4_head": {k_: v_ for k_, v_ in int4.items() if k_ != "argmax_rows"},
-        "ablations": {"selection": {k_: v_ for k_, v_ in selab.items() if k_ != "argmax_rows"}},
+        "ablations": {"selection": {k_: v_ for k_, v_ in selab.items() if k_ != "argmax_rows"},
+                      "coarse_variants": variants},
         **result,
         "bands": bands,
         "cpu_baseline": cpu,

@@ -18,7 +18,7 @@ import torch
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
            "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8", "pack4", "coarse4_topk",
-           "select_tokens", "GROUP",
+           "select_tokens", "pack_variant", "xsum_group", "coarse_variant_topk", "GROUP",
            "BLOCK_N"]
 
 GROUP = 128
@@ -53,6 +53,9 @@ _SIGNATURES = {
     "i2h_pack4": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_coarse4_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P], _INT),
     "i2h_select_tokens": ([_P, _I64, _I64, _INT, _P, _P], _INT),
+    "i2h_pack_variant": ([_P, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P], _INT),
+    "i2h_xsum_group": ([_P, _I64, _I64, _INT, _P, _P], _INT),
+    "i2h_coarse_variant_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _INT, _INT, _INT, _P, _P, _P], _INT),
     "i2h_rerank_fp8": ([_P, _I64, _P, _I64, _I64, _I64, _P, _P, _INT, _P, _P], _INT),
     "i2h_select_rerank_topk_fp8": ([_P, _P, _I64, _I64, _INT, _INT, _P, _P, _P, _I64, _I64, _I64, _INT, _P, _P, _P,
                                     _P, _P], _INT),
@@ -511,3 +514,57 @@ def select_tokens(y, R: int):
     sel = torch.empty(M, R, dtype=torch.int32, device=y.device)
     _check("i2h_select_tokens", lib().i2h_select_tokens(_ptr(y), M, N, R, _ptr(sel), _stream(y)))
     return sel
+
+
+_LAYOUTS = {"quarter": 0, "contiguous": 1}
+_SCALINGS = {"accumulator": 0, "tile": 1}
+
+
+def pack_variant(W, group: int = GROUP, layout: str = "quarter"):
+    """(packed uint8 [N, K/4], S bf16 [N, K/group], ZS bf16 [N, K/group]) at group 64 or 128 in
+    the quarter-split or contiguous-4 layout."""
+    _need(W, "W", torch.bfloat16, 2)
+    N, K = W.shape
+    ldw = _rows(W, "W")
+    packed = torch.empty(N, K // 4, dtype=torch.uint8, device=W.device)
+    S = torch.empty(N, K // group, dtype=torch.bfloat16, device=W.device)
+    ZS = torch.empty(N, K // group, dtype=torch.bfloat16, device=W.device)
+    _check("i2h_pack_variant", lib().i2h_pack_variant(_ptr(W), ldw, N, K, group, _LAYOUTS[layout], _ptr(packed),
+                                                      _ptr(S), _ptr(ZS), _stream(W)))
+    return packed, S, ZS
+
+
+def xsum_group(x, group: int = GROUP):
+    """xs fp32 [M, K/group]: the sums of x over each group of `group` k."""
+    _need(x, "x", torch.bfloat16, 2)
+    _dense(x, "x")
+    M, K = x.shape
+    xs = torch.empty(M, K // group, dtype=torch.float32, device=x.device)
+    _check("i2h_xsum_group", lib().i2h_xsum_group(_ptr(x), M, K, group, _ptr(xs), _stream(x)))
+    return xs
+
+
+def coarse_variant_topk(x, xs, packed, S, ZS, group: int = GROUP, layout: str = "quarter",
+                        scaling: str = "accumulator", kcand: int = 8):
+    """(cand_score fp32 [M, NBLK*kcand], cand_idx int32 [M, NBLK*kcand]) of a variant head."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 2)
+    for t, nm in ((x, "x"), (packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    M, K = x.shape
+    N = packed.shape[0]
+    _shape(packed, "packed", (N, K // 4))
+    _shape(S, "S", (N, K // group))
+    _shape(ZS, "ZS", (N, K // group))
+    if xs is not None:
+        _need(xs, "xs", torch.float32, 2)
+        _dense(xs, "xs")
+        _shape(xs, "xs", (M, K // group))
+    nblk = (N + BLOCK_N - 1) // BLOCK_N
+    cs = torch.empty(M, nblk * kcand, dtype=torch.float32, device=x.device)
+    ci = torch.empty(M, nblk * kcand, dtype=torch.int32, device=x.device)
+    _check("i2h_coarse_variant_topk",
+           lib().i2h_coarse_variant_topk(_ptr(x), _ptr(xs), M, _ptr(packed), _ptr(S), _ptr(ZS), N, K, group,
+                                         _LAYOUTS[layout], _SCALINGS[scaling], kcand, _ptr(cs), _ptr(ci),
+                                         _stream(x)))
+    return cs, ci

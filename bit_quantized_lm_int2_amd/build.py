@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libi2h.so")
 ARCH = os.environ.get("I2H_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["pack.hip", "coarse.hip", "coarse_tile.hip", "select.hip", "select_rerank.hip", "rerank.hip", "head.hip",
-           "logits.hip", "coarse4.hip", "select_tokens.hip"]
+           "logits.hip", "coarse4.hip", "select_tokens.hip", "variant.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -33,7 +33,8 @@ COMMON = [
 ]
 # The packer must be bit-exact against an eager fp32 evaluation: no contraction into FMA and
 # correctly rounded division. Its inputs are finite, so min / max need no NaN quieting.
-EXTRA = {"pack.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-honor-nans"]}
+EXTRA = {"pack.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-honor-nans"],
+         "variant.hip": ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-honor-nans"]}
 
 
 def _hipcc() -> str:

@@ -14,6 +14,7 @@
 // bitonic sort (any kcand <= 64).
 #include "dequant.h"
 #include "host_util.h"
+#include "wave_sort.h"
 
 namespace i2h {
 namespace {
@@ -78,26 +79,6 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
     for (int r = 0; r < 4; ++r) {
       const float a = fmaf(sv, p[mt][r], acc[mt][r]);
       acc[mt][r] = fmaf(-xv[r], zv, a);
-    }
-  }
-}
-
-// Descending bitonic sort across the wave of (value, column); better = larger value, then lower
-// column. Afterwards lane r holds the r-th best.
-__device__ __forceinline__ void wave_sort_vc(float& v, int& c, int lane) {
-#pragma unroll
-  for (int size = 2; size <= kWave; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float ov = __shfl_xor(v, stride);
-      const int oc = __shfl_xor(c, stride);
-      const bool lower = (lane & stride) == 0;
-      const bool desc = (lane & size) == 0;
-      const bool other_better = (ov > v) || (ov == v && oc < c);
-      if ((lower == desc) == other_better) {
-        v = ov;
-        c = oc;
-      }
     }
   }
 }

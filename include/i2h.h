@@ -236,6 +236,39 @@ I2H_API int i2h_coarse4_topk(const uint16_t* x, const float* xs, int64_t M, cons
  */
 I2H_API int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* stream);
 
+/*
+ * The design alternatives the head is measured against (radiance_drafthead.py, module
+ * docstring: group 128 against 64, quarter-split against contiguous-4 bytes, the scale applied to
+ * the accumulator against a dequantised weight tile). Measurement variants, not the per-call path.
+ */
+#define I2H_LAYOUT_QUARTER 0 /* byte j of a row holds k = j, K/4 + j, K/2 + j, 3K/4 + j */
+#define I2H_LAYOUT_CONTIG 1  /* byte j of a row holds k = 4j .. 4j + 3 (bits 0-1 .. 6-7) */
+#define I2H_SCALE_ACC 0      /* per group S * sum x (1 + v/4) - xs * ZS on the fp32 accumulator */
+#define I2H_SCALE_TILE 1     /* each weight bf16(fl32(S (1 + v/4)) - ZS), then the bf16 dot */
+
+/*
+ * i2h_pack at group `group` (64 or 128) in layout I2H_LAYOUT_*: the same quantiser and
+ * premultiplied scales; packed [N, K/4], S and ZS [N, K/group]. Bit-exact. Limits: K a multiple
+ * of 4 * group up to I2H_MAX_K, ldw >= K, N * K / (4 * group) < 2^31.
+ */
+I2H_API int i2h_pack_variant(const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int group, int layout,
+                             uint8_t* packed, uint16_t* S, uint16_t* ZS, void* stream);
+
+/* i2h_xsum at group `group` (64 or 128): xs [M, K/group] fp32; K a multiple of group. */
+I2H_API int i2h_xsum_group(const uint16_t* x, int64_t M, int64_t K, int group, float* xs, void* stream);
+
+/*
+ * Coarse logits and block candidates of a head packed by i2h_pack_variant with the same group
+ * and layout, scaled per I2H_SCALE_*: c[m, n] = sum_g S * sum_{k in g} x (1 + v/4) - xs ZS
+ * (accumulator; xs from i2h_xsum_group required) or sum_k x[m, k] w~[n, k] with the rounded tile
+ * w~ (xs unused, may be NULL); fp32 accumulation; the block top-kcand as in i2h_coarse_topk.
+ * Limits: 1 <= M <= 16, 1 <= kcand <= 64, K a multiple of 4 * group up to I2H_MAX_K, N <= 2^30.
+ */
+I2H_API int i2h_coarse_variant_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                                    const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int group,
+                                    int layout, int scaling, int kcand, float* cand_score, int32_t* cand_idx,
+                                    void* stream);
+
 /* Workspace bytes i2h_head needs for these sizes (negative I2H_ERR_* on invalid sizes). */
 I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, int R);
 

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
             "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
             "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk",
-            "i2h_select_tokens"}
+            "i2h_select_tokens", "i2h_pack_variant", "i2h_xsum_group", "i2h_coarse_variant_topk"}
     assert names == want
 
 
@@ -237,3 +237,26 @@ def test_select_tokens_rejects_before_launch():
     assert f(P, 1, 100, 1025, P, None) == LIMIT
     assert f(P + 1, 1, 100, 32, P, None) == ALIGN
     assert f(P, 1, 100, 32, P + 2, None) == ALIGN
+
+
+def test_variant_entry_points_reject_before_launch():
+    lib = i2h.lib()
+    # W, ldw, N, K, group, layout, packed, S, ZS, stream
+    f = lib.i2h_pack_variant
+    assert f(None, 5120, 10, 5120, 128, 0, P, P, P, None) == ARG
+    assert f(P, 5120, 10, 5120, 96, 0, P, P, P, None) == ARG         # group 64 or 128
+    assert f(P, 5120, 10, 5120, 128, 2, P, P, P, None) == ARG        # layout 0 or 1
+    assert f(P, 5120, 10, 5000, 128, 0, P, P, P, None) == SHAPE      # K % (4 group)
+    assert f(P, 5120, 10, 5376, 64, 1, P, P, P, None) == SHAPE       # ldw < K
+    assert f(P + 1, 5120, 10, 5120, 64, 1, P, P, P, None) == ALIGN
+    # x, M, K, group, xs, stream
+    g = lib.i2h_xsum_group
+    assert g(P, 1, 5120, 32, P, None) == ARG
+    assert g(P, 1, 5100, 64, P, None) == SHAPE
+    # x, xs, M, packed, S, ZS, N, K, group, layout, scaling, kcand, cand_score, cand_idx, stream
+    c = lib.i2h_coarse_variant_topk
+    assert c(P, None, 1, P, P, P, 1000, 5120, 128, 0, 0, 8, P, P, None) == ARG      # xs for the accumulator
+    assert c(P, P, 17, P, P, P, 1000, 5120, 128, 0, 0, 8, P, P, None) == SHAPE      # M <= 16
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 2, 8, P, P, None) == ARG
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 0, P, P, None) == LIMIT
+    assert c(P + 8, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 8, P, P, None) == ALIGN

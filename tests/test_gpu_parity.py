@@ -579,3 +579,66 @@ def test_select_tokens_all_ties_and_signed_zeros(i2h):
     sel = i2h.select_tokens(dev_bf16(y), 40)
     torch.cuda.synchronize()
     assert np.array_equal(host(sel), oracle.select_tokens(y, 40))
+
+
+# ---------------------------------------------------------------------------------------------
+# design alternatives (group 64, contiguous-4 bytes, dequantised weight tile): pack bit-exact,
+# coarse candidates within the coarse tolerance of the oracle's variant
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("group,layout", [(128, "quarter"), (64, "quarter"), (128, "contiguous"), (64, "contiguous")])
+@pytest.mark.parametrize("N,K", [(1000, 1024), (37, 5120), (300, 512)])
+def test_pack_variant_bit_exact(i2h, group, layout, N, K):
+    say(f"pack_variant G={group} {layout} N={N} K={K}")
+    W = si.bits(si.gen_weight(N, K, seed=500 + N + group))
+    W = np.concatenate([W, degenerate_rows(K)])
+    p, S, ZS = i2h.pack_variant(dev_bf16(W), group, layout)
+    torch.cuda.synchronize()
+    po, So, ZSo = oracle.pack_variant(W, G=group, layout=layout)
+    assert np.array_equal(host(p), po)
+    assert np.array_equal(host(S), So) and np.array_equal(host(ZS), ZSo)
+
+
+def variant_oracle(xb, p, S, ZS, group, layout, scaling):
+    if scaling == "tile":
+        assert layout == "quarter"
+        return oracle.coarse_logits_tile(xb, p, S, ZS, group)
+    if layout == "contiguous":
+        return oracle.coarse_logits_contiguous4(xb, p, S, ZS, group)
+    return oracle.coarse_logits(xb, p, S, ZS, group)
+
+
+VARIANTS = [(128, "quarter", "accumulator"), (64, "quarter", "accumulator"), (128, "contiguous", "accumulator"),
+            (64, "contiguous", "accumulator"), (128, "quarter", "tile"), (64, "quarter", "tile")]
+
+
+@pytest.mark.parametrize("group,layout,scaling", VARIANTS)
+@pytest.mark.parametrize("M,N,K,kc", [(1, 4096, 512, 8), (5, 1000, 1024, 8), (16, 2011, 5120, 4)])
+def test_coarse_variant(i2h, group, layout, scaling, M, N, K, kc):
+    say(f"coarse_variant G={group} {layout} {scaling} M={M} N={N} K={K} kc={kc}")
+    xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=600 + M + K))
+    Wb = si.bits(si.gen_weight(N, K, seed=700 + N + K))
+    p, S, ZS = oracle.pack_variant(Wb, G=group, layout=layout)
+    x = dev_bf16(xb)
+    xs = i2h.xsum_group(x, group) if scaling == "accumulator" else None
+    cs, ci = i2h.coarse_variant_topk(x, xs, torch.from_numpy(p).to(DEV), dev_bf16(S), dev_bf16(ZS), group, layout,
+                                     scaling, kc)
+    torch.cuda.synchronize()
+    c = variant_oracle(xb, p, S, ZS, group, layout, scaling)
+    pu.check_candidates(host(cs), host(ci), c, kc)
+
+
+@pytest.mark.parametrize("group,layout,scaling", [(64, "quarter", "accumulator"), (128, "quarter", "tile")])
+def test_coarse_variant_full_vocab_slice(i2h, group, layout, scaling):
+    M, N, K, kc = 1, 124160, 5120, 8
+    say(f"coarse_variant full size G={group} {layout} {scaling}")
+    xb = si.bits(si.gen_x(M, K, outliers=8, seed=800))
+    Wb = si.bits(si.gen_weight(N, K, seed=801))
+    W = dev_bf16(Wb)
+    pg, Sg, ZSg = i2h.pack_variant(W, group, layout)
+    x = dev_bf16(xb)
+    xs = i2h.xsum_group(x, group) if scaling == "accumulator" else None
+    cs, ci = i2h.coarse_variant_topk(x, xs, pg, Sg, ZSg, group, layout, scaling, kc)
+    torch.cuda.synchronize()
+    p, S, ZS = oracle.pack_variant(Wb, G=group, layout=layout)
+    assert np.array_equal(host(pg), p) and np.array_equal(host(Sg), S) and np.array_equal(host(ZSg), ZS)
+    pu.check_candidates(host(cs), host(ci), variant_oracle(xb, p, S, ZS, group, layout, scaling), kc)
