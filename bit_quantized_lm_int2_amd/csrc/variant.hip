@@ -12,8 +12,9 @@
 // each quarter (the lane's G/4 bytes of the row serve all four), in the contiguous layout 4
 // consecutive groups (the lane takes G/16 bytes of each). Every group instance is G/32 MFMAs
 // (16x16x32 bf16) over k0 + (G/4) h + 8 s .. + 8, the same k slots in both layouts, so the
-// x fragments are addressed alike. Up to 4 rows of x are staged in LDS once per workgroup when
-// they fit in 64 KiB with the rest (otherwise x is read from L2); the next span's bytes and scales are loaded one span ahead. The emit is
+// x fragments are addressed alike. The block's S and ZS are staged in LDS once per workgroup (so
+// both layouts read a group's scales the same way), and so are up to 4 rows of x, when they fit
+// in 64 KiB with the rest (otherwise they are read from L2); the next span's bytes and scales are loaded one span ahead. The emit is
 // the int4 kernel's (a wave bitonic sort).
 //
 // Pack kernel (load time): one 256-thread workgroup per (row, span), the page's quantiser with
@@ -160,7 +161,7 @@ __device__ __forceinline__ bf16x8 tile8(const u32x4& c, float sv, float zv) {
 
 constexpr int kVXRows = 4;  // rows of x staged in LDS
 
-template <int G, int LAYOUT, int SCALE, bool XL>
+template <int G, int LAYOUT, int SCALE, bool XL, bool SZL>
 __global__ __launch_bounds__(kVThreads) void coarse_variant_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M, const uint8_t* __restrict__ packed,
     const uint16_t* __restrict__ S, const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk,
@@ -172,7 +173,8 @@ __global__ __launch_bounds__(kVThreads) void coarse_variant_kernel(
   const int KG = K / G, Q = K / 4, nsp = K / (4 * G);
   float* xsT = smem;                                          // [KG][16] (accumulator scaling)
   float* cbuf = smem + (SCALE == kAcc ? KG * 16 : 0);         // [16][64]
-  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + 16 * kBlockN);  // [M][K] when XL
+  uint32_t* szl = reinterpret_cast<uint32_t*>(cbuf + 16 * kBlockN);  // [KG][64] S | ZS << 16 when SZL
+  uint16_t* xl = reinterpret_cast<uint16_t*>(szl + (SZL ? KG * kBlockN : 0));  // [M][K] when XL
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x;
@@ -189,7 +191,15 @@ __global__ __launch_bounds__(kVThreads) void coarse_variant_kernel(
     for (int i = tid; i < M * K / 8; i += kVThreads)
       *reinterpret_cast<u32x4*>(xl + 8 * i) = ld16(x + 8 * (int64_t)i);
   }
-  if constexpr (SCALE == kAcc || XL) __syncthreads();
+  if constexpr (SZL) {
+    for (int i = tid; i < KG * kBlockN; i += kVThreads) {
+      const int r = i / KG, g = i - r * KG;
+      const int nn = b * kBlockN + r;
+      const int64_t at = (int64_t)(nn < N ? nn : 0) * KG + g;
+      szl[g * kBlockN + r] = (uint32_t)S[at] | ((uint32_t)ZS[at] << 16);
+    }
+  }
+  if constexpr (SCALE == kAcc || XL || SZL) __syncthreads();
   const uint8_t* prow = packed + (int64_t)nr * Q;
   const uint16_t* srow = S + (int64_t)nr * KG;
   const uint16_t* zrow = ZS + (int64_t)nr * KG;
@@ -218,8 +228,14 @@ __global__ __launch_bounds__(kVThreads) void coarse_variant_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = bf16_lo(srow[gidx(sp, i)]);
-      zv[i] = bf16_lo(zrow[gidx(sp, i)]);
+      if constexpr (SZL) {
+        const uint32_t v = szl[gidx(sp, i) * kBlockN + wave * 16 + col];
+        sv[i] = bf16_lo(v);
+        zv[i] = bf16_hi(v);
+      } else {
+        sv[i] = bf16_lo(srow[gidx(sp, i)]);
+        zv[i] = bf16_lo(zrow[gidx(sp, i)]);
+      }
     }
   };
 
@@ -287,15 +303,26 @@ __global__ __launch_bounds__(kVThreads) void coarse_variant_kernel(
 template <int G, int LAYOUT, int SCALE>
 void launch_variant(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                     const uint16_t* ZS, int N, int K, int kc, int nblk, float* cs, int32_t* ci, hipStream_t s) {
+  // what fits in the default 64 KiB of dynamic LDS: the block's scales, then up to 4 rows of x
   size_t lds = ((SCALE == kAcc ? (size_t)(K / G) * 16 : 0) + (size_t)16 * kBlockN) * sizeof(float);
-  if (M <= kVXRows && lds + (size_t)M * K * sizeof(uint16_t) <= 65536) {  // default dynamic LDS limit
-    lds += (size_t)M * K * sizeof(uint16_t);
-    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, true>), dim3((unsigned)nblk), dim3(kVThreads), lds, s,
-                       x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci);
-  } else {
-    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, false>), dim3((unsigned)nblk), dim3(kVThreads), lds,
-                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci);
-  }
+  const size_t szb = (size_t)(K / G) * kBlockN * sizeof(uint32_t), xb = (size_t)M * K * sizeof(uint16_t);
+  const bool szl = lds + szb <= 65536;
+  if (szl) lds += szb;
+  const bool xl = M <= kVXRows && lds + xb <= 65536;
+  if (xl) lds += xb;
+  const dim3 grid((unsigned)nblk), block(kVThreads);
+  if (szl && xl)
+    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, true, true>), grid, block, lds, s, x, xs, M, packed,
+                       S, ZS, N, K, kc, nblk, cs, ci);
+  else if (szl)
+    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, false, true>), grid, block, lds, s, x, xs, M, packed,
+                       S, ZS, N, K, kc, nblk, cs, ci);
+  else if (xl)
+    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, true, false>), grid, block, lds, s, x, xs, M, packed,
+                       S, ZS, N, K, kc, nblk, cs, ci);
+  else
+    hipLaunchKernelGGL((coarse_variant_kernel<G, LAYOUT, SCALE, false, false>), grid, block, lds, s, x, xs, M,
+                       packed, S, ZS, N, K, kc, nblk, cs, ci);
 }
 
 template <int G>

@@ -612,8 +612,10 @@ VARIANTS = [(128, "quarter", "accumulator"), (64, "quarter", "accumulator"), (12
 
 
 @pytest.mark.parametrize("group,layout,scaling", VARIANTS)
-@pytest.mark.parametrize("M,N,K,kc", [(1, 4096, 512, 8), (5, 1000, 1024, 8), (16, 2011, 5120, 4)])
+@pytest.mark.parametrize("M,N,K,kc", [(1, 4096, 512, 8), (5, 1000, 1024, 8), (16, 2011, 5120, 4),
+                                      (1, 300, 16384, 4), (5, 300, 16384, 4)])
 def test_coarse_variant(i2h, group, layout, scaling, M, N, K, kc):
+    """Scales and x staged in LDS (small K), x only (K = 16384 at one row), neither (K = 16384, 5 rows)."""
     say(f"coarse_variant G={group} {layout} {scaling} M={M} N={N} K={K} kc={kc}")
     xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=600 + M + K))
     Wb = si.bits(si.gen_weight(N, K, seed=700 + N + K))
