@@ -142,7 +142,9 @@ class Head:
         self.a_srr_sel = (P(self.cs), P(self.ci), M, nblk, KC, R, P(x), P(W), W.stride(0), N, K, 1, P(self.sel),
                           P(self.ex), P(self.oi), P(self.ov), s)
         # token-level selection over the coarse row (the alternative to block candidates)
-        self.a_seltok = (P(self.y), M, N, R, P(self.sel), s)
+        nws = i2h.lib().i2h_select_tokens_workspace_bytes(M, N, R)
+        self.ws_tok = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        self.a_seltok = (P(self.y), M, N, R, P(self.sel), P(self.ws_tok) if nws > 0 else None, nws, s)
         self.a_rr_sel = (P(x), M, P(W), W.stride(0), N, K, P(self.sel), R, 1, None, P(self.oi), P(self.ov), s)
         self.a_logits = {topk: (None if topk else P(self.y), M, N, P(self.sel), P(self.ex), R, int(topk), None, 0,
                                 P(self.y), 1, s) for topk in (False, True)}

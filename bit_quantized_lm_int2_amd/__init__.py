@@ -52,7 +52,8 @@ _SIGNATURES = {
     "i2h_pack_fp8": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_pack4": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_coarse4_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _P, _P, _P, _P], _INT),
-    "i2h_select_tokens": ([_P, _I64, _I64, _INT, _P, _P], _INT),
+    "i2h_select_tokens": ([_P, _I64, _I64, _INT, _P, _P, _I64, _P], _INT),
+    "i2h_select_tokens_workspace_bytes": ([_I64, _I64, _INT], _I64),
     "i2h_pack_variant": ([_P, _I64, _I64, _I64, _INT, _INT, _P, _P, _P, _P], _INT),
     "i2h_xsum_group": ([_P, _I64, _I64, _INT, _P, _P], _INT),
     "i2h_coarse_variant_topk": ([_P, _P, _I64, _P, _P, _P, _I64, _I64, _INT, _INT, _INT, _INT, _P, _P, _P], _INT),
@@ -505,14 +506,18 @@ def coarse4_topk(x, xs, packed4, S, ZS, kcand: int = 1, want_y: bool = False):
     return (cs, ci, y) if want_y else (cs, ci)
 
 
-def select_tokens(y, R: int):
+def select_tokens(y, R: int, chunked: bool = True):
     """sel int32 [M, R]: the R largest entries of each bf16 row of y (value descending, lower
-    index first on ties), -1 past a row's end."""
+    index first on ties), -1 past a row's end. chunked=False takes one workgroup per row."""
     _need(y, "y", torch.bfloat16, 2)
     _dense(y, "y")
     M, N = y.shape
     sel = torch.empty(M, R, dtype=torch.int32, device=y.device)
-    _check("i2h_select_tokens", lib().i2h_select_tokens(_ptr(y), M, N, R, _ptr(sel), _stream(y)))
+    nws = lib().i2h_select_tokens_workspace_bytes(M, N, R) if chunked else 0
+    if nws < 0:
+        raise I2HError("i2h_select_tokens_workspace_bytes", nws)
+    ws = torch.empty(nws, dtype=torch.uint8, device=y.device) if nws > 0 else None
+    _check("i2h_select_tokens", lib().i2h_select_tokens(_ptr(y), M, N, R, _ptr(sel), _ptr(ws), nws, _stream(y)))
     return sel
 
 

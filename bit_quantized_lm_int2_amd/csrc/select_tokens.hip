@@ -23,6 +23,8 @@ constexpr int kStPer = 8;                      // entries per thread per sweep (
 constexpr int kStSpan = kStThreads * kStPer;   // entries per sweep
 constexpr int kStBins = 4096;                  // top 12 bits of the key
 constexpr int kStNB = 16;                      // sweeps loaded together (one batch)
+constexpr int kStChunk = 2 * kStSpan;          // entries per workgroup in the chunked form
+constexpr int kStMergeMax = 8192;              // chunk keys one merge sorts (64 KiB of LDS)
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 struct StLds {
@@ -100,14 +102,12 @@ __device__ __forceinline__ void append(StLds& L, uint32_t key, int64_t i) {
   if (p < I2H_MAX_R) L.list[p] = ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)i);
 }
 
-__global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_t* __restrict__ y, int64_t N, int R,
-                                                                   bool vec, int32_t* __restrict__ sel) {
-  __shared__ StLds L;
+// The `target` best entries of row[0, len) (value descending, lower index first), as ranking keys
+// key16 << 32 | ~(base_idx + i), unordered in L.list[0, target). The whole workgroup calls it.
+template <int NB>
+__device__ __forceinline__ void radix_select(const uint16_t* __restrict__ row, int64_t len, int64_t base_idx,
+                                             uint32_t target, bool vec, StLds& L) {
   const int tid = threadIdx.x;
-  const int64_t m = blockIdx.x;
-  const uint16_t* row = y + m * N;
-  const uint32_t target = (uint32_t)(N < (int64_t)R ? N : (int64_t)R);
-
   for (int b = tid; b < kStBins; b += kStThreads) L.hist[b] = 0u;
   if (tid < 16) L.hist2[tid] = 0u;
   if (tid == 0) {
@@ -116,23 +116,23 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
   }
   __syncthreads();
 
-  // batches of kStNB sweeps; a row of at most one batch is loaded once for all passes
-  const int64_t batch = (int64_t)kStNB * kStSpan;
-  const bool resident = N <= batch;
-  u32x4 v[kStNB];
+  // batches of NB sweeps; a row of at most one batch is loaded once for all passes
+  const int64_t batch = (int64_t)NB * kStSpan;
+  const bool resident = len <= batch;
+  u32x4 v[NB];
   auto load_batch = [&](int64_t b0) {
 #pragma unroll
-    for (int j = 0; j < kStNB; ++j) v[j] = load8(row, N, b0 + (int64_t)j * kStSpan + kStPer * tid, vec);
+    for (int j = 0; j < NB; ++j) v[j] = load8(row, len, b0 + (int64_t)j * kStSpan + kStPer * tid, vec);
   };
   if (resident) load_batch(0);
   uint32_t k[kStPer];
 
   // 1. histogram of the top 12 bits
-  for (int64_t b0 = 0; b0 < N; b0 += batch) {
+  for (int64_t b0 = 0; b0 < len; b0 += batch) {
     if (!resident) load_batch(b0);
 #pragma unroll
-    for (int j = 0; j < kStNB; ++j) {
-      const int nv = valid_count(N, b0 + (int64_t)j * kStSpan + kStPer * tid);
+    for (int j = 0; j < NB; ++j) {
+      const int nv = valid_count(len, b0 + (int64_t)j * kStSpan + kStPer * tid);
       keys_of(v[j], k);
 #pragma unroll
       for (int e = 0; e < kStPer; ++e)
@@ -165,11 +165,11 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
   __syncthreads();
   // 2. the low 4 bits inside that bin
   const uint32_t bin = L.bin;
-  for (int64_t b0 = 0; b0 < N; b0 += batch) {
+  for (int64_t b0 = 0; b0 < len; b0 += batch) {
     if (!resident) load_batch(b0);
 #pragma unroll
-    for (int j = 0; j < kStNB; ++j) {
-      const int nv = valid_count(N, b0 + (int64_t)j * kStSpan + kStPer * tid);
+    for (int j = 0; j < NB; ++j) {
+      const int nv = valid_count(len, b0 + (int64_t)j * kStSpan + kStPer * tid);
       keys_of(v[j], k);
 #pragma unroll
       for (int e = 0; e < kStPer; ++e)
@@ -194,18 +194,18 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
   const uint32_t T = L.T, need = L.need;
   const bool all_eq = L.eq == need;  // no tie at the threshold is cut
   uint32_t taken = 0;                // entries equal to T already placed (workgroup-uniform)
-  for (int64_t b0 = 0; b0 < N; b0 += batch) {
+  for (int64_t b0 = 0; b0 < len; b0 += batch) {
     if (!resident) load_batch(b0);
 #pragma unroll
-    for (int j = 0; j < kStNB; ++j) {
+    for (int j = 0; j < NB; ++j) {
       const int64_t i0 = b0 + (int64_t)j * kStSpan + kStPer * tid;
-      const int nv = valid_count(N, i0);
+      const int nv = valid_count(len, i0);
       keys_of(v[j], k);
       uint32_t c = 0;
 #pragma unroll
       for (int e = 0; e < kStPer; ++e) {
         if (e >= nv) continue;
-        if (k[e] > T || (all_eq && k[e] == T)) append(L, k[e], i0 + e);
+        if (k[e] > T || (all_eq && k[e] == T)) append(L, k[e], base_idx + i0 + e);
         c += (k[e] == T) ? 1u : 0u;
       }
       if (!all_eq && taken < need) {
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
 #pragma unroll
         for (int e = 0; e < kStPer; ++e) {
           if (e < nv && k[e] == T) {
-            if (r < need) append(L, k[e], i0 + e);
+            if (r < need) append(L, k[e], base_idx + i0 + e);
             ++r;
           }
         }
@@ -222,6 +222,15 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
       }
     }
   }
+}
+
+__global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_t* __restrict__ y, int64_t N, int R,
+                                                                   bool vec, int32_t* __restrict__ sel) {
+  __shared__ StLds L;
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const uint32_t target = (uint32_t)(N < (int64_t)R ? N : (int64_t)R);
+  radix_select<kStNB>(y + m * N, N, 0, target, vec, L);
   __syncthreads();
   // 4. order the target entries (key descending, index ascending), padding to a power of two
   const int P = pow2_at_least((int)target);
@@ -232,17 +241,69 @@ __global__ __launch_bounds__(kStThreads) void select_tokens_kernel(const uint16_
     sel[m * R + j] = j < (int)target ? (int32_t)(~(uint32_t)L.list[j]) : -1;
 }
 
+// Chunked form for long rows: chunk c of a row (kStChunk entries) selects its own best R into
+// ws[m][c][0, R) (keys, 0 past the chunk's count); every entry of the row's best R is among its
+// chunk's best R under the same order, so the merge sorts the chunks' keys and keeps R.
+__global__ __launch_bounds__(kStThreads) void select_chunks_kernel(const uint16_t* __restrict__ y, int64_t N, int R,
+                                                                   bool vec, uint64_t* __restrict__ ws) {
+  __shared__ StLds L;
+  const int tid = threadIdx.x;
+  const int64_t c = blockIdx.x, m = blockIdx.y, nc = gridDim.x;
+  const int64_t c0 = c * kStChunk;
+  const int64_t len = N - c0 < kStChunk ? N - c0 : kStChunk;
+  const uint32_t target = (uint32_t)(len < (int64_t)R ? len : (int64_t)R);
+  radix_select<kStChunk / kStSpan>(y + m * N + c0, len, c0, target, vec, L);
+  __syncthreads();
+  uint64_t* out = ws + (m * nc + c) * R;
+  for (int j = tid; j < R; j += kStThreads) out[j] = j < (int)target ? L.list[j] : 0ull;
+}
+
+__global__ __launch_bounds__(kStThreads) void merge_chunks_kernel(const uint64_t* __restrict__ ws, int nc, int R,
+                                                                  int32_t* __restrict__ sel) {
+  __shared__ uint64_t keys[kStMergeMax];
+  const int tid = threadIdx.x;
+  const int64_t m = blockIdx.x;
+  const int n = nc * R, P = pow2_at_least(n);
+  for (int i = tid; i < P; i += kStThreads) keys[i] = i < n ? ws[m * n + i] : 0ull;
+  __syncthreads();
+  block_sort_desc(keys, P);
+  for (int j = tid; j < R; j += kStThreads) sel[m * R + j] = keys[j] == 0ull ? -1 : (int32_t)(~(uint32_t)keys[j]);
+}
+
 }  // namespace
 }  // namespace i2h
 
-extern "C" int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* stream) {
+namespace {
+// Chunks of a row and whether the chunked form applies (at least two chunks, the merge fits).
+int64_t chunks_of(int64_t N) { return (N + i2h::kStChunk - 1) / i2h::kStChunk; }
+bool chunked(int64_t N, int R) { return chunks_of(N) >= 2 && chunks_of(N) * R <= i2h::kStMergeMax; }
+}  // namespace
+
+extern "C" int64_t i2h_select_tokens_workspace_bytes(int64_t M, int64_t N, int R) {
+  if (M < 1 || N < 1 || R < 1 || R > I2H_MAX_R) return I2H_ERR_LIMIT;
+  return chunked(N, R) ? M * chunks_of(N) * R * (int64_t)sizeof(uint64_t) : 0;
+}
+
+extern "C" int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
   using namespace i2h;
   if (!y || !sel) return I2H_ERR_ARG;
-  if (M < 1 || M > 0x7fffffff || N < 1 || N > 0x7fffffff) return I2H_ERR_SHAPE;
+  if (M < 1 || M > 65535 || N < 1 || N > 0x7fffffff) return I2H_ERR_SHAPE;
   if (R < 1 || R > I2H_MAX_R) return I2H_ERR_LIMIT;
-  if (!aligned(y, 2) || !aligned(sel, 4)) return I2H_ERR_ALIGN;
-  const bool vec = aligned(y, 16) && (N % 8) == 0;  // then every row starts on a 16-byte boundary
-  hipLaunchKernelGGL(select_tokens_kernel, dim3((unsigned)M), dim3(kStThreads), 0, (hipStream_t)stream, y, N, R,
-                     vec, sel);
+  if (!aligned(y, 2) || !aligned(sel, 4) || (workspace && !aligned(workspace, 8))) return I2H_ERR_ALIGN;
+  const bool vec = aligned(y, 16) && (N % 8) == 0;  // then every row (and chunk) starts on a 16-byte boundary
+  const hipStream_t s = (hipStream_t)stream;
+  if (workspace && chunked(N, R)) {
+    if (workspace_bytes < M * chunks_of(N) * R * (int64_t)sizeof(uint64_t)) return I2H_ERR_WORKSPACE;
+    const int nc = (int)chunks_of(N);
+    hipLaunchKernelGGL(select_chunks_kernel, dim3((unsigned)nc, (unsigned)M), dim3(kStThreads), 0, s, y, N, R, vec,
+                       static_cast<uint64_t*>(workspace));
+    const int st = check_launch();
+    if (st != I2H_OK) return st;
+    hipLaunchKernelGGL(merge_chunks_kernel, dim3((unsigned)M), dim3(kStThreads), 0, s,
+                       static_cast<const uint64_t*>(workspace), nc, R, sel);
+    return check_launch();
+  }
+  hipLaunchKernelGGL(select_tokens_kernel, dim3((unsigned)M), dim3(kStThreads), 0, s, y, N, R, vec, sel);
   return check_launch();
 }

@@ -231,10 +231,16 @@ I2H_API int i2h_coarse4_topk(const uint16_t* x, const float* xs, int64_t M, cons
  * measures; radiance_drafthead.py, _emit docstring and the module docstring's note on
  * selection): sel [M, R] int32 = for each row of y [M, N] bf16 (row-major, row stride N), the
  * indices of its R largest entries, value descending, lower index first on ties, -0.0 equal to
- * +0.0; -1 in slots past N. Feed sel to i2h_rerank or i2h_rerank_topk. y finite. Limits:
- * 1 <= M, N <= 2^31 - 1, 1 <= R <= I2H_MAX_R; y 2-byte and sel 4-byte aligned.
+ * +0.0; -1 in slots past N. Feed sel to i2h_rerank or i2h_rerank_topk. y finite. With a
+ * workspace of i2h_select_tokens_workspace_bytes() (caller-owned, 8-byte aligned, contents
+ * undefined afterwards) a long row is split over workgroups of 16384 entries whose winners are
+ * merged; with workspace NULL (or a size of 0 bytes returned) one workgroup takes each row. Both
+ * give the same sel. Limits: 1 <= M <= 65535, 1 <= N <= 2^31 - 1, 1 <= R <= I2H_MAX_R; y 2-byte
+ * and sel 4-byte aligned; a workspace smaller than needed is I2H_ERR_WORKSPACE.
  */
-I2H_API int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* stream);
+I2H_API int64_t i2h_select_tokens_workspace_bytes(int64_t M, int64_t N, int R);
+I2H_API int i2h_select_tokens(const uint16_t* y, int64_t M, int64_t N, int R, int32_t* sel, void* workspace,
+                              int64_t workspace_bytes, void* stream);
 
 /*
  * The design alternatives the head is measured against (radiance_drafthead.py, module

@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
             "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
             "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
             "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk",
-            "i2h_select_tokens", "i2h_pack_variant", "i2h_xsum_group", "i2h_coarse_variant_topk"}
+            "i2h_select_tokens", "i2h_select_tokens_workspace_bytes", "i2h_pack_variant", "i2h_xsum_group", "i2h_coarse_variant_topk"}
     assert names == want
 
 
@@ -227,16 +227,23 @@ def test_int4_entry_points_reject_before_launch():
 
 def test_select_tokens_rejects_before_launch():
     f = i2h.lib().i2h_select_tokens
-    # y, M, N, R, sel, stream
-    assert f(None, 1, 100, 32, P, None) == ARG
-    assert f(P, 1, 100, 32, None, None) == ARG
-    assert f(P, 0, 100, 32, P, None) == SHAPE
-    assert f(P, 1, 0, 32, P, None) == SHAPE
-    assert f(P, 1, 1 << 31, 32, P, None) == SHAPE
-    assert f(P, 1, 100, 0, P, None) == LIMIT
-    assert f(P, 1, 100, 1025, P, None) == LIMIT
-    assert f(P + 1, 1, 100, 32, P, None) == ALIGN
-    assert f(P, 1, 100, 32, P + 2, None) == ALIGN
+    # y, M, N, R, sel, workspace, workspace_bytes, stream
+    assert f(None, 1, 100, 32, P, None, 0, None) == ARG
+    assert f(P, 1, 100, 32, None, None, 0, None) == ARG
+    assert f(P, 0, 100, 32, P, None, 0, None) == SHAPE
+    assert f(P, 65536, 100, 32, P, None, 0, None) == SHAPE
+    assert f(P, 1, 0, 32, P, None, 0, None) == SHAPE
+    assert f(P, 1, 1 << 31, 32, P, None, 0, None) == SHAPE
+    assert f(P, 1, 100, 0, P, None, 0, None) == LIMIT
+    assert f(P, 1, 100, 1025, P, None, 0, None) == LIMIT
+    assert f(P + 1, 1, 100, 32, P, None, 0, None) == ALIGN
+    assert f(P, 1, 100, 32, P + 2, None, 0, None) == ALIGN
+    assert f(P, 1, 124160, 32, P, P + 4, 1 << 20, None) == ALIGN
+    wsb = i2h.lib().i2h_select_tokens_workspace_bytes
+    assert wsb(1, 124160, 32) == 8 * 32 * 8                 # 8 chunks of 16384 entries
+    assert wsb(2, 248320, 1024) == 0                         # 16 x 1024 keys exceed one merge
+    assert wsb(1, 16384, 32) == 0                            # one chunk: one workgroup
+    assert f(P, 1, 124160, 32, P, P, 8 * 32 * 8 - 1, None) == WS
 
 
 def test_variant_entry_points_reject_before_launch():

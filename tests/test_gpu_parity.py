@@ -561,11 +561,13 @@ def test_int4_head_parity(i2h, M, N, K, kc, R, k):
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,R,levels", [(3, 1000, 32, 0), (2, 37, 64, 0), (4, 4099, 32, 2), (2, 8191, 100, 1),
                                           (1, 124160, 32, 0), (2, 248320, 1024, 0), (2, 124160, 16, 3),
-                                          (3, 9000, 1024, 1)])
-def test_select_tokens_exact(i2h, M, N, R, levels):
-    say(f"select_tokens M={M} N={N} R={R} levels={levels}")
+                                          (3, 9000, 1024, 1), (2, 16385, 32, 0), (3, 50001, 64, 2),
+                                          (1, 124160, 1024, 1), (2, 248320, 512, 0)])
+@pytest.mark.parametrize("chunked", [True, False])
+def test_select_tokens_exact(i2h, M, N, R, levels, chunked):
+    say(f"select_tokens M={M} N={N} R={R} levels={levels} chunked={chunked}")
     y = si.gen_coarse_row(M, N, seed=300 + N, levels=levels)
-    sel = i2h.select_tokens(y.to(DEV), R)
+    sel = i2h.select_tokens(y.to(DEV), R, chunked=chunked)
     torch.cuda.synchronize()
     assert np.array_equal(host(sel), oracle.select_tokens(si.bits(y), R))
 
@@ -576,9 +578,11 @@ def test_select_tokens_all_ties_and_signed_zeros(i2h):
     y[1, ::2] = 0x8000                       # -0.0 and +0.0 interleaved: all equal
     y[2] = 0x3F80
     y[2, 19990:] = 0x4000                    # ten larger entries at the end, then ties
-    sel = i2h.select_tokens(dev_bf16(y), 40)
-    torch.cuda.synchronize()
-    assert np.array_equal(host(sel), oracle.select_tokens(y, 40))
+    want = oracle.select_tokens(y, 40)
+    for chunked in (True, False):
+        sel = i2h.select_tokens(dev_bf16(y), 40, chunked=chunked)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(sel), want)
 
 
 # ---------------------------------------------------------------------------------------------
