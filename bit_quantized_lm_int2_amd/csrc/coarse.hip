@@ -538,14 +538,10 @@ bool small_sums_x(int64_t M, int64_t K) {
 }  // namespace
 
 // True when every launch coarse_launch makes for M rows of K sums the groups of x itself: the
-// small kernel with x in LDS (M <= 4) or the tile kernel, per chunk of kTileMaxRows rows.
+// small kernel with x in LDS, for M <= 4 (the many-row kernels take the sums from i2h_xsum).
 bool coarse_sums_x(int64_t M, int64_t K) {
-  if (M < 1 || check_k(K) != I2H_OK) return false;
-  for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
-    const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
-    if (!(mc <= 4 ? small_sums_x(mc, K) : tile_supported(mc, K))) return false;
-  }
-  return true;
+  if (M < 1 || M > 4 || check_k(K) != I2H_OK) return false;
+  return small_sums_x(M, K);
 }
 
 namespace {
@@ -605,6 +601,8 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     int st;
     if (mc <= 4 && (xsc || small_sums_x(mc, K)))
       st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+    else if (!xsc)
+      st = I2H_ERR_ARG;
     else if (tile_supported(mc, K))
       st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, s);
     else

@@ -4,12 +4,15 @@
 // (bit-pattern dequant, scale and zero applied per group to the accumulator, KCAND best columns
 // of every 64-column block per row), laid out for many rows.
 //
-// Layout on gfx950. A workgroup of 4 waves covers 4 consecutive 64-column blocks; wave w owns
-// block 4 blockIdx.x + w whole, as four 16-column MFMA tiles (v_mfma_f32_16x16x32_bf16), so
-// each A fragment of x read from LDS feeds four MFMAs and the block's emit needs no other wave.
-// x is streamed through LDS in stages of 16 KB (all rows, QS quarters of one 128-byte span of
-// the packed rows), double-buffered and shared by the four waves, and the group sums of x are
-// reduced from the staged registers on the way. The wave's S and ZS rows sit in LDS for the
+// Layout on gfx950. A workgroup of WAVES waves covers WAVES consecutive 64-column blocks; wave w
+// owns block WAVES blockIdx.x + w whole, as four 16-column MFMA tiles (v_mfma_f32_16x16x32_bf16)
+// for each 16 rows, so each A fragment of x read from LDS feeds four MFMAs and the block's emit
+// needs no other wave. x is streamed through LDS in stages of 16 KB (all rows, QS quarters of one
+// 128-byte span of the packed rows), double-buffered and shared by the waves. The loop applies
+// only the scale of each group to the accumulator; the zero term, the sum over groups of
+// xs[m, g] z[n, g], is one more small contraction on the matrix cores after the loop, with both
+// factors split exactly into bf16 parts, so that the VALU does the dequant and one FMA per output
+// and group. The group sums xs come from i2h_xsum. The wave's S and ZS rows sit in LDS for the
 // whole K loop. The packed stream is loaded one span ahead, after the next stage of x, so that
 // waiting for x never waits for packed bytes that are not needed yet (loads retire in order).
 // The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
@@ -40,7 +43,7 @@ struct Tile {
 template <int MT, int WAVES>
 constexpr size_t tile_lds_bytes(int KG) {
   using T = Tile<MT, WAVES>;
-  const size_t loop = 2 * (size_t)T::XBUF + 2 * (size_t)T::QS * T::MR * 4 + (size_t)WAVES * 64 * (KG | 1) * 4;
+  const size_t loop = 2 * (size_t)T::XBUF + (size_t)WAVES * 64 * (KG | 1) * 4;
   const size_t emit = (size_t)WAVES * T::MR * kTRow * 4;
   return loop > emit ? loop : emit;
 }
@@ -166,8 +169,8 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
   }
 }
 
-// Up to 32 rows two workgroups share a CU (at most 256 registers per lane); 64 rows need more
-// registers (accumulators, per-quarter partial sums, two packed spans) and run one per CU.
+// Occupancy: a workgroup of 8 waves runs two waves per SIMD (at most 256 registers per lane);
+// 64 rows hold 128 accumulator registers (the sums and each group's partial sums).
 // XPF: x stages loaded ahead of the one being stored; RPF: packed spans loaded ahead of the one in
 // use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
 // arrives with HBM latency; both are therefore fetched more than one stage ahead.
@@ -182,59 +185,38 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   constexpr int NST = NG * T::SPS;
   constexpr int SZU = (64 * KG / 8 + 63) / 64;  // 16-byte units of the wave's S rows per lane
   extern __shared__ __align__(16) uint8_t lds[];
-  uint8_t* xbuf = lds;                                                   // [2][MR][RS]
-  float* xsb = reinterpret_cast<float*>(lds + 2 * T::XBUF);              // [2][QS][MR]
-  uint32_t* szl = reinterpret_cast<uint32_t*>(xsb + 2 * T::QS * T::MR);  // [4][64][KGP]
+  uint8_t* xbuf = lds;                                             // [2][MR][RS]
+  uint32_t* szl = reinterpret_cast<uint32_t*>(lds + 2 * T::XBUF);  // [WAVES][64][KGP]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
   const int n0 = b * kBlockN;
 
-  // --- x stages: unit u = tid + 256 i is 16 bytes (8 k) of row m, quarter t0 + q; the 16 units of
-  // a (row, quarter) group sit in 16 consecutive lanes. Every load is issued unconditionally (rows
-  // past M read row M - 1 and are zeroed when stored): a load under a branch makes the compiler's
-  // wait counts assume it may not have been issued, and every later wait then also waits for it.
-  // xsrc is xs, or when own_sums x itself read at one address (the value is unused).
-  const bool own_sums = xs == nullptr;
-  const float* xsrc = own_sums ? reinterpret_cast<const float*>(x) : xs;
+  // --- x stages: unit u = tid + THREADS i is 16 bytes (8 k) of row m, quarter t0 + q; the 16
+  // units of a (row, quarter) group sit in 16 consecutive lanes. Every load is issued
+  // unconditionally (rows past M read row M - 1, finite, and their results are never emitted): a
+  // load under a branch makes the compiler's wait counts assume it may not have been issued, and
+  // every later wait then also waits for it.
   u32x4 xr[XPF][T::UPT];
-  float xsr[XPF];
-  // load i < UPT of stage st: unit i of x; i == UPT: the group sum (when given)
   auto x_load_one = [&](int st, int i) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
-    if (i < T::UPT) {
-      const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
-      const int q = gq % T::QS, m = gq / T::QS;
-      const int mm = m < M ? m : M - 1;
-      xr[st % XPF][i] = ld16(x + (int64_t)mm * K + (t0 + q) * Q + gb * kGroup + 8 * j);
-    } else {
-      const int q = (tid / T::MR) % T::QS, m = tid % T::MR;
-      xsr[st % XPF] = xsrc[own_sums ? 0 : (int64_t)(m < M ? m : M - 1) * KG + (t0 + q) * NG + gb];
-    }
+    const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
+    const int q = gq % T::QS, m = gq / T::QS;
+    const int mm = m < M ? m : M - 1;
+    xr[st % XPF][i] = ld16(x + (int64_t)mm * K + (t0 + q) * Q + gb * kGroup + 8 * j);
   };
   auto x_load = [&](int st) {
 #pragma unroll
-    for (int i = 0; i <= T::UPT; ++i) x_load_one(st, i);
+    for (int i = 0; i < T::UPT; ++i) x_load_one(st, i);
   };
   auto x_put = [&](int st) {
     uint8_t* xb = xbuf + (st & 1) * T::XBUF;
-    float* xsd = xsb + (st & 1) * T::QS * T::MR;
 #pragma unroll
     for (int i = 0; i < T::UPT; ++i) {
       const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
       const int q = gq % T::QS, m = gq / T::QS;
-      const u32x4 v = m < M ? xr[st % XPF][i] : u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(v);
-      if (own_sums) {
-        float sm = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm += bf16_lo(v[e]) + bf16_hi(v[e]);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
-        if (j == 0) xsd[q * T::MR + m] = sm;
-      }
+      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(xr[st % XPF][i]);
     }
-    if (!own_sums && tid < T::QS * T::MR) xsd[tid] = tid % T::MR < M ? xsr[st % XPF] : 0.f;
   };
 
   // --- packed rows of the wave's four tiles (rows past N read row N - 1; never emitted)
@@ -246,26 +228,31 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   }
   constexpr int kSlots = RPF + 1;  // spans RPF ahead of the one in use
   u32x4 ring[kSlots][kNT][2];
-  auto ring_load_one = [&](int gb, int k) {  // k = 2 nt + half
-    ring[gb % kSlots][k >> 1][k & 1] = ld16(prow[k >> 1] + gb * kGroup + 64 * (k & 1));
+  // slot: the ring entry, gb % kSlots, passed separately so that it is a compile-time constant
+  // wherever the span loop is not fully unrolled (a runtime index would put the ring in scratch)
+  auto ring_load_one = [&](int gb, int slot, int k) {  // k = 2 nt + half
+    ring[slot][k >> 1][k & 1] = ld16(prow[k >> 1] + gb * kGroup + 64 * (k & 1));
   };
   auto ring_load = [&](int gb) {
 #pragma unroll
-    for (int k = 0; k < 2 * kNT; ++k) ring_load_one(gb, k);
+    for (int k = 0; k < 2 * kNT; ++k) ring_load_one(gb, gb % kSlots, k);
   };
   // The loads stage st issues for later stages, in this order: x stage st + XPF (UPT units and the
   // group sums), then, at the first stage of span gb, the packed span gb + RPF. They are spread
   // over the stage's MFMA slices: issued as one burst, they stall the wave at issue while the
   // memory pipeline drains, with the current stage's operands already in registers.
-  constexpr int kStageLoads = T::UPT + 1 + 2 * kNT;
+  constexpr int kStageLoads = T::UPT + 2 * kNT;
   constexpr int kPerSlice = (kStageLoads + 4 * T::QS - 1) / (4 * T::QS);
-  auto stage_load = [&](int st, int k) {
+  // slot: the ring entry of span gb. With clamp (a runtime span loop) the loads past the last
+  // stage or span are issued anyway, for the last one again (an L2 hit), so that no load sits
+  // under a branch.
+  auto stage_load = [&](int st, int slot, int k, bool clamp) {
     const int gb = st / T::SPS, ss = st % T::SPS;
-    const int nx = st + XPF < NST ? T::UPT + 1 : 0;
+    const int nx = clamp || st + XPF < NST ? T::UPT : 0;
     if (k < nx) {
-      x_load_one(st + XPF, k);
-    } else if (ss == 0 && gb + RPF < NG && k - nx < 2 * kNT) {
-      ring_load_one(gb + RPF, k - nx);
+      x_load_one(st + XPF < NST ? st + XPF : NST - 1, k);
+    } else if (ss == 0 && (clamp || gb + RPF < NG) && k - nx < 2 * kNT) {
+      ring_load_one(gb + RPF < NG ? gb + RPF : NG - 1, (slot + RPF) % kSlots, k - nx);
     }
   };
 
@@ -323,10 +310,9 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   const DqConst dqc = dq_const();
   const uint32_t* szc = szw + col * KGP;
 
-  auto compute = [&](int st) {
+  auto compute = [&](int st, int slot, bool clamp) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
     const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + 32 * h;
-    const float* xsd = xsb + (st & 1) * T::QS * T::MR;
     // dw: the span's packed dwords per tile; hw = dw >> 8, kept for the whole stage when the
     // registers allow (16 rows), else formed at each use
     constexpr bool kKeepHw = MT == 1;
@@ -335,8 +321,8 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dw[nt][i] = ring[gb % kSlots][nt][0][i];
-        dw[nt][4 + i] = ring[gb % kSlots][nt][1][i];
+        dw[nt][i] = ring[slot][nt][0][i];
+        dw[nt][4 + i] = ring[slot][nt][1][i];
         if constexpr (kKeepHw) {
           hw[nt][i] = dw[nt][i] >> 8;
           hw[nt][4 + i] = dw[nt][4 + i] >> 8;
@@ -380,30 +366,21 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
                                                                 0, 0, 0);
         }
 #pragma unroll
-        for (int j = 0; j < kPerSlice; ++j) stage_load(st, (qq * 4 + s) * kPerSlice + j);
+        for (int j = 0; j < kPerSlice; ++j) stage_load(st, slot, (qq * 4 + s) * kPerSlice + j, clamp);
         // the scheduler may not pull later slices (their x fragments and dequant) into this one
         __builtin_amdgcn_sched_barrier(0);
       }
+      // the scale term of the group (the zero term is added after the loop)
       const int gi = t * NG + gb;
-      float s2[kNT], z2[kNT];
+      float s2[kNT];
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const uint32_t w = szc[16 * nt * KGP + gi];
-        const float sc = __uint_as_float(w << 16), zc = __uint_as_float(w & 0xffff0000u);
-        s2[nt] = kBiasF[t] * sc;
-        z2[nt] = fmaf(kBiasF[t] - 1.f, sc, zc);
-      }
+      for (int nt = 0; nt < kNT; ++nt) s2[nt] = kBiasF[t] * __uint_as_float(szc[16 * nt * KGP + gi] << 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsd + qq * T::MR + 16 * mt + 4 * h);
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = fmaf(s2[nt], p[mt][nt][r], acc[mt][nt][r]);
-            acc[mt][nt][r] = fmaf(-xv[r], z2[nt], a);
-          }
-      }
+          for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(s2[nt], p[mt][nt][r], acc[mt][nt][r]);
       // the accumulators are complete here: without this the compiler sinks the scaling of every
       // quarter towards the epilogue and keeps all partial sums alive until then
 #pragma unroll
@@ -413,19 +390,81 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
     }
   };
 
+  if constexpr (MT == 1) {
+    // 16 rows: the whole K loop unrolled
 #pragma unroll
-  for (int gb = 0; gb < NG; ++gb) {
+    for (int gb = 0; gb < NG; ++gb) {
 #pragma unroll
-    for (int ss = 0; ss < T::SPS; ++ss) {
-      const int st = gb * T::SPS + ss;
-      __builtin_amdgcn_sched_barrier(0);
-      compute(st);
-      if (st + 1 < NST) {
-        x_put(st + 1);
-        __syncthreads();
+      for (int ss = 0; ss < T::SPS; ++ss) {
+        const int st = gb * T::SPS + ss;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st, gb % kSlots, false);
+        if (st + 1 < NST) {
+          x_put(st + 1);
+          __syncthreads();
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+  } else {
+    // more rows: a runtime loop over groups of kSlots spans, each span's stages unrolled with
+    // its ring slot fixed
+    for (int g0 = 0; g0 < NG; g0 += kSlots) {
+#pragma unroll
+      for (int sl = 0; sl < kSlots; ++sl) {
+        const int gb = g0 + sl;
+        if (NG % kSlots != 0 && gb >= NG) break;
+#pragma unroll
+        for (int ss = 0; ss < T::SPS; ++ss) {
+          const int st = gb * T::SPS + ss;
+          __builtin_amdgcn_sched_barrier(0);
+          compute(st, sl, true);
+          if (st + 1 < NST) {
+            x_put(st + 1);
+            __syncthreads();
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+
+  // --- zero term: c -= sum over groups g of xs[m, g] z[n, g], z = (f_t - 1) S + ZS for the quarter
+  // t of g (the bias fold of the dequant), on the matrix cores. Both factors are split exactly into
+  // bf16 parts, -xs (fp32) into three and z (at most 16 significant bits for the scales the packer
+  // writes) into two, and each group takes the 8 k-slots of one lane block: the six cross products
+  // and two zeros. Step ks covers groups 4 ks + h.
+#pragma unroll 2
+  for (int ks = 0; ks < KG / 4; ++ks) {
+    const int g = 4 * ks + h, t = g / NG;
+    const float fm1 = t == 0 ? 31.f : (t == 1 ? 7.f : (t == 2 ? 1.f : 0.f));  // kBiasF[t] - 1
+    u32x4 za[MT], zb[kNT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + col;
+      const float v = -xs[(int64_t)(m < M ? m : M - 1) * KG + g];
+      const uint32_t p1 = __float_as_uint(v) & 0xffff0000u;
+      const float r1 = v - __uint_as_float(p1);
+      const uint32_t p2 = __float_as_uint(r1) & 0xffff0000u;
+      const uint32_t p3 = __float_as_uint(r1 - __uint_as_float(p2));
+      za[mt] = u32x4{__builtin_amdgcn_perm(p1, p1, 0x07060302u), __builtin_amdgcn_perm(p2, p2, 0x07060302u),
+                     __builtin_amdgcn_perm(p3, p3, 0x07060302u), 0u};
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const uint32_t w = szc[16 * nt * KGP + g];
+      const float z = fmaf(fm1, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+      const uint32_t zh = __float_as_uint(z) & 0xffff0000u;
+      const uint32_t zl = __float_as_uint(z - __uint_as_float(zh));
+      const uint32_t pr = __builtin_amdgcn_perm(zl, zh, 0x07060302u);  // bf16 zh | bf16 zl << 16
+      zb[nt] = u32x4{pr, pr, pr, 0u};
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[mt]),
+                                                              __builtin_bit_cast(bf16x8, zb[nt]), acc[mt][nt], 0, 0, 0);
   }
 
   // --- epilogue: acc[mt][nt][r] is c[m = 16 mt + 4 h + r][n = n0 + 16 nt + col]
@@ -482,11 +521,14 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
 #ifndef I2H_TILE_WAVES
 #define I2H_TILE_WAVES 8
 #endif
-// Tiles above 16 rows re-read x (from L2, or beyond it when the packed stream evicts it) for
-// every 64 * WAVES columns, and measure slower than running the 16-row tile per 16 rows, which
-// re-reads the packed stream instead: by default rows go through the 16-row tile.
+// 33..64 rows: 8 waves of 64 rows x 64 columns, two per SIMD (a few address registers spill to
+// scratch outside the inner loop; measured faster than 4 waves with no spills, one per SIMD)
+#ifndef I2H_TILE_WAVES64
+#define I2H_TILE_WAVES64 8
+#endif
+// the largest row tile used: 1 (16 rows), 2 (32) or 4 (64); more rows go in chunks of it
 #ifndef I2H_TILE_MAXMT
-#define I2H_TILE_MAXMT 1
+#define I2H_TILE_MAXMT 4
 #endif
 
 template <int NGC>
@@ -495,8 +537,8 @@ int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, 
   if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
   if constexpr (I2H_TILE_MAXMT >= 2)
     if (M <= 32) return launch_tile<2, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
-  if constexpr (I2H_TILE_MAXMT >= 4) return launch_tile<4, 4, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
-  // rows in chunks of 16 through the 16-row tile
+  if constexpr (I2H_TILE_MAXMT >= 4) return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+  // rows in chunks of 16 through the 16-row tile (a build limited to it)
   const int64_t ld = nblk_of(N) * kc, KG = NGC * 4;
   for (int m0 = 0; m0 < M; m0 += 16) {
     const int mc = M - m0 < 16 ? M - m0 : 16;
@@ -516,6 +558,7 @@ int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* pa
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
                 hipStream_t s) {
   if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
+  if (!xs) return I2H_ERR_ARG;
   if (K == 5120) return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
   return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
 }

@@ -29,7 +29,7 @@ inline int64_t nblk_of(int64_t N) { return (N + I2H_BLOCK_N - 1) / I2H_BLOCK_N; 
 bool coarse_sums_x(int64_t M, int64_t K);
 
 // The many-row coarse kernel (coarse_tile.hip): up to kTileMaxRows rows of x per launch, for the
-// K it is built for; it sums the groups of x itself when xs is null.
+// K it is built for; it takes the group sums xs (never null) from i2h_xsum.
 constexpr int64_t kTileMaxRows = 64;
 bool tile_supported(int64_t M, int64_t K);
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,

@@ -61,10 +61,11 @@ def test_coarse_sums_x():
     lib = i2h.lib()
     assert lib.i2h_coarse_sums_x(1, 5120) == 1
     assert lib.i2h_coarse_sums_x(4, 5120) == 1
-    assert lib.i2h_coarse_sums_x(16, 5120) == 1   # the many-row kernel sums x itself
-    assert lib.i2h_coarse_sums_x(64, 5120) == 1
-    assert lib.i2h_coarse_sums_x(130, 512) == 1   # chunks of 64, 64 and 2 rows
-    assert lib.i2h_coarse_sums_x(16, 1024) == 0   # a K the many-row kernel is not built for
+    assert lib.i2h_coarse_sums_x(2, 512) == 1
+    assert lib.i2h_coarse_sums_x(5, 5120) == 0    # the many-row kernel takes xs from i2h_xsum
+    assert lib.i2h_coarse_sums_x(16, 5120) == 0
+    assert lib.i2h_coarse_sums_x(64, 5120) == 0
+    assert lib.i2h_coarse_sums_x(130, 512) == 0   # chunks of 64, 64 and 2 rows
     assert lib.i2h_coarse_sums_x(4, 16384) == 0   # x does not fit in LDS
     assert lib.i2h_coarse_sums_x(1, 1000) == 0
     c = lib.i2h_coarse_topk
