@@ -256,7 +256,7 @@ def to_dev_bits(torch, np, b, dev):
 
 def traffic_probe(torch, i2h, si, dev):
     """Launches for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: the coarse kernel on the timed
-    workload at M = 1, 16, 64 (cold weight copies, 6 launches each), and a plain device copy of a
+    workload at M = 1, 16, 32, 64 (cold weight copies, 6 launches each), and a plain device copy of a
     512 MiB buffer (4 launches) whose counter readings give the bytes-per-count factor."""
     cfg = si.WORKLOADS[WORKLOAD]
     K, N = cfg["K"], cfg["N"]
@@ -265,7 +265,7 @@ def traffic_probe(torch, i2h, si, dev):
     del W
     copies = [(packed, S, ZS)] + [(packed.clone(), S.clone(), ZS.clone()) for _ in range(COPIES - 1)]
     x_all = si.gen_x(64, K, outliers=cfg["outliers"]).to(dev)
-    for M in (1, 16, 64):
+    for M in (1, 16, 32, 64):
         x = x_all[:M].contiguous()
         xs = None if i2h.coarse_sums_x(M, K) else i2h.xsum(x)
         for i in range(6):
@@ -278,7 +278,7 @@ def traffic_probe(torch, i2h, si, dev):
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(), "M": [1, 16, 64]}), flush=True)
+    print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(), "M": [1, 16, 32, 64]}), flush=True)
 
 
 def main():
@@ -289,7 +289,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bands", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="only launch the coarse kernel 6 times per M in (1, 16, 64) on cold weight copies, "
+                    help="only launch the coarse kernel 6 times per M in (1, 16, 32, 64) on cold weight copies, "
                          "then copy a 512 MiB buffer 4 times (the calibration kernel for HBM byte counters)")
     ap.add_argument("--match-rows", type=int, default=32)
     args = ap.parse_args()
@@ -536,7 +536,7 @@ def main():
 
     bands = []
     if not args.no_bands:
-        for Mb in (16, 64):
+        for Mb in (16, 32, 64):
             log(f"[bench] timing band M={Mb}")
             hbh, dtb, cmsb, dtfb = measure(Mb, max(20, args.steps // 2), max(5, args.warmup // 2))
             hbb = head_bytes(Mb, N, K, own_sums=hbh.own_sums)

@@ -169,8 +169,9 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
   }
 }
 
-// Occupancy: a workgroup of 8 waves runs two waves per SIMD (at most 256 registers per lane);
-// 64 rows hold 128 accumulator registers (the sums and each group's partial sums).
+// Occupancy: two waves per SIMD (at most 256 registers per lane), as two workgroups of 4 waves or
+// one of 8 per CU; 64 rows hold 128 accumulator registers (the sums and each group's partial
+// sums).
 // XPF: x stages loaded ahead of the one being stored; RPF: packed spans loaded ahead of the one in
 // use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
 // arrives with HBM latency; both are therefore fetched more than one stage ahead.
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xbuf = lds;                                             // [2][MR][RS]
   uint32_t* szl = reinterpret_cast<uint32_t*>(lds + 2 * T::XBUF);  // [WAVES][64][KGP]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
   const int n0 = b * kBlockN;
@@ -198,12 +199,16 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   // load under a branch makes the compiler's wait counts assume it may not have been issued, and
   // every later wait then also waits for it.
   u32x4 xr[XPF][T::UPT];
-  auto x_load_one = [&](int st, int i) {
-    const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
+  uint32_t xo[T::UPT];  // element offset of unit i in x, less the stage's (t0 Q + gb G)
+#pragma unroll
+  for (int i = 0; i < T::UPT; ++i) {
     const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
     const int q = gq % T::QS, m = gq / T::QS;
-    const int mm = m < M ? m : M - 1;
-    xr[st % XPF][i] = ld16(x + (int64_t)mm * K + (t0 + q) * Q + gb * kGroup + 8 * j);
+    xo[i] = (uint32_t)((m < M ? m : M - 1) * K + q * Q + 8 * j);
+  }
+  auto x_load_one = [&](int st, int i) {
+    const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
+    xr[st % XPF][i] = ld16(x + (xo[i] + (uint32_t)(t0 * Q + gb * kGroup)));
   };
   auto x_load = [&](int st) {
 #pragma unroll
@@ -220,18 +225,21 @@ __global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kerne
   };
 
   // --- packed rows of the wave's four tiles (rows past N read row N - 1; never emitted)
-  const uint8_t* prow[kNT];
+  // (one wave-uniform base and a 32-bit offset per tile: the base stays in scalar registers)
+  const int nb = n0 < N ? n0 : N - 1;
+  const uint8_t* pbase = packed + (int64_t)nb * Q;
+  uint32_t poff[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int n = n0 + 16 * nt + col;
-    prow[nt] = packed + (int64_t)(n < N ? n : N - 1) * Q + 16 * h;
+    poff[nt] = (uint32_t)((n < N ? n : N - 1) - nb) * Q + 16 * h;
   }
   constexpr int kSlots = RPF + 1;  // spans RPF ahead of the one in use
   u32x4 ring[kSlots][kNT][2];
   // slot: the ring entry, gb % kSlots, passed separately so that it is a compile-time constant
   // wherever the span loop is not fully unrolled (a runtime index would put the ring in scratch)
   auto ring_load_one = [&](int gb, int slot, int k) {  // k = 2 nt + half
-    ring[slot][k >> 1][k & 1] = ld16(prow[k >> 1] + gb * kGroup + 64 * (k & 1));
+    ring[slot][k >> 1][k & 1] = ld16(pbase + (poff[k >> 1] + gb * kGroup + 64 * (k & 1)));
   };
   auto ring_load = [&](int gb) {
 #pragma unroll
@@ -518,8 +526,10 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
   return check_launch();
 }
 
+// up to 32 rows: workgroups of 4 waves, two per CU (measured 3-5% faster than one of 8 waves:
+// each x stage barrier waits for fewer waves)
 #ifndef I2H_TILE_WAVES
-#define I2H_TILE_WAVES 8
+#define I2H_TILE_WAVES 4
 #endif
 // 33..64 rows: 8 waves of 64 rows x 64 columns, two per SIMD (a few address registers spill to
 // scratch outside the inner loop; measured faster than 4 waves with no spills, one per SIMD)
