@@ -31,6 +31,9 @@ selection alone, with the token-level path's argmax agreement with the dense bf1
 `ablations.coarse_variants` times one coarse kernel family in four forms that differ in one
 property each (the design: group 128, quarter-split, scale on the accumulator; group 64;
 contiguous-4 bytes; dequantised weight tile) at M = 1 and 16 on cold copies, with each pack.
+`bands` times the per-call path and the coarse kernel alone at M = 16, 32, 64 on the same slice;
+`full_vocab_top16` the unsharded 248320-row vocabulary with the top-16 caller: the GPU pack of its
+bf16 weight, and one i2h_head call at each M in (1, 2, 4, 8, 16, 32, 64, 72) on cold copies.
 """
 from __future__ import annotations
 
@@ -501,6 +504,54 @@ def main():
                 res[name][f"M{Mv}_vs_design"] = round(res[name][f"M{Mv}_coarse_us"] / res["design"][f"M{Mv}_coarse_us"], 3)
         return res
 
+    def measure_full_vocab(steps, warmup):
+        """The unsharded 248320-row vocabulary with the top-16 caller: the GPU quantise+pack of the
+        bf16 weight (2.54 GB) timed on its own, then one i2h_head call (top-16 drawn from the 32
+        reranked tokens) at each M of the band list, on 6 rotated packed copies (2.1 GB)."""
+        cfg = si.WORKLOADS["full_vocab_top16_k5120_n248320"]
+        Nf, Kf, kf = cfg["N"], cfg["K"], cfg["topk"]
+        Wf = si.gen_weight(Nf, Kf).to(dev)
+        pf = i2h.pack(Wf)
+        pk = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            i2h.pack(Wf, out=pf)
+            b.record()
+            torch.cuda.synchronize()
+            pk.append(a.elapsed_time(b) * 1e3)
+        pbytes = Nf * Kf * 2 + Nf * Kf // 4 + 2 * Nf * (Kf // 128) * 2
+        cps = [pf] + [(pf[0].clone(), pf[1].clone(), pf[2].clone()) for _ in range(5)]
+        xf = si.gen_x(max(cfg["M"]), Kf, outliers=cfg["outliers"]).to(dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        s = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        L = i2h.lib()
+        rows = []
+        for Mf in cfg["M"]:
+            x = xf[:Mf].contiguous()
+            oi = torch.empty(Mf, kf, dtype=torch.int32, device=dev)
+            ov = torch.empty(Mf, kf, dtype=torch.float32, device=dev)
+            wsn = i2h.workspace_bytes(Mf, Nf, Kf, KC, R)
+            ws = torch.empty(max(wsn, 1), dtype=torch.uint8, device=dev)
+            args = [(P(x), Mf, P(p), P(S_), P(Z_), P(Wf), Wf.stride(0), Nf, Kf, KC, R, kf, P(oi), P(ov), None,
+                     P(ws), wsn, s) for (p, S_, Z_) in cps]
+            it = iter(range(1 << 30))
+            us_f = back_to_back_us(torch, lambda: L.i2h_head(*args[next(it) % len(args)]), steps, warmup)
+            hb_f = head_bytes(Mf, Nf, Kf, k=kf, own_sums=i2h.coarse_sums_x(Mf, Kf))
+            fl = 2.0 * Mf * Kf * Nf
+            rows.append(dict(M=Mf, us_per_call=round(us_f, 2), gbps=round(hb_f["total"] / us_f / 1e3, 1),
+                             hbm_frac=round(hb_f["total"] / us_f / 1e3 / HBM_PEAK_GBS, 4),
+                             tflops_useful=round(fl / us_f / 1e6, 1),
+                             mfma_util_useful=round(fl / us_f / 1e6 / BF16_PEAK_TFS, 4)))
+        res = dict(N=Nf, K=Kf, topk=kf, cold_cache_copies=len(cps),
+                   pack_us=round(float(np.median(pk)), 1),
+                   pack_gbps=round(pbytes / (float(np.median(pk)) * 1e-6) / 1e9, 1),
+                   pack_hbm_frac=round(pbytes / (float(np.median(pk)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   calls=rows)
+        del Wf, pf, cps
+        torch.cuda.synchronize()
+        return res
+
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
         res = {}
@@ -533,6 +584,11 @@ def main():
     log(f"[bench] timing the drop-in logits row at M={M}")
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
+
+    full_vocab = None
+    if not args.no_bands:
+        log("[bench] full vocabulary (248320 rows), top-16 caller: pack and one call per M")
+        full_vocab = measure_full_vocab(max(20, args.steps // 4), max(5, args.warmup // 2))
 
     bands = []
     if not args.no_bands:
@@ -620,6 +676,7 @@ def main():
                       "coarse_variants": variants},
         **result,
         "bands": bands,
+        "full_vocab_top16": full_vocab,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -538,9 +538,11 @@ bool small_sums_x(int64_t M, int64_t K) {
 }  // namespace
 
 // True when every launch coarse_launch makes for M rows of K sums the groups of x itself: the
-// small kernel with x in LDS, for M <= 4 (the many-row kernels take the sums from i2h_xsum).
+// small kernel with x in LDS, for one row, or for up to 4 rows of a K the tile kernel is not
+// built for (the tile kernels, which take the sums from i2h_xsum, are faster from 2 rows on).
 bool coarse_sums_x(int64_t M, int64_t K) {
   if (M < 1 || M > 4 || check_k(K) != I2H_OK) return false;
+  if (M > 1 && tile_supported(M, K)) return false;
   return small_sums_x(M, K);
 }
 
@@ -589,8 +591,9 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
       !aligned(cand_score, 4) || !aligned(cand_idx, 4) || (y && !aligned(y, 2)))
     return I2H_ERR_ALIGN;
   const int64_t ld = nblk_of(N) * kcand;
-  // rows go in chunks of kTileMaxRows; a chunk of at most 4 rows runs the small kernel, a larger
-  // one the tile kernel where it is built for K, else the generic kernel
+  // rows go in chunks of kTileMaxRows; a chunk of one row, or of at most 4 rows without xs or
+  // with a K the tile kernel is not built for, runs the small kernel; a larger one the tile kernel
+  // where it is built for K, else the generic kernel
   for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
     const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
     const uint16_t* xc = x + m0 * K;
@@ -599,7 +602,7 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     int32_t* cic = cand_idx + m0 * ld;
     uint16_t* yc = y ? y + m0 * N : nullptr;
     int st;
-    if (mc <= 4 && (xsc || small_sums_x(mc, K)))
+    if (mc <= 4 && (mc == 1 || !xsc || !tile_supported(mc, K)) && (xsc || small_sums_x(mc, K)))
       st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
     else if (!xsc)
       st = I2H_ERR_ARG;

@@ -60,9 +60,11 @@ def test_sizes():
 def test_coarse_sums_x():
     lib = i2h.lib()
     assert lib.i2h_coarse_sums_x(1, 5120) == 1
-    assert lib.i2h_coarse_sums_x(4, 5120) == 1
-    assert lib.i2h_coarse_sums_x(2, 512) == 1
-    assert lib.i2h_coarse_sums_x(5, 5120) == 0    # the many-row kernel takes xs from i2h_xsum
+    assert lib.i2h_coarse_sums_x(1, 1024) == 1
+    assert lib.i2h_coarse_sums_x(3, 1024) == 1    # no tile kernel for this K: the small kernel
+    assert lib.i2h_coarse_sums_x(4, 5120) == 0    # from 2 rows the tile kernel, with xs from i2h_xsum
+    assert lib.i2h_coarse_sums_x(2, 512) == 0
+    assert lib.i2h_coarse_sums_x(5, 5120) == 0
     assert lib.i2h_coarse_sums_x(16, 5120) == 0
     assert lib.i2h_coarse_sums_x(64, 5120) == 0
     assert lib.i2h_coarse_sums_x(130, 512) == 0   # chunks of 64, 64 and 2 rows

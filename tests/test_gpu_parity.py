@@ -335,7 +335,7 @@ def test_head_zero_rows(i2h):
 
 
 # ---------------------------------------------------------------------------------------------
-# full sizes: one rank's 124160-row vocab slice at M = 1, 16, 64, and the full 248320-row vocab
+# full sizes: one rank's 124160-row vocab slice at M = 1 to 64, and the full 248320-row vocab
 # ---------------------------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def slice_head():
@@ -349,7 +349,7 @@ def slice_head():
     return xb, Wb, packed_o, coarse_o
 
 
-@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("M", [1, 5, 16, 32, 40, 64])   # small kernel; 16-, 32- and 64-row tiles
 def test_vocab_slice_full_size(i2h, slice_head, M):
     xb, Wb, packed_o, coarse_o = slice_head
     say(f"vocab slice M={M}")
