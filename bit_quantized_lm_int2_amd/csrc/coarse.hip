@@ -488,18 +488,36 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
   emit_ranked(ck, M, b, N, kc, (int64_t)nblk * kc, cand_score, cand_idx);
 }
 
+// One wave per row of x: lane l sums elements 8l..8l+7 of each 512-element chunk (one 16-byte
+// load; all of a row's loads are issued before any sum), then the 16 lanes of each group of 128
+// reduce by butterfly. Rows are independent, so any M takes ceil(M / 4) workgroups.
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                    float* __restrict__ xs) {
+  constexpr int kBatch = 10;  // 512-element chunks in flight per lane (K = 5120 in one batch)
   const int KG = K / kGroup;
   const int lane = threadIdx.x & 63;
-  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (u >= M * KG) return;
-  const int m = u / KG, g = u - m * KG;
-  const uint32_t v = *reinterpret_cast<const uint32_t*>(x + (int64_t)m * K + g * kGroup + 2 * lane);
-  float s = bf16_lo(v) + bf16_hi(v);
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const uint16_t* xr = x + (int64_t)m * K;
+  const int nch = (K + 511) / 512;
+  for (int c0 = 0; c0 < nch; c0 += kBatch) {
+    u32x4 v[kBatch];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) xs[(int64_t)m * KG + g] = s;
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = (c0 + j) * 512 + 8 * lane;
+      v[j] = c0 + j < nch && e < K ? ld16(xr + e) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      float sm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm += bf16_lo(v[j][e]) + bf16_hi(v[j][e]);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
+      const int g = (c0 + j) * 4 + (lane >> 4);
+      if ((lane & 15) == 0 && c0 + j < nch && g < KG) xs[(int64_t)m * KG + g] = sm;
+    }
+  }
 }
 
 template <int MT>
@@ -575,8 +593,7 @@ int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t 
   if (M < 1 || K <= 0 || K % kGroup != 0 || K > I2H_MAX_K || M * (K / kGroup) > (int64_t)1 << 30)
     return I2H_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(xs, 4)) return I2H_ERR_ALIGN;
-  const int64_t units = M * (K / kGroup);
-  hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, x, (int)M, (int)K, xs);
+  hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, (int)M, (int)K, xs);
   return check_launch();
 }
 

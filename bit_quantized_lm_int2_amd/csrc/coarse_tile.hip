@@ -176,7 +176,7 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
 // use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
 // arrives with HBM latency; both are therefore fetched more than one stage ahead.
 template <int MT, int WAVES, int NGC, int XPF, int RPF>
-__global__ __launch_bounds__(64 * WAVES, MT <= 2 ? 2 : 1) void coarse_tile_kernel(
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,

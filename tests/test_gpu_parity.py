@@ -86,7 +86,7 @@ def test_pack_exact_grid_head(i2h):
 # ---------------------------------------------------------------------------------------------
 # xsum
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("M,K", [(1, 512), (72, 5120), (3, 16384)])
+@pytest.mark.parametrize("M,K", [(1, 512), (72, 5120), (3, 16384), (5, 640), (2, 256)])
 def test_xsum(i2h, M, K):
     xb = si.bits(si.gen_x(M, K, outliers=8, seed=3))
     xs = host(i2h.xsum(dev_bf16(xb)))
