@@ -360,22 +360,34 @@ def test_vocab_slice_full_size(i2h, slice_head, M):
     say(f"  argmax match vs oracle: {out['match']}/{out['places']}")
 
 
-def test_full_vocab_top16(i2h):
+@pytest.fixture(scope="module")
+def full_vocab_head():
     cfg = si.WORKLOADS["full_vocab_top16_k5120_n248320"]
     N, K = cfg["N"], cfg["K"]
     say("generating the 248320 x 5120 head")
     Wb = si.bits(si.gen_weight(N, K))
     xb = si.bits(si.gen_x(72, K, outliers=cfg["outliers"]))
-    rows = [0, 31, 71]
-    # the pack is checked bit-exactly on sampled vocab rows
+    say("oracle pack of the full vocabulary")
+    return xb, Wb, oracle.pack(Wb)
+
+
+def test_full_vocab_pack_sampled(i2h, full_vocab_head):
+    """The pack of the 248320-row head, bit-exact on sampled vocab rows."""
+    xb, Wb, packed_o = full_vocab_head
     p, S, ZS = i2h.pack(dev_bf16(Wb))
-    pick = np.sort(np.random.default_rng(0).choice(N, 4096, replace=False))
-    po, So, ZSo = oracle.pack(Wb[pick])
-    assert np.array_equal(host(p)[pick], po)
-    assert np.array_equal(host(S)[pick], So) and np.array_equal(host(ZS)[pick], ZSo)
-    say("oracle on sampled rows")
-    packed_o = oracle.pack(Wb)
-    out = run_and_check(i2h, xb, Wb, k=16, packed_o=packed_o, rows=rows)
+    pick = np.sort(np.random.default_rng(0).choice(Wb.shape[0], 4096, replace=False))
+    assert np.array_equal(host(p)[pick], packed_o[0][pick])
+    assert np.array_equal(host(S)[pick], packed_o[1][pick]) and np.array_equal(host(ZS)[pick], packed_o[2][pick])
+
+
+# every row count of the full-vocabulary band (each takes a different kernel or chunking: the
+# M = 1 kernel, the 16-, 32- and 64-row tiles, 64 + 8 rows); the oracle checks sampled rows
+@pytest.mark.parametrize("M,rows", [(1, [0]), (2, [1]), (8, [0, 7]), (32, [5, 31]), (64, [0, 63]),
+                                    (72, [0, 31, 71])])
+def test_full_vocab_top16(i2h, full_vocab_head, M, rows):
+    xb, Wb, packed_o = full_vocab_head
+    say(f"full vocabulary M={M}, oracle rows {rows}")
+    out = run_and_check(i2h, xb[:M], Wb, k=16, packed_o=packed_o, rows=rows)
     say(f"  top-16 match vs oracle: {out['match']}/{out['places']}")
 
 
