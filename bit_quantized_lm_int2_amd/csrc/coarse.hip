@@ -11,10 +11,10 @@
 // 64b + 16w .. +15 and every row of x (up to 16*MT rows per launch). The contraction runs on
 // v_mfma_f32_16x16x32_bf16: A = 16 rows of x, B = 16 columns of dequantised weights, and lane
 // (col = l & 15, h = l >> 4) feeds column col with k-slots 8h .. 8h+7. A lane streams 32
-// consecutive packed bytes of its row per 128-byte span (two 16-byte loads); the 8 bytes of
-// slice s serve all four quarters t, i.e. the k-slots t*Q + 128 gb + 32h + 8s + (0..7) of four
-// different quantisation groups, each with its own MFMA accumulator that is scaled and folded
-// into the result once the group is complete. A byte permute puts bytes (0,2,1,3) of each
+// packed bytes of its row per 128-byte span (two 16-byte loads; the M <= 4 kernel takes bytes
+// 16h and 64 + 16h, whole 64-byte sectors per load); the 8 bytes of slice s serve all four
+// quarters t, i.e. four different quantisation groups, each with its own MFMA accumulator that
+// is scaled and folded into the result once the group is complete. A byte permute puts bytes (0,2,1,3) of each
 // dword in place so that the bit-pattern dequant yields bf16 pairs in natural k order, which
 // lets the x fragment be one contiguous 16-byte load.
 #include "dequant.h"
@@ -195,6 +195,13 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 #define I2H_COARSE_PF 4
 #endif
 constexpr int kPf = I2H_COARSE_PF;
+// Packed bytes per lane and span: 1 = aligned 64-byte sectors (lane h takes bytes 16h and
+// 64 + 16h, so each load instruction reads whole sectors), 0 = 32 consecutive bytes at 32h.
+#ifndef I2H_SMALL_SECTOR
+#define I2H_SMALL_SECTOR 1
+#endif
+constexpr int kLaneOff = I2H_SMALL_SECTOR ? 16 : 32;  // byte offset of lane h's first load
+constexpr int kHalfOff = I2H_SMALL_SECTOR ? 64 : 16;  // byte offset of its second load
 #ifndef I2H_COARSE_SLICE_FENCE
 #define I2H_COARSE_SLICE_FENCE 1
 #endif  // 128-byte spans of the packed stream in flight per lane
@@ -302,13 +309,13 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       }
     }
   }
-  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + 32 * h;
+  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + kLaneOff * h;
   u32x4 ring[kPf][2];
 #pragma unroll
   for (int p = 0; p < kPf; ++p) {
     const int g = p < NG ? p : NG - 1;
     ring[p][0] = ld16(prow + g * kGroup);
-    ring[p][1] = ld16(prow + g * kGroup + 16);
+    ring[p][1] = ld16(prow + g * kGroup + kHalfOff);
   }
 
   // x rows in LDS, laid out by span: xl[m][gb][t][j] holds x[m][t Q + 128 gb + j], so the four
@@ -408,7 +415,9 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     f32x4 p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint16_t* xa = XLDS ? xl + arow * K + gb * 512 + 32 * h : x + (int64_t)arow * K + gb * kGroup + 32 * h;
+    const uint16_t* xa = XLDS ? xl + arow * K + gb * 512 + kLaneOff * h : x + (int64_t)arow * K + gb * kGroup + kLaneOff * h;
+    // k offset of slice s within lane h's part of the group
+    auto soff = [](int s_) { return I2H_SMALL_SECTOR ? 8 * (s_ & 1) + 64 * (s_ >> 1) : 8 * s_; };
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -420,8 +429,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
         else if (t == 2) bw = dequant8_mask<2>(d0, d1, h0, h1, dqc);
         else bw = dequant8_mask<3>(d0, d1, h0, h1, dqc);
         u32x4 a;
-        if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xa + t * kGroup + 8 * s);
-        else a = ld16(xa + t * Q + 8 * s);
+        if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xa + t * kGroup + soff(s));
+        else a = ld16(xa + t * Q + soff(s));
         p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
       }
 #if I2H_COARSE_SLICE_FENCE
@@ -455,7 +464,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       body(gb, ring[gb % kPf][0], ring[gb % kPf][1]);
       if (gb + kPf < NGC) {
         ring[gb % kPf][0] = ld16(prow + (gb + kPf) * kGroup);
-        ring[gb % kPf][1] = ld16(prow + (gb + kPf) * kGroup + 16);
+        ring[gb % kPf][1] = ld16(prow + (gb + kPf) * kGroup + kHalfOff);
       }
     }
   } else {
@@ -467,7 +476,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
           body(gb, ring[p][0], ring[p][1]);
           const int nx = gb + kPf < NG ? gb + kPf : NG - 1;
           ring[p][0] = ld16(prow + nx * kGroup);
-          ring[p][1] = ld16(prow + nx * kGroup + 16);
+          ring[p][1] = ld16(prow + nx * kGroup + kHalfOff);
         }
       }
     }
