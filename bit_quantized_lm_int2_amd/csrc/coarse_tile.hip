@@ -174,7 +174,7 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
 // sums).
 // XPF: x stages loaded ahead of the one being stored; RPF: packed spans loaded ahead of the one in
 // use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
-// arrives with HBM latency; both are therefore fetched more than one stage ahead.
+// arrives with HBM latency: within a stage x is therefore issued before the packed span.
 template <int MT, int WAVES, int NGC, int XPF, int RPF>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
@@ -245,8 +245,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 #pragma unroll
     for (int k = 0; k < 2 * kNT; ++k) ring_load_one(gb, gb % kSlots, k);
   };
-  // The loads stage st issues for later stages, in this order: x stage st + XPF (UPT units and the
-  // group sums), then, at the first stage of span gb, the packed span gb + RPF. They are spread
+  // The loads stage st issues for later stages, in this order: x stage st + XPF (UPT units), then,
+  // at the first stage of span gb, the packed span gb + RPF. They are spread
   // over the stage's MFMA slices: issued as one burst, they stall the wave at issue while the
   // memory pipeline drains, with the current stage's operands already in registers.
   constexpr int kStageLoads = T::UPT + 2 * kNT;
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     emit_counted<T::MR>(tw, M, b, N, kc, ld, cand_score, cand_idx);
 }
 
-// Loads ahead: x one stage, the packed stream one span (measured best for the 16-row tile).
+// Loads ahead: x one stage, the packed stream one span (measured best at 16, 32 and 64 rows).
 #ifndef I2H_TILE_XPF
 #define I2H_TILE_XPF 1
 #endif
