@@ -14,7 +14,8 @@ steps rotate over COPIES independent copies of it (2.1 GB) and every step reads 
 HBM. The quantise+pack of the bf16 weight is a load-time step and is timed on its own.
 
 Prints one JSON line. `value` is the head's algorithmic HBM bytes per call divided by the
-measured time per call (GB/s); `us_per_call` is the same time. `roofline` covers the coarse
+measured time per call (GB/s); `us_per_call` is the same time. `us_per_call_graph` is the same
+call (i2h_head) replayed from a HIP graph holding one call per cold copy. `roofline` covers the coarse
 kernel, the dominant one, timed with HIP events on the launch stream over the timed region.
 `cpu_baseline` times the oracle (test infrastructure, CPU) on the same workload.
 `dropin_logits` times the drop-in logits row at the same M: coarse pass with its bf16 row, the
@@ -349,6 +350,45 @@ def main():
         torch.cuda.synchronize()
         return h, dt, coarse_ms, dt_fused
 
+    def measure_graph(Mg, reps):
+        """Per-call µs of i2h_head replayed from a HIP graph that holds one call per cold copy (the
+        library allocates, clears and synchronises nothing, so the whole call is captured); the
+        first replay's outputs are checked against eager calls."""
+        x = x_all[:Mg].contiguous()
+        ws = torch.empty(i2h.workspace_bytes(Mg, N, K, KC, R), dtype=torch.uint8, device=dev)
+        outs = [(torch.empty(Mg, 1, dtype=torch.int32, device=dev), torch.empty(Mg, 1, dtype=torch.float32, device=dev))
+                for _ in copies]
+        eager = [i2h.head(x, p_, S_, Z_, W, kcand=KC, R=R, k=1) for (p_, S_, Z_) in copies]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for (p_, S_, Z_), o in zip(copies, outs):
+                i2h.head(x, p_, S_, Z_, W, kcand=KC, R=R, k=1, workspace=ws, out=o)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for (p_, S_, Z_), o in zip(copies, outs):
+                i2h.head(x, p_, S_, Z_, W, kcand=KC, R=R, k=1, workspace=ws, out=o)
+        for o in outs:
+            o[0].fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        for (ei, ev), (oi, ov) in zip(eager, outs):
+            if not (torch.equal(ei, oi) and torch.equal(ev, ov)):
+                raise RuntimeError("graph replay differs from the eager call")
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) * 1e3 / (reps * len(copies))
+
     def measure_fp8(h, steps, warmup):
         """The FP8 e4m3 per-row-scale source (the same weights in FP8): its load-time pack, and the
         fused tail (selection, exact rerank against the FP8 rows, argmax) beside the bf16 one, each
@@ -568,6 +608,8 @@ def main():
     log(f"[bench] timing M={M}: {args.warmup} warmup + {args.steps} steps")
     h, dt, coarse_ms, dt_fused = measure(M, args.steps, args.warmup)
     hb = head_bytes(M, N, K, own_sums=h.own_sums)
+    log(f"[bench] i2h_head replayed from a HIP graph at M={M}")
+    us_graph = measure_graph(M, max(10, args.steps // 12))
     us = dt * 1e6
     coarse_us = coarse_ms * 1e3
     achieved = hb["coarse"] / (coarse_us * 1e-6) / 1e9
@@ -598,6 +640,7 @@ def main():
             hbb = head_bytes(Mb, N, K, own_sums=hbh.own_sums)
             flops = 2.0 * Mb * K * N
             bands.append(dict(M=Mb, us_per_call=round(dtb * 1e6, 2), us_per_call_fused=round(dtfb * 1e6, 2),
+                              us_per_call_graph=round(measure_graph(Mb, max(10, args.steps // 24)), 2),
                               coarse_us=round(cmsb * 1e3, 2),
                               gbps=round(hbb["total"] / dtb / 1e9, 1),
                               coarse_gbps=round(hbb["coarse"] / (cmsb * 1e-3) / 1e9, 1),
@@ -660,6 +703,7 @@ def main():
                    "cold_cache_copies": COPIES, "group": 128, "block_n": 64},
         "us_per_call": round(us, 2),
         "us_per_call_fused_entry": round(dt_fused * 1e6, 2),
+        "us_per_call_graph": round(us_graph, 2),
         "bytes_per_call": hb["total"],
         "gbps_packed_only": round(N * K / 4 / dt / 1e9, 1),
         "hbm_frac": round(hb["total"] / dt / 1e9 / HBM_PEAK_GBS, 4),

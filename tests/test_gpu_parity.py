@@ -322,6 +322,39 @@ def test_head_parity(i2h, M, N, K, kc, R, k):
     run_and_check(i2h, xb, Wb, kc=kc, R=R, k=k)
 
 
+@pytest.mark.parametrize("M,N,K,k", [(1, 4133, 5120, 1), (16, 4133, 5120, 16), (40, 2000, 512, 4)])
+def test_head_graph_replay(i2h, M, N, K, k):
+    """i2h_head captured in a HIP graph (the library allocates, clears and synchronises nothing):
+    three replays, with eager work and a synchronisation between them, each give the eager result
+    bit for bit."""
+    say(f"graph replay M={M} N={N} K={K} k={k}")
+    xb = si.bits(si.gen_x(M, K, outliers=8 if K >= 1024 else 0, seed=M + 7))
+    Wb = si.bits(si.gen_weight(N, K, seed=N + 3))
+    x, W = dev_bf16(xb), dev_bf16(Wb)
+    p, S, ZS = i2h.pack(W)
+    ws = torch.empty(i2h.workspace_bytes(M, N, K, 8, 32), dtype=torch.uint8, device=DEV)
+    oi = torch.empty(M, k, dtype=torch.int32, device=DEV)
+    ov = torch.empty(M, k, dtype=torch.float32, device=DEV)
+    ei, ev = i2h.head(x, p, S, ZS, W, k=k)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        i2h.head(x, p, S, ZS, W, k=k, workspace=ws, out=(oi, ov))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        i2h.head(x, p, S, ZS, W, k=k, workspace=ws, out=(oi, ov))
+    for r in range(3):
+        oi.fill_(-7)
+        ov.fill_(0.0)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(oi, ei) and torch.equal(ov, ev), f"replay {r} differs from the eager call"
+
+
 def test_head_zero_rows(i2h):
     """x rows of zeros: every score ties, the tie rules decide (lowest indices win)."""
     K, N = 512, 4096
