@@ -14,8 +14,10 @@ steps rotate over COPIES independent copies of it (2.1 GB) and every step reads 
 HBM. The quantise+pack of the bf16 weight is a load-time step and is timed on its own.
 
 Prints one JSON line. `value` is the head's algorithmic HBM bytes per call divided by the
-measured time per call (GB/s); `us_per_call` is the same time. `us_per_call_graph` is the same
-call (i2h_head) replayed from a HIP graph holding one call per cold copy. `roofline` covers the coarse
+measured time per call (GB/s); `us_per_call` is the same time, `us_per_call_p10_p50_p90` its
+spread over single calls (HIP events between calls). `us_per_call_graph` is the same call
+(i2h_head) replayed from a HIP graph holding one call per cold copy. `device` names the GPU, the
+HIP version and the compute-unit count. `roofline` covers the coarse
 kernel, the dominant one, timed with HIP events on the launch stream over the timed region.
 `cpu_baseline` times the oracle (test infrastructure, CPU) on the same workload.
 `dropin_logits` times the drop-in logits row at the same M: coarse pass with its bf16 row, the
@@ -252,6 +254,26 @@ def time_steps(torch, fn, steps, warmup, events=False):
     if events:
         coarse_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     return dt, coarse_ms
+
+
+def call_percentiles(torch, np, fn, n, first):
+    """(p10, p50, p90) µs of n consecutive calls of fn(i) (each enqueues one call), from a chain of
+    HIP events between calls on the current stream (each interval holds one whole call)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n):
+        fn(first + i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    d = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
+    return [round(float(v), 2) for v in np.percentile(d, [10, 50, 90])]
+
+
+def device_info(torch):
+    """GPU name and HIP runtime version."""
+    return {"name": torch.cuda.get_device_name(0), "hip": torch.version.hip,
+            "compute_units": torch.cuda.get_device_properties(0).multi_processor_count}
 
 
 def to_dev_bits(torch, np, b, dev):
@@ -608,6 +630,7 @@ def main():
     log(f"[bench] timing M={M}: {args.warmup} warmup + {args.steps} steps")
     h, dt, coarse_ms, dt_fused = measure(M, args.steps, args.warmup)
     hb = head_bytes(M, N, K, own_sums=h.own_sums)
+    pct = call_percentiles(torch, np, h.step, args.steps, args.warmup + args.steps)
     log(f"[bench] i2h_head replayed from a HIP graph at M={M}")
     us_graph = measure_graph(M, max(10, args.steps // 12))
     us = dt * 1e6
@@ -704,6 +727,7 @@ def main():
         "us_per_call": round(us, 2),
         "us_per_call_fused_entry": round(dt_fused * 1e6, 2),
         "us_per_call_graph": round(us_graph, 2),
+        "us_per_call_p10_p50_p90": pct,
         "bytes_per_call": hb["total"],
         "gbps_packed_only": round(N * K / 4 / dt / 1e9, 1),
         "hbm_frac": round(hb["total"] / dt / 1e9 / HBM_PEAK_GBS, 4),
@@ -721,6 +745,7 @@ def main():
         **result,
         "bands": bands,
         "full_vocab_top16": full_vocab,
+        "device": device_info(torch),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
