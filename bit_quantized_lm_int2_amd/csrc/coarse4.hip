@@ -9,9 +9,11 @@
 // first half and group KG/2 + gb of the second, each through 4 MFMAs (16x16x32 bf16) per m-tile.
 //
 // One 4-wave workgroup per 64-column block; lane (col = l & 15, h = l >> 4) streams bytes
-// 32 h .. 32 h + 31 of each span of its row, kC4Pf spans ahead (with its x fragments when one
-// m-tile covers the rows; x comes from L2), and the emit ranks the block's columns with a wave
-// bitonic sort (any kcand <= 64).
+// 32 h .. 32 h + 31 of each span of its row. When x is small (up to 32 KB: M <= 3 at K = 5120) it
+// is staged in LDS once per workgroup and two spans of packed bytes and scales are in flight per
+// lane; otherwise one span is, with the lane's x fragments when one m-tile covers the rows (x
+// then comes from L2). The emit ranks the block's columns with a wave bitonic sort (any
+// kcand <= 64).
 #include "dequant.h"
 #include "host_util.h"
 #include "wave_sort.h"
@@ -24,6 +26,14 @@ constexpr int kC4Threads = 256;
 #define I2H_C4_PF 1
 #endif
 constexpr int kC4Pf = I2H_C4_PF;  // spans of packed bytes (and x) in flight per lane
+#ifndef I2H_C4_PF_XL
+#define I2H_C4_PF_XL 2
+#endif
+constexpr int kC4PfXl = I2H_C4_PF_XL;  // spans in flight when x sits in LDS
+#ifndef I2H_C4_XL_BYTES
+#define I2H_C4_XL_BYTES 32768
+#endif
+constexpr size_t kC4XlBytes = I2H_C4_XL_BYTES;  // largest x staged in LDS (M = 3 at K = 5120)
 
 // Bytes [b0 b1 b2 b3] -> [b0 b2 b1 b3], so that one mask takes the nibbles of b0 and b1 (then b2
 // and b3) into the two bf16 halves of a dword.
@@ -83,7 +93,9 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
   }
 }
 
-template <int MT>
+// XL: x (at most kC4XlBytes) is staged in LDS once per workgroup and the fragments are read from
+// there, so a ring slot holds only the packed bytes and the scales and PF slots fit in registers.
+template <int MT, bool XL, int PF>
 __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ xs,
                                                              int M, const uint8_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ S,
@@ -95,6 +107,7 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   const int H = K >> 1, NS = H / kGroup, KG = K / kGroup;
   float* xsT = smem;             // [KG][MR]: xs transposed, zero past row M
   float* cbuf = smem + KG * MR;  // [MR][64]: the block's logits for the emit
+  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + MR * kBlockN);  // [M][K] when XL
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x;
@@ -106,6 +119,9 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
     const int g = i / MR, m = i - g * MR;
     xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
   }
+  if constexpr (XL)
+    for (int u = tid; u < M * K / 8; u += kC4Threads)
+      *reinterpret_cast<u32x4*>(xl + 8 * u) = ld16(x + 8 * u);
   __syncthreads();
 
   f32x4 acc[MT];
@@ -118,7 +134,7 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   // a ring of kC4Pf spans in flight: the packed bytes and the two groups' S / ZS (rows past N
   // read row 0, never stored) and, for one m-tile, the lane's x fragments of both halves (rows
   // past M read row 0, unused)
-  constexpr int kXF = MT == 1 ? 8 : 1;
+  constexpr int kXF = MT == 1 && !XL ? 8 : 1;
   const int xrow = MT == 1 ? (col < M ? col : 0) : 0;
   struct Slot {
     u32x4 p0, p1;
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
     sl.z0 = zrow[gb];
     sl.s1 = srow[KG / 2 + gb];
     sl.z1 = zrow[KG / 2 + gb];
-    if constexpr (MT == 1) {
+    if constexpr (MT == 1 && !XL) {
       const uint16_t* xq = xh + (int64_t)xrow * K + gb * kGroup;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -150,20 +166,32 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
     }
     const uint16_t* xg = xh + gb * kGroup;
     const int g0 = gb, g1 = KG / 2 + gb;
-    half4<MT, 0>(acc, dw, sl.xa, xg, M, K, col, bf16_lo(sl.s0), bf16_lo(sl.z0), xsT + g0 * MR, h);
-    half4<MT, 1>(acc, dw, sl.xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(sl.s1), bf16_lo(sl.z1),
+    const u32x4* xa = sl.xa;
+    u32x4 xv[8];
+    if constexpr (XL) {
+      // the lane's x fragments of this span, from LDS
+      const uint16_t* xq = xl + xrow * K + gb * kGroup + 32 * h;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        xv[s] = *reinterpret_cast<const u32x4*>(xq + 8 * s);
+        xv[4 + s] = *reinterpret_cast<const u32x4*>(xq + H + 8 * s);
+      }
+      xa = xv;
+    }
+    half4<MT, 0>(acc, dw, xa, xg, M, K, col, bf16_lo(sl.s0), bf16_lo(sl.z0), xsT + g0 * MR, h);
+    half4<MT, 1>(acc, dw, xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(sl.s1), bf16_lo(sl.z1),
                  xsT + g1 * MR, h);
   };
-  Slot ring[kC4Pf];
+  Slot ring[PF];
 #pragma unroll
-  for (int q = 0; q < kC4Pf; ++q) fetch(ring[q], q < NS ? q : NS - 1);
-  for (int gb0 = 0; gb0 < NS; gb0 += kC4Pf) {
+  for (int q = 0; q < PF; ++q) fetch(ring[q], q < NS ? q : NS - 1);
+  for (int gb0 = 0; gb0 < NS; gb0 += PF) {
 #pragma unroll
-    for (int q = 0; q < kC4Pf; ++q) {
+    for (int q = 0; q < PF; ++q) {
       const int gb = gb0 + q;
       if (gb < NS) {
         body(ring[q], gb);
-        const int nx = gb + kC4Pf;
+        const int nx = gb + PF;
         fetch(ring[q], nx < NS ? nx : NS - 1);
       }
     }
@@ -205,8 +233,16 @@ template <int MT>
 void launch4(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S, const uint16_t* ZS,
              int N, int K, int kc, int nblk, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
   const size_t lds = ((size_t)(K / kGroup) * 16 * MT + (size_t)16 * MT * kBlockN) * sizeof(float);
-  hipLaunchKernelGGL((coarse4_kernel<MT>), dim3((unsigned)nblk), dim3(kC4Threads), lds, s, x, xs, M, packed, S, ZS, N,
-                     K, kc, nblk, cs, ci, y);
+  const size_t xbytes = (size_t)M * K * 2;
+  if constexpr (MT == 1) {
+    if (xbytes <= kC4XlBytes) {
+      hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl>), dim3((unsigned)nblk), dim3(kC4Threads), lds + xbytes, s,
+                         x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((coarse4_kernel<MT, false, kC4Pf>), dim3((unsigned)nblk), dim3(kC4Threads), lds, s, x, xs, M,
+                     packed, S, ZS, N, K, kc, nblk, cs, ci, y);
 }
 
 }  // namespace
