@@ -17,7 +17,8 @@ Prints one JSON line. `value` is the head's algorithmic HBM bytes per call divid
 measured time per call (GB/s); `us_per_call` is the same time, `us_per_call_p10_p50_p90` its
 spread over single calls (HIP events between calls). `us_per_call_graph` is the same call
 (i2h_head) replayed from a HIP graph holding one call per cold copy. `device` names the GPU, the
-HIP version and the compute-unit count. `roofline` covers the coarse
+HIP version and the compute-unit count; `roofline.copy_gbps_measured` is torch's device copy over
+512 MiB on the same box (read + write), the practical HBM rate beside the 8 TB/s peak. `roofline` covers the coarse
 kernel, the dominant one, timed with HIP events on the launch stream over the timed region.
 `cpu_baseline` times the oracle (test infrastructure, CPU) on the same workload.
 `dropin_logits` times the drop-in logits row at the same M: coarse pass with its bf16 row, the
@@ -268,6 +269,26 @@ def call_percentiles(torch, np, fn, n, first):
     torch.cuda.synchronize()
     d = np.array([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(n)])
     return [round(float(v), 2) for v in np.percentile(d, [10, 50, 90])]
+
+
+def copy_gbps(torch, dev, nbytes=512 << 20, reps=10):
+    """Device-to-device copy bandwidth (bytes read + written per second, GB/s) of torch's copy
+    kernel over a 512 MiB buffer: the box's practical HBM rate, for context beside the 8 TB/s
+    peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    del src, dst
+    return round(2 * nbytes / us / 1e3, 1)
 
 
 def device_info(torch):
@@ -733,6 +754,7 @@ def main():
         "hbm_frac": round(hb["total"] / dt / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "copy_gbps_measured": copy_gbps(torch, dev),
                      "kernel": "coarse_small_kernel<1, true, 10>", "kernel_us": round(coarse_us, 2),
                      "algorithmic_bytes": hb["coarse"]},
         "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
