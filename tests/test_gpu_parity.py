@@ -314,6 +314,9 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (16, 130, 5120, 8, 16, 1),     # three blocks: one workgroup with an idle wave
     (24, 3001, 5120, 12, 64, 16),  # 32-row tile; kcand above 8 (counted emit)
     (40, 1000, 512, 3, 16, 4),     # 64-row tile, three candidates per block
+    (4, 1037, 5120, 8, 32, 16),    # 2-4 rows through the 16-row tile (with i2h_xsum), ragged tail
+    (65, 1000, 5120, 8, 32, 1),    # a 64-row launch and a 1-row chunk on the M = 1 kernel with xs
+    (33, 643, 5120, 8, 32, 16),    # 64-row tile with one row of its last m-tile, tail block
 ])
 def test_head_parity(i2h, M, N, K, kc, R, k):
     say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
