@@ -317,6 +317,9 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (4, 1037, 5120, 8, 32, 16),    # 2-4 rows through the 16-row tile (with i2h_xsum), ragged tail
     (65, 1000, 5120, 8, 32, 1),    # a 64-row launch and a 1-row chunk on the M = 1 kernel with xs
     (33, 643, 5120, 8, 32, 16),    # 64-row tile with one row of its last m-tile, tail block
+    (1, 1, 512, 8, 32, 1),         # a one-token vocabulary: one valid candidate
+    (5, 63, 512, 8, 8, 4),         # one partial block
+    (40, 65, 5120, 8, 16, 16),     # nine valid candidates for R = 16: empty places in the top-16
 ])
 def test_head_parity(i2h, M, N, K, kc, R, k):
     say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
