@@ -562,15 +562,25 @@ int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, 
 
 }  // namespace
 
-bool tile_supported(int64_t M, int64_t K) { return M >= 1 && M <= kTileMaxRows && (K == 512 || K == 5120); }
+// K of the head's family the tile kernel is built for (the span loop is unrolled at compile time)
+bool tile_supported(int64_t M, int64_t K) {
+  return M >= 1 && M <= kTileMaxRows &&
+         (K == 512 || K == 1024 || K == 2048 || K == 3072 || K == 4096 || K == 5120);
+}
 
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
                 hipStream_t s) {
   if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
   if (!xs) return I2H_ERR_ARG;
-  if (K == 5120) return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-  return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+  switch (K / 512) {
+    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+  }
 }
 
 }  // namespace i2h

@@ -61,7 +61,8 @@ def test_coarse_sums_x():
     lib = i2h.lib()
     assert lib.i2h_coarse_sums_x(1, 5120) == 1
     assert lib.i2h_coarse_sums_x(1, 1024) == 1
-    assert lib.i2h_coarse_sums_x(3, 1024) == 1    # no tile kernel for this K: the small kernel
+    assert lib.i2h_coarse_sums_x(3, 1536) == 1    # no tile kernel for this K: the small kernel
+    assert lib.i2h_coarse_sums_x(3, 4096) == 0    # the 16-row tile is built for K = 4096
     assert lib.i2h_coarse_sums_x(4, 5120) == 0    # from 2 rows the tile kernel, with xs from i2h_xsum
     assert lib.i2h_coarse_sums_x(2, 512) == 0
     assert lib.i2h_coarse_sums_x(5, 5120) == 0

@@ -320,6 +320,11 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (1, 1, 512, 8, 32, 1),         # a one-token vocabulary: one valid candidate
     (5, 63, 512, 8, 8, 4),         # one partial block
     (40, 65, 5120, 8, 16, 16),     # nine valid candidates for R = 16: empty places in the top-16
+    (16, 3001, 4096, 8, 32, 1),    # tiles built for other K of the family: 16, 32 and 64 rows
+    (24, 2000, 3072, 8, 32, 16),
+    (50, 1500, 2048, 8, 32, 4),
+    (3, 1100, 1024, 8, 32, 1),
+    (2, 700, 1536, 8, 32, 1),      # a K with no tile: the small kernel for up to 4 rows
 ])
 def test_head_parity(i2h, M, N, K, kc, R, k):
     say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
