@@ -17,6 +17,8 @@
 // is scaled and folded into the result once the group is complete. A byte permute puts bytes (0,2,1,3) of each
 // dword in place so that the bit-pattern dequant yields bf16 pairs in natural k order, which
 // lets the x fragment be one contiguous 16-byte load.
+#include <type_traits>
+
 #include "dequant.h"
 #include "host_util.h"
 
@@ -545,15 +547,20 @@ int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packe
                  const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
-  if (K == 5120)
-    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 10>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
-                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
-  else if (K == 512)
-    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 1>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
-                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
-  else
-    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, 0>), dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M,
-                       packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  // the span loop unrolled for the K of the head's family, a run-time loop otherwise
+  auto go = [&](auto ngc) {
+    hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, decltype(ngc)::value>), dim3(nblk), dim3(kCoarseThreads), lds,
+                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+  };
+  switch (K) {
+    case 5120: go(std::integral_constant<int, 10>{}); break;
+    case 4096: go(std::integral_constant<int, 8>{}); break;
+    case 3072: go(std::integral_constant<int, 6>{}); break;
+    case 2048: go(std::integral_constant<int, 4>{}); break;
+    case 1024: go(std::integral_constant<int, 2>{}); break;
+    case 512: go(std::integral_constant<int, 1>{}); break;
+    default: go(std::integral_constant<int, 0>{}); break;
+  }
   return check_launch();
 }
 

@@ -325,6 +325,10 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (50, 1500, 2048, 8, 32, 4),
     (3, 1100, 1024, 8, 32, 1),
     (2, 700, 1536, 8, 32, 1),      # a K with no tile: the small kernel for up to 4 rows
+    (1, 2001, 4096, 8, 32, 1),     # the M = 1 kernel unrolled for other K of the family
+    (1, 1999, 3072, 8, 32, 16),
+    (1, 777, 2048, 8, 32, 1),
+    (1, 640, 1024, 8, 32, 1),
 ])
 def test_head_parity(i2h, M, N, K, kc, R, k):
     say(f"head M={M} N={N} K={K} kc={kc} R={R} k={k}")
