@@ -257,8 +257,10 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
   constexpr int RR = MAXR < 4 ? MAXR : 4;  // accumulator rows per lane that can be real
+  // zc (may be null): one int per row, set to 0 (the arrival counters of the head's tail)
+  if (zc != nullptr && blockIdx.x == 0 && (int)threadIdx.x < M) zc[threadIdx.x] = 0;
   extern __shared__ __align__(16) uint32_t lds[];
   if constexpr (NGC > 0) K = NGC * 512;
   const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / kGroup;
@@ -502,13 +504,15 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
 // One wave per row of x: lane l sums elements 8l..8l+7 of each 512-element chunk (one 16-byte
 // load; all of a row's loads are issued before any sum), then the 16 lanes of each group of 128
 // reduce by butterfly. Rows are independent, so any M takes ceil(M / 4) workgroups.
+// zc (may be null): one int per row, set to 0 here (the arrival counters of the head's tail).
 __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ x, int M, int K,
-                                                   float* __restrict__ xs) {
+                                                   float* __restrict__ xs, int32_t* __restrict__ zc) {
   constexpr int kBatch = 10;  // 512-element chunks in flight per lane (K = 5120 in one batch)
   const int KG = K / kGroup;
   const int lane = threadIdx.x & 63;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;
+  if (zc != nullptr && lane == 0) zc[m] = 0;
   const uint16_t* xr = x + (int64_t)m * K;
   const int nch = (K + 511) / 512;
   for (int c0 = 0; c0 < nch; c0 += kBatch) {
@@ -544,13 +548,14 @@ int launch_coarse(const uint16_t* x, const float* xs, int M, const uint8_t* pack
 
 template <int MAXR, bool XLDS>
 int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
+                 hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
   // the span loop unrolled for the K of the head's family, a run-time loop otherwise
   auto go = [&](auto ngc) {
     hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, decltype(ngc)::value>), dim3(nblk), dim3(kCoarseThreads), lds,
-                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y, zc);
   };
   switch (K) {
     case 5120: go(std::integral_constant<int, 10>{}); break;
@@ -584,12 +589,13 @@ namespace {
 
 // M <= 4 rows.
 int small_band(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-               const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+               const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
+               hipStream_t s) {
   if (M == 1 && small_lds_bytes(K, 1) <= 65536)
-    return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+    return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
   if (M <= 4 && small_lds_bytes(K, 4) <= 65536)
-    return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
-  return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+    return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
+  return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
 }
 
 // The generic kernel (global A loads, any K) for up to kTileMaxRows rows; needs xs.
@@ -603,19 +609,20 @@ int generic_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packe
 
 }  // namespace
 
-int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s) {
+int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s, int32_t* zero_cnt) {
   if (!x || !xs) return I2H_ERR_ARG;
   // whole groups suffice here (the int4 head allows K a multiple of 256)
   if (M < 1 || K <= 0 || K % kGroup != 0 || K > I2H_MAX_K || M * (K / kGroup) > (int64_t)1 << 30)
     return I2H_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(xs, 4)) return I2H_ERR_ALIGN;
-  hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, (int)M, (int)K, xs);
+  if (zero_cnt && !aligned(zero_cnt, 4)) return I2H_ERR_ALIGN;
+  hipLaunchKernelGGL(xsum_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, s, x, (int)M, (int)K, xs, zero_cnt);
   return check_launch();
 }
 
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                   const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
-                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s) {
+                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s, int32_t* zero_cnt) {
   if (!x || !packed || !S || !ZS || !cand_score || !cand_idx) return I2H_ERR_ARG;
   if (!xs && !coarse_sums_x(M, K)) return I2H_ERR_ARG;  // in-kernel group sums need x in LDS
   if (M < 1 || N < 1 || N > ((int64_t)1 << 30) || check_k(K) != I2H_OK) return I2H_ERR_SHAPE;
@@ -623,6 +630,8 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(xs, 4) || !aligned(S, 16) || !aligned(ZS, 16) ||
       !aligned(cand_score, 4) || !aligned(cand_idx, 4) || (y && !aligned(y, 2)))
     return I2H_ERR_ALIGN;
+  // only the small kernel zeroes counters: the caller passes them when every row runs there
+  if (zero_cnt && (xs || !coarse_sums_x(M, K) || !aligned(zero_cnt, 4))) return I2H_ERR_ARG;
   const int64_t ld = nblk_of(N) * kcand;
   // rows go in chunks of kTileMaxRows; a chunk of one row, or of at most 4 rows without xs or
   // with a K the tile kernel is not built for, runs the small kernel; a larger one the tile kernel
@@ -636,7 +645,8 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     uint16_t* yc = y ? y + m0 * N : nullptr;
     int st;
     if (mc <= 4 && (mc == 1 || !xsc || !tile_supported(mc, K)) && (xsc || small_sums_x(mc, K)))
-      st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+      st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc,
+                      zero_cnt ? zero_cnt + m0 : nullptr, s);
     else if (!xsc)
       st = I2H_ERR_ARG;
     else if (tile_supported(mc, K))

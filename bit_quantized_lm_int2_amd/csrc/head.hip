@@ -2,7 +2,10 @@
 //
 // radiance_drafthead.py, _apply_head_int2: group sums of x, the coarse int2 pass with its block
 // candidates, the top-R selection, the exact rerank and the caller's argmax or top-k, in
-// stream order with no host synchronisation.
+// stream order with no host synchronisation. The fused tail splits each row over several
+// workgroups; their per-row arrival counters live in the workspace and are zeroed by the head's
+// first kernel (the group sums, or the small coarse kernel when it sums x itself), so a call
+// clears nothing from the host and captures into a graph as it stands.
 #include "device_util.h"
 #include "host_util.h"
 
@@ -15,7 +18,7 @@ constexpr int64_t kAlign = 256;
 int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Workspace {
-  int64_t xs, cand_score, cand_idx, sel, exact, total;
+  int64_t xs, cand_score, cand_idx, sel, exact, cnt, total;
 };
 
 Workspace layout(int64_t M, int64_t N, int64_t K, int kcand, int R) {
@@ -26,7 +29,8 @@ Workspace layout(int64_t M, int64_t N, int64_t K, int kcand, int R) {
   w.cand_idx = up(w.cand_score + M * ncand * 4);
   w.sel = up(w.cand_idx + M * ncand * 4);
   w.exact = up(w.sel + M * (int64_t)R * 4);
-  w.total = up(w.exact + M * (int64_t)R * 4);
+  w.cnt = up(w.exact + M * (int64_t)R * 4);
+  w.total = up(w.cnt + M * 4);
   return w;
 }
 
@@ -86,15 +90,20 @@ extern "C" int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, con
   int32_t* ci = reinterpret_cast<int32_t*>(base + w.cand_idx);
   int32_t* sel = reinterpret_cast<int32_t*>(base + w.sel);
   float* ex = reinterpret_cast<float*>(base + w.exact);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt);
   hipStream_t s = (hipStream_t)stream;
+  const bool fused = select_rerank_supported(nblk_of(N), kcand, R, N, K);
+  const int G = fused ? select_rerank_split(M, R) : 1;
+  int32_t* zc = G > 1 ? cnt : nullptr;
   // for a few rows the coarse kernel holds x in LDS and sums its groups itself
   const bool own_sums = coarse_sums_x(M, K);
-  int st = own_sums ? I2H_OK : xsum_launch(x, M, K, xs, s);
-  if (st == I2H_OK) st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s);
+  int st = own_sums ? I2H_OK : xsum_launch(x, M, K, xs, s, zc);
+  if (st == I2H_OK)
+    st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s, own_sums ? zc : nullptr);
   if (st != I2H_OK) return st;
-  if (select_rerank_supported(nblk_of(N), kcand, R, N, K))
+  if (fused)
     return select_rerank_launch(cs, ci, M, nblk_of(N), kcand, R, x, W, ldw, N, K, k, nullptr, nullptr, out_idx,
-                                out_val, s);
+                                out_val, s, G, zc, ex);
   st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
   if (st == I2H_OK) st = rerank_finalize_launch(x, M, W, ldw, N, K, sel, R, k, ex, out_idx, out_val, s);
   return st;

@@ -38,15 +38,22 @@ int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* pa
 
 // The fused selection + exact rerank + top-k kernel (select_rerank.hip) and its limits.
 bool select_rerank_supported(int64_t nblk, int kc, int R, int64_t N, int64_t K);
+// G > 1 workgroups per row split the exact rerank: each publishes its scores to exw [M, R] and
+// the last to arrive (counted in cnt [M], which must be 0 at launch and is left at G) ranks them.
+// G = 1 needs neither. select_rerank_split gives the G the head uses for M rows.
+int select_rerank_split(int64_t M, int R);
 int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
                          const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
-                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s);
+                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s, int G = 1,
+                         int32_t* cnt = nullptr, float* exw = nullptr);
 
-// Entry points used by i2h_head (same checks and kernels as the exported calls).
-int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s);
+// Entry points used by i2h_head (same checks and kernels as the exported calls). zero_cnt (may be
+// null): M ints the launch sets to 0; coarse_launch takes it only with xs null (the small kernel).
+int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s, int32_t* zero_cnt = nullptr);
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                   const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
-                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s);
+                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s,
+                  int32_t* zero_cnt = nullptr);
 int select_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk,
                   int kcand, int R, int32_t* sel, hipStream_t s);
 int rerank_launch(const uint16_t* x, int64_t M, const uint16_t* W, int64_t ldw, int64_t N,

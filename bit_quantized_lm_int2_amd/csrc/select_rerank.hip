@@ -15,6 +15,10 @@
 // gathered and one wave sorts them.
 // The exact dot products use the same lane mapping and summation order as rerank.hip, so both
 // paths give the same bits.
+// One workgroup pulls the R weight rows at what one CU can keep in flight, well below HBM rate,
+// so the head splits a row over G workgroups: each repeats the (cheap, L2-resident) selection,
+// scores every G-th selected token, publishes its scores, and the last of the G to arrive (an
+// atomic count per row, zeroed by the head's first kernel) ranks all R.
 #include "dequant.h"
 #include "fp8.h"
 #include "host_util.h"
@@ -36,6 +40,7 @@ struct SrLds {
   uint64_t wmax[kSrWaves], wor[kSrWaves];
   int32_t wnum[kSrWaves];
   int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
+  int32_t last;             // this workgroup is the last of its row's G to finish
   uint64_t lower;
   int32_t sel[kSrMaxR];
   float ex[kSrMaxR];
@@ -235,16 +240,19 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
 }
 
 // FP8: the weight rows are e4m3 bytes (Wv) with a per-row fp32 scale (wscale); else bf16 rows.
+// G workgroups per row (blocks m * G .. m * G + G - 1); with G > 1, cnt [M] (0 at launch) and
+// exw [M, R] carry the split rerank.
 template <int BPT, bool FP8>
 __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     const float* __restrict__ cs, const int32_t* __restrict__ ci, int nblk, int kc, int R,
     const uint16_t* __restrict__ x, const void* __restrict__ Wv, const float* __restrict__ wscale, int64_t ldw,
     int N, int K, int k, int32_t* __restrict__ sel_out, float* __restrict__ ex_out, int32_t* __restrict__ oi,
-    float* __restrict__ ov) {
+    float* __restrict__ ov, int G, int32_t* __restrict__ cnt, float* __restrict__ exw) {
   extern __shared__ __align__(16) uint8_t smem[];
   SrLds& L = *reinterpret_cast<SrLds*>(smem);
   uint16_t* xl = reinterpret_cast<uint16_t*>(smem + kSrLdsHead);
-  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = (int)blockIdx.x / G, g = (int)blockIdx.x - m * G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t ld = (int64_t)nblk * kc;
   const float* s = cs + (int64_t)m * ld;
   const int32_t* c = ci + (int64_t)m * ld;
@@ -325,11 +333,12 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   if (tid < R) L.sel[tid] = token_key_token(L.top[tid]);
   __syncthreads();
 
-  // --- exact rerank: wave w scores selected tokens w, w + 16, ... two rows at a time, with the
-  // loads of both rows (up to kSrChunk 512-k steps each) in flight together
+  // --- exact rerank of this workgroup's share, the selected tokens g, g + G, ...: wave w scores
+  // the w-th, (w + 16)-th, ... of them two at a time, with the loads of both rows (up to kSrChunk
+  // 512-k steps each) in flight together
   const int steps = K / 512;
-  for (int j0 = wave; j0 < R; j0 += 2 * kSrWaves) {
-    const int j1 = j0 + kSrWaves;
+  for (int i0 = wave; g + G * i0 < R; i0 += 2 * kSrWaves) {
+    const int j0 = g + G * i0, j1 = g + G * (i0 + kSrWaves);
     const int n0 = L.sel[j0], n1 = j1 < R ? L.sel[j1] : -1;
     const bool v0 = n0 >= 0 && n0 < N, v1 = n1 >= 0 && n1 < N;
     float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
@@ -399,6 +408,26 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     if (lane == 0) {
       L.ex[j0] = v0 ? d0 : -__builtin_inff();
       if (j1 < R) L.ex[j1] = v1 ? d1 : -__builtin_inff();
+      if (G > 1) {
+        exw[(int64_t)m * R + j0] = L.ex[j0];
+        if (j1 < R) exw[(int64_t)m * R + j1] = L.ex[j1];
+      }
+    }
+    // the barrier below does not wait for global stores: the writing wave waits for its own, so
+    // that they are in L2 before thread 0's release writes L2 back
+    if (G > 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  if (G > 1) {
+    // One device-scope release per workgroup and one acquire in the last arrival only: each
+    // such fence writes back or invalidates the XCD's L2, which costs every workgroup sharing it.
+    __syncthreads();
+    if (tid == 0)
+      L.last = __hip_atomic_fetch_add(cnt + m, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
+    __syncthreads();
+    if (!L.last) return;  // workgroup-uniform
+    if (wave == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (lane < R) L.ex[lane] = __hip_atomic_load(exw + (int64_t)m * R + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
@@ -420,6 +449,21 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
 
 }  // namespace
 
+// Workgroups per row for the head: up to 16 rows, 8 (at most one per selected token), so the R
+// weight rows are pulled by several CUs; from 32 rows one per row, since the repeated selection
+// and the fences then cost more than the rerank gains (on MI355X at K = 5120, R = 32: 4.3 us
+// saved at one row, 1.4 at 16, 1.6 to 3.8 lost at 32 to 72).
+#ifndef I2H_SR_SPLIT
+#define I2H_SR_SPLIT 8
+#endif
+int select_rerank_split(int64_t M, int R) {
+  if (M > 16) return 1;
+  int64_t g = 256 / M;
+  if (g > I2H_SR_SPLIT) g = I2H_SR_SPLIT;
+  if (g > R) g = R;
+  return g < 1 ? 1 : (int)g;
+}
+
 bool select_rerank_supported(int64_t nblk, int kc, int R, int64_t N, int64_t K) {
   return nblk >= 1 && nblk <= 4 * kSrThreads && kc >= 1 && kc <= kSrMaxKc && R >= 1 && R <= kSrMaxR &&
          N >= 1 && N <= (int64_t)1 << 19 && check_k(K) == I2H_OK;
@@ -429,35 +473,39 @@ namespace {
 template <bool FP8>
 int select_rerank_launch_t(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
                            const uint16_t* x, const void* W, const float* wscale, int64_t ldw, int64_t N, int64_t K,
-                           int k, int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s) {
+                           int k, int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s,
+                           int G, int32_t* cnt, float* exw) {
   if (!cand_score || !cand_idx || !x || !W || !out_idx || !out_val || (FP8 && !wscale)) return I2H_ERR_ARG;
+  if (G < 1 || G > R || (G > 1 && (!cnt || !exw || M * G > ((int64_t)1 << 30)))) return I2H_ERR_ARG;
   if (M < 1 || M > (1 << 30) || nblk != nblk_of(N) || ldw < K) return I2H_ERR_SHAPE;
   if (!select_rerank_supported(nblk, kc, R, N, K)) return I2H_ERR_LIMIT;
   if (k < 1 || k > R) return I2H_ERR_LIMIT;
   if (!aligned(cand_score, 4) || !aligned(cand_idx, 4) || !aligned(x, 16) || !aligned(W, FP8 ? 8 : 16) ||
       ldw % 8 != 0 || (FP8 && !aligned(wscale, 4)) || !aligned(out_idx, 4) || !aligned(out_val, 4) ||
-      (sel && !aligned(sel, 4)) || (exact && !aligned(exact, 4)))
+      (sel && !aligned(sel, 4)) || (exact && !aligned(exact, 4)) || (cnt && !aligned(cnt, 4)) ||
+      (exw && !aligned(exw, 4)))
     return I2H_ERR_ALIGN;
   const size_t lds = kSrLdsHead + (size_t)K * 2;
-  const dim3 grid((unsigned)M), block(kSrThreads);
+  const dim3 grid((unsigned)(M * G)), block(kSrThreads);
   if (nblk <= kSrThreads)
     hipLaunchKernelGGL((select_rerank_kernel<1, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
   else if (nblk <= 2 * kSrThreads)
     hipLaunchKernelGGL((select_rerank_kernel<2, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
   else
     hipLaunchKernelGGL((select_rerank_kernel<4, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
   return check_launch();
 }
 }  // namespace
 
 int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
                          const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
-                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s) {
+                         int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s, int G,
+                         int32_t* cnt, float* exw) {
   return select_rerank_launch_t<false>(cand_score, cand_idx, M, nblk, kc, R, x, W, nullptr, ldw, N, K, k, sel, exact,
-                                       out_idx, out_val, s);
+                                       out_idx, out_val, s, G, cnt, exw);
 }
 
 }  // namespace i2h
@@ -475,5 +523,5 @@ extern "C" int i2h_select_rerank_topk_fp8(const float* cand_score, const int32_t
                                           int64_t ldw, int64_t N, int64_t K, int k, int32_t* sel, float* exact,
                                           int32_t* out_idx, float* out_val, void* stream) {
   return i2h::select_rerank_launch_t<true>(cand_score, cand_idx, M, nblk, kcand, R, x, W8, wscale, ldw, N, K, k, sel,
-                                           exact, out_idx, out_val, (hipStream_t)stream);
+                                           exact, out_idx, out_val, (hipStream_t)stream, 1, nullptr, nullptr);
 }

@@ -285,9 +285,13 @@ I2H_API int64_t i2h_workspace_bytes(int64_t M, int64_t N, int64_t K, int kcand, 
 
 /*
  * One call of the head: i2h_xsum (skipped when i2h_coarse_sums_x), i2h_coarse_topk, then
- * i2h_select_rerank_topk within its limits, else i2h_select and i2h_rerank_topk, in stream order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
- * aligned, caller-owned, contents undefined afterwards). Arguments as in those calls; y may be
- * NULL. The limits of every step apply.
+ * i2h_select_rerank_topk within its limits, else i2h_select and i2h_rerank_topk, in stream
+ * order, with the intermediates in `workspace` (at least i2h_workspace_bytes(), 256-byte
+ * aligned, caller-owned, contents undefined on entry and afterwards). Arguments as in those
+ * calls; y may be NULL. The limits of every step apply. Up to 16 rows the fused tail runs
+ * several workgroups per row, which count their arrivals in the workspace; the call's first
+ * kernel zeroes those counters, so results equal i2h_select_rerank_topk's bit for bit and two
+ * calls must not share a workspace while both are in flight (as for every intermediate).
  */
 I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t* S,
                      const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
