@@ -69,16 +69,29 @@ __device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
 }
 
 // Appends the keys with `take` set to L.list (at most `cap` stored; L.dec[3] counts them all):
-// one atomic per wave, lanes placed by their rank in the wave's ballot.
-__device__ __forceinline__ void wave_append(SrLds& L, uint64_t key, bool take, int cap) {
-  const uint64_t bal = __builtin_amdgcn_ballot_w64(take);
-  if (bal == 0) return;  // wave-uniform
+// one LDS atomic per wave for all BPT key slots (atomics on one address serialise), lanes placed
+// by slot, then by their rank in the slot's ballot.
+template <int BPT>
+__device__ __forceinline__ void wave_append(SrLds& L, const uint64_t (&key)[BPT], const bool (&take)[BPT], int cap) {
+  uint64_t bal[BPT];
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    bal[j] = __builtin_amdgcn_ballot_w64(take[j]);
+    tot += __builtin_popcountll(bal[j]);
+  }
+  if (tot == 0) return;  // wave-uniform
   const int lane = threadIdx.x & 63;
   int base = 0;
-  if (lane == 0) base = atomicAdd(&L.dec[3], __builtin_popcountll(bal));
+  if (lane == 0) base = atomicAdd(&L.dec[3], tot);
   base = __shfl(base, 0);
-  const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-  if (take && at < cap) L.list[at] = key;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int at = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+    if (take[j] && at < cap) L.list[at] = key[j];
+    base += __builtin_popcountll(bal[j]);
+  }
 }
 
 // Radix select of the R largest keys: the bits every key shares with the largest are skipped,
@@ -168,8 +181,10 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
 //
 // Fast path: a lower bound T of the R-th largest key (if not given: the smallest of the waves'
 // t-th best keys, t = ceil(R / 16), since the 16 t keys at or above it are distinct); if at most
-// 128 keys are at or above T they are gathered, sorted (two waves for more than 64) and the best
-// R kept. Otherwise radix_narrow leaves at most 64 to gather and sort.
+// 128 keys are at or above T they are gathered and ranked, and the best R kept. Otherwise
+// radix_narrow leaves at most 64 to gather and rank. Ranking is by counting over the whole
+// workgroup (8 threads per gathered key, 16 comparisons each): the keys are unique, so a key's
+// place is the number of keys above it, and no sorting network is needed.
 template <int BPT>
 __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
@@ -199,8 +214,10 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
   }
   // gather every key at or above the bound while there is room, counting all of them
   const uint64_t lo = lower != 0 ? lower : 1ull;
+  bool take[BPT];
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) wave_append(L, k[j], k[j] >= lo, kCap);
+  for (int j = 0; j < BPT; ++j) take[j] = k[j] >= lo;
+  wave_append<BPT>(L, k, take, kCap);
   __syncthreads();
   int n = L.dec[3];
   if (n > kCap) {  // block-uniform: narrow down by digits, then gather again
@@ -210,31 +227,29 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
     if (tid == 0) L.dec[3] = 0;
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < BPT; ++j)
-      wave_append(L, k[j], k[j] != 0 && ((k[j] & kLow) >> shift) >= (prefix >> shift), kCap);
+    for (int j = 0; j < BPT; ++j) take[j] = k[j] != 0 && ((k[j] & kLow) >> shift) >= (prefix >> shift);
+    wave_append<BPT>(L, k, take, kCap);
     __syncthreads();
     n = L.dec[3];  // at most 64
   }
-  // sort: one wave for up to 64 keys; else waves 0 and 1 sort 64 each in place and wave 0 merges
-  if (n <= 64) {
-    if (wave == 0) {
-      double v[1] = {lane < n ? __builtin_bit_cast(double, L.list[lane]) : 0.0};
-      wave_sort_f64<1>(v);
-      L.top[lane] = lane < R ? v[0] : 0.0;
+  // rank by counting: gathered key i (n <= 128) is compared by threads 8i .. 8i + 7, thread part
+  // p with keys p, p + 8, ... (the 8 parts read 8 consecutive keys: no LDS bank conflict); places
+  // at or past min(n, R) are 0
+  {
+    const int i = tid >> 3, part = tid & 7;
+    const uint64_t me = i < n ? L.list[i] : 0ull;
+    uint32_t above = 0;
+#pragma unroll
+    for (int q = 0; q < kCap / 8; ++q) {
+      const int j = 8 * q + part;
+      above += (j < n && L.list[j] > me) ? 1u : 0u;
     }
-  } else {
-    if (wave < 2) {
-      const int i = wave * 64 + lane;
-      double v[1] = {i < n ? __builtin_bit_cast(double, L.list[i]) : 0.0};
-      wave_sort_f64<1>(v);
-      L.list[i] = __builtin_bit_cast(uint64_t, v[0]);  // each wave rewrites only what it read
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const double a = __builtin_bit_cast(double, L.list[lane]);
-      const double m = wave_merge64_f64(a, reinterpret_cast<const double*>(L.list + 64));
-      L.top[lane] = lane < R ? m : 0.0;
-    }
+    above += lane_xor<1>(above);
+    above += lane_xor<2>(above);
+    above += lane_xor<4>(above);
+    if (part == 0 && i < n && (int)above < R) L.top[above] = __builtin_bit_cast(double, me);
+    const int filled = n < R ? n : R;
+    if (tid >= filled && tid < 64) L.top[tid] = 0.0;
   }
   __syncthreads();
 }
