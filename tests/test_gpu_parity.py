@@ -370,28 +370,30 @@ def test_head_graph_replay(i2h, M, N, K, k):
         assert torch.equal(oi, ei) and torch.equal(ov, ev), f"replay {r} differs from the eager call"
 
 
-@pytest.mark.parametrize("M,N,K,R,k", [
-    (1, 124160, 5120, 32, 1),   # the draft slot: 8 workgroups of 4 tokens each
-    (3, 20011, 5120, 32, 16),   # ragged tail block
-    (16, 9000, 2048, 32, 4),    # the largest row count that splits
-    (2, 5000, 512, 5, 5),       # R below 8: one token per workgroup
+@pytest.mark.parametrize("M,N,K,kc,R,k", [
+    (1, 124160, 5120, 8, 32, 1),  # the draft slot: 8 workgroups of 4 tokens each
+    (3, 20011, 5120, 8, 32, 16),  # ragged tail block
+    (16, 9000, 2048, 8, 32, 4),   # the largest row count that splits
+    (2, 5000, 512, 8, 5, 5),      # R below 8: one token per workgroup
+    (1, 7000, 5120, 8, 64, 64),   # the largest R: 8 tokens per workgroup, every one returned
+    (4, 3000, 1024, 1, 16, 16),   # one candidate per block
 ])
-def test_head_split_tail(i2h, M, N, K, R, k):
+def test_head_split_tail(i2h, M, N, K, kc, R, k):
     """Up to 16 rows the head splits each row's exact rerank over several workgroups, with an
     arrival count per row in the workspace that the head's first kernel zeroes. Its outputs equal
     those of the one-workgroup tail (i2h_select_rerank_topk on the same candidates) bit for bit,
     on a workspace filled with garbage and again on a second call that reuses it."""
-    say(f"split tail M={M} N={N} K={K} R={R} k={k}")
+    say(f"split tail M={M} N={N} K={K} kc={kc} R={R} k={k}")
     xb = si.bits(si.gen_x(M, K, outliers=8, seed=M + 31))
     Wb = si.bits(si.gen_weight(N, K, seed=N + 5))
     x, W = dev_bf16(xb), dev_bf16(Wb)
     p, S, ZS = i2h.pack(W)
     xs = None if i2h.coarse_sums_x(M, K) else i2h.xsum(x)
-    cs, ci, _ = i2h.coarse_topk(x, xs, p, S, ZS, kcand=8)
-    ei, ev = i2h.select_rerank_topk(cs, ci, 8, R, x, W, k)
-    ws = torch.full((i2h.workspace_bytes(M, N, K, 8, R),), 0xFF, dtype=torch.uint8, device=DEV)
+    cs, ci, _ = i2h.coarse_topk(x, xs, p, S, ZS, kcand=kc)
+    ei, ev = i2h.select_rerank_topk(cs, ci, kc, R, x, W, k)
+    ws = torch.full((i2h.workspace_bytes(M, N, K, kc, R),), 0xFF, dtype=torch.uint8, device=DEV)
     for call in range(2):
-        oi, ov = i2h.head(x, p, S, ZS, W, kcand=8, R=R, k=k, workspace=ws)
+        oi, ov = i2h.head(x, p, S, ZS, W, kcand=kc, R=R, k=k, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(oi, ei) and torch.equal(ov, ev), f"call {call} differs from the one-workgroup tail"
 
