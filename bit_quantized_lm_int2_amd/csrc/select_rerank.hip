@@ -16,9 +16,9 @@
 // The exact dot products use the same lane mapping and summation order as rerank.hip, so both
 // paths give the same bits.
 // One workgroup pulls the R weight rows at what one CU can keep in flight, well below HBM rate,
-// so the head splits a row over G workgroups: each repeats the (cheap, L2-resident) selection,
-// scores every G-th selected token, publishes its scores, and the last of the G to arrive (an
-// atomic count per row, zeroed by the head's first kernel) ranks all R.
+// so the head splits a row over G workgroups (32 at one row): each repeats the (L2-resident)
+// selection, scores every G-th selected token, publishes its scores, and the last of the G to
+// arrive (an atomic count per row, zeroed by the head's first kernel) ranks all R.
 #include "dequant.h"
 #include "fp8.h"
 #include "host_util.h"
@@ -464,16 +464,17 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
 
 }  // namespace
 
-// Workgroups per row for the head: up to 16 rows, 8 (at most one per selected token), so the R
-// weight rows are pulled by several CUs; from 32 rows one per row, since the repeated selection
-// and the fences then cost more than the rerank gains (on MI355X at K = 5120, R = 32: 4.3 us
-// saved at one row, 1.4 at 16, 1.6 to 3.8 lost at 32 to 72).
+// Workgroups per row for the head: up to 16 rows, about 64 workgroups in all (at most 32 per row
+// and one per selected token), so the R weight rows are pulled by several CUs; from 32 rows one
+// per row, since the repeated selection and the fences then cost more than the rerank gains. On
+// MI355X at K = 5120, R = 32, per head call: 3.2 us saved at one row (32 workgroups), 3.9 and
+// 4.3 at 2 and 4 rows, 1.6 at 16; 1.6 to 3.8 us lost at 32 to 72 rows.
 #ifndef I2H_SR_SPLIT
-#define I2H_SR_SPLIT 8
+#define I2H_SR_SPLIT 32
 #endif
 int select_rerank_split(int64_t M, int R) {
   if (M > 16) return 1;
-  int64_t g = 256 / M;
+  int64_t g = 64 / M;
   if (g > I2H_SR_SPLIT) g = I2H_SR_SPLIT;
   if (g > R) g = R;
   return g < 1 ? 1 : (int)g;

@@ -371,11 +371,11 @@ def test_head_graph_replay(i2h, M, N, K, k):
 
 
 @pytest.mark.parametrize("M,N,K,kc,R,k", [
-    (1, 124160, 5120, 8, 32, 1),  # the draft slot: 8 workgroups of 4 tokens each
+    (1, 124160, 5120, 8, 32, 1),  # the draft slot: 32 workgroups of one token each
     (3, 20011, 5120, 8, 32, 16),  # ragged tail block
-    (16, 9000, 2048, 8, 32, 4),   # the largest row count that splits
-    (2, 5000, 512, 8, 5, 5),      # R below 8: one token per workgroup
-    (1, 7000, 5120, 8, 64, 64),   # the largest R: 8 tokens per workgroup, every one returned
+    (16, 9000, 2048, 8, 32, 4),   # the largest row count that splits (4 per row)
+    (2, 5000, 512, 8, 5, 5),      # R below the split: one token per workgroup
+    (1, 7000, 5120, 8, 64, 64),   # the largest R: 2 tokens per workgroup, every one returned
     (4, 3000, 1024, 1, 16, 16),   # one candidate per block
 ])
 def test_head_split_tail(i2h, M, N, K, kc, R, k):
