@@ -301,13 +301,16 @@ I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const 
 /*
  * The drop-in logits row (radiance_drafthead.py, _apply_head_int2, after the exact rerank):
  *   row     = topk_only ? -inf : y[m, :]            (y: the coarse bf16 row from i2h_coarse_topk)
- *   row[sel[m, j]] = bf16(exact[m, j])               for every sel[m, j] in [0, N)
+ *   row[sel[m, j]] = bf16(exact[m, j])               for every sel[m, j] >= 0
  *   out[m, :] = cast_out(row + bias)                 with torch's type promotion: a bf16 bias
  *             rounds the fp32 sum back to bf16; an fp16 or fp32 bias gives the fp32 sum; no bias
  *             keeps the bf16 row; the cast to out_dtype rounds to nearest-even.
  *   y       bf16 [M, N] (row stride N), 16-byte aligned; may be NULL when topk_only.
  *   sel     int32 [M, R], exact fp32 [M, R] (from i2h_select_rerank_topk or i2h_select +
- *           i2h_rerank); a row's tokens must be distinct (as those calls give them).
+ *           i2h_rerank); each entry is -1 (no token) or a token in [0, N), and a row's tokens
+ *           are distinct (as those calls give them). Any other entry is outside the contract
+ *           (the page's scatter would reject it); the kernel ignores it, so nothing outside the
+ *           row is ever written.
  *   bias    [N] of bias_dtype (I2H_DTYPE_NONE with bias NULL for none), naturally aligned.
  *   out     [M, N] of out_dtype (BF16 / F16: uint16 bits; F32), 16-byte aligned. out may be y
  *           itself when out_dtype is I2H_DTYPE_BF16 (each entry is read before it is written,

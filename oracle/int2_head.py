@@ -360,15 +360,20 @@ def logits_row(y_bits: np.ndarray, sel: np.ndarray, exact: np.ndarray, topk_only
 
     y_bits bf16 bits [M, N]; sel int32 [M, R] (distinct tokens per row, -1 = none); exact
     float32 [M, R]; bias [N] given as uint16 bits (bf16), float16 or float32 per bias_dtype.
+    A token outside [0, N) other than -1 raises ValueError: the page writes the exact scores
+    back with a scatter over the row, which rejects an index past the row's end.
     """
     assert out_dtype in LOGIT_DTYPES and (bias is None) == (bias_dtype is None)
     M, N = y_bits.shape
+    sel = np.asarray(sel)
+    if ((sel < -1) | (sel >= N)).any():
+        raise ValueError("sel holds a token outside [0, N) that is not -1 (none)")
     # the row before the bias: coarse bf16 values, or -inf for a top-k caller
     y = np.full((M, N), -np.inf, dtype=np.float32) if topk_only else bf16_to_f32(y_bits)
     e = bf16_to_f32(f32_to_bf16(np.asarray(exact, dtype=np.float32)))  # ex.to(bfloat16)
     for m in range(M):
         for j in range(sel.shape[1]):
-            if 0 <= sel[m, j] < N:  # -1 (none) and tokens past the row are skipped
+            if sel[m, j] >= 0:  # -1: no token in this slot
                 y[m, sel[m, j]] = e[m, j]
     # the bias, then the row's dtype after promotion
     if bias is None:

@@ -478,8 +478,6 @@ def _logits_inputs(M, N, R, seed):
     y_bits = oracle.f32_to_bf16(g.normal(0, 4, (M, N)).astype(np.float32))
     sel = np.stack([g.choice(N, R, replace=False) for _ in range(M)]).astype(np.int32)
     sel[0, -3:] = -1                      # fewer than R reranked tokens in row 0
-    if M > 1:
-        sel[1, 0] = N + 7                 # out of range: never written
     ex = g.normal(0, 8, (M, R)).astype(np.float32)
     bias = g.normal(0, 2, N).astype(np.float32)
     return y_bits, sel, ex, bias

@@ -457,6 +457,19 @@ def test_logits_row_hand_example():
     assert out.tolist() == [[b01 + 0.5, 2.0 + 2.0 ** -8, 8.25, 0.0]]
 
 
+def test_logits_row_rejects_tokens_outside_the_row():
+    """The write-back is a scatter over the row: -1 marks an empty slot, anything else outside
+    [0, N) is an error, not a skipped entry."""
+    y = _bf([1.0, 2.0, -3.0, 0.5])
+    ex = np.array([[7.25, 0.1]], np.float32)
+    assert oracle.logits_row(y, np.array([[-1, 3]], np.int32), ex, False).shape == (1, 4)
+    for bad in ([[4, 0]], [[0, -2]], [[2, 11]]):
+        with pytest.raises(ValueError):
+            oracle.logits_row(y, np.array(bad, np.int32), ex, False)
+        with pytest.raises(ValueError):
+            oracle.logits_row(y, np.array(bad, np.int32), ex, True)
+
+
 def test_logits_row_rounding_ties():
     """Half-way sums round to the even neighbour: bf16 at 1 + 2^-8 and 1 + 3*2^-8 (spacing 2^-7),
     fp16 at 1 + 3*2^-11 (spacing 2^-10)."""
