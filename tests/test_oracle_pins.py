@@ -569,6 +569,36 @@ def test_fp8_quantize_matches_eager_fp32_ops():
     assert np.array_equal(So, si.bits(S)) and np.array_equal(ZSo, si.bits(ZS))
 
 
+def test_pack_fp8_hand_example():
+    """The hand-worked FP8 row (tests/golden/fp8_pack_example.txt): subnormal codes, a zero point
+    clamped from -1 to 0, a code clamped from 4 to 3, both half-way codes rounded to even."""
+    kv, _ = read_golden("fp8_pack_example.txt")
+    row = np.concatenate([np.tile(np.array(hexs(kv[f"pattern{t}"]), np.uint8), 32) for t in range(4)])
+    packed, S, ZS = oracle.pack_fp8(row[None, :], np.array([float(kv["scale"])], np.float32))
+    assert packed.shape == (1, 128)
+    assert packed[0].tolist() == hexs(kv["packed_pattern"]) * 32
+    assert S[0].tolist() == hexs(kv["S"]) and ZS[0].tolist() == hexs(kv["ZS"])
+
+
+def test_pack_fp8_matches_eager_torch_chain():
+    """The whole FP8 pack as eager torch ops: the e4m3fn decode times the row scale (fp32), the
+    quantiser, the bias-4 premultiply and the quarter-split bytes assembled by shifts."""
+    N, K = 260, 1024
+    W8, scale = si.gen_weight_fp8(N, K, seed=88)
+    w = (W8.view(torch.float8_e4m3fn).float() * scale[:, None]).reshape(N, K // 128, 128)
+    lo, hi = w.amin(2), w.amax(2)
+    sc = ((hi - lo) / 3).clamp(min=1e-8)
+    zp = torch.round(-lo / sc).clamp(0, 3)
+    q = torch.round(w / sc[:, :, None] + zp[:, :, None]).clamp(0, 3).to(torch.uint8).reshape(N, K)
+    Q = K // 4
+    packed = q[:, :Q] | (q[:, Q:2 * Q] << 2) | (q[:, 2 * Q:3 * Q] << 4) | (q[:, 3 * Q:] << 6)
+    S = (4.0 * sc).to(torch.bfloat16)
+    ZS = (4.0 * sc + zp * sc).to(torch.bfloat16)
+    po, So, ZSo = oracle.pack_fp8(W8.numpy(), scale.numpy())
+    assert np.array_equal(po, packed.numpy())
+    assert np.array_equal(So, si.bits(S)) and np.array_equal(ZSo, si.bits(ZS))
+
+
 # ---------------------------------------------------------------------------------------------
 # int4 head (radiance_drafthead.py, _quantize_head_now BITS = 4: codes 0..15, half-split bytes,
 # bias 16)
@@ -616,6 +646,64 @@ def test_int4_exact_grid_head_recovers_codes_and_logits():
     assert np.array_equal(oracle.dequantize4(p, S, ZS), oracle.bf16_to_f32(Wb).astype(np.float64))
     x = si.bits(si.gen_x(3, K, outliers=4, seed=41))
     assert np.allclose(oracle.coarse_logits4(x, p, S, ZS), oracle.exact_logits(x, Wb), rtol=0, atol=1e-9)
+
+
+def block_top(vals, kc, block_n=64):
+    """Per row, the kc best (value, token) pairs of each 64-column block by repeated pick (largest
+    value, lower column on ties), in pure Python."""
+    out = []
+    for row in vals:
+        r = []
+        for b0 in range(0, len(row), block_n):
+            cols = list(range(b0, min(b0 + block_n, len(row))))
+            for _ in range(kc):
+                best = cols[0]
+                for c in cols[1:]:
+                    if row[c] > row[best]:
+                        best = c
+                r.append((float(row[best]), best))
+                cols.remove(best)
+        out.append(r)
+    return out
+
+
+def test_head4_all_tokens_reranked_equals_brute_force():
+    """P-5 for the int4 head: with KCAND = BLOCK_N and R = N every token is reranked exactly, so
+    argmax and top-16 are those of the dense bf16 head."""
+    N, K = 256, 512
+    W = si.bits(si.gen_weight(N, K, seed=89))
+    x = si.bits(si.gen_x(3, K, outliers=4, seed=42))
+    p4, S4, ZS4 = oracle.pack4(W)
+    ex = oracle.exact_logits(x, W)
+    for k in (1, 16):
+        r = oracle.head4(x, W, p4, S4, ZS4, kcand=64, R=N, k=k)
+        want = brute_topk(ex, k)
+        for m in range(3):
+            assert list(r["idx"][m]) == want[m]
+            assert np.allclose(r["val"][m], ex[m, want[m]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kcand", [1, 3])
+def test_head4_exact_grid_head_end_to_end(kcand):
+    """On an exact int4 grid the coarse logits are the exact bf16 logits, so every step is fixed
+    by brute force: the block candidates are each block's kcand best exact logits, the selection
+    the R best of those, and the result the best of the selection by exact score."""
+    N, K, R = 1000, 512, 12                # 16 blocks, the last one 40 columns wide
+    Wb, _, _, _ = grid_head4(N, K, 6)
+    x = si.bits(si.gen_x(2, K, outliers=4, seed=43))
+    p4, S4, ZS4 = oracle.pack4(Wb)
+    r = oracle.head4(x, Wb, p4, S4, ZS4, kcand=kcand, R=R, k=4)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    wf = oracle.bf16_to_f32(Wb).astype(np.float64)
+    exact = [[math.fsum(xf[m] * wf[n]) for n in range(N)] for m in range(2)]
+    assert np.allclose(r["coarse"], np.array(exact), rtol=0, atol=1e-9)
+    cands = block_top(exact, kcand)
+    for m in range(2):
+        assert r["cand_idx"][m].tolist() == [t for _, t in cands[m]]
+        assert np.allclose(r["cand_score"][m], [v for v, _ in cands[m]], rtol=0, atol=1e-9)
+        top = sorted(cands[m], key=lambda p: (-p[0], p[1]))[:R]
+        assert len(top) == R and r["sel"][m].tolist() == [t for _, t in top]
+        assert r["idx"][m].tolist() == [t for _, t in top[:4]]
 
 
 def test_int4_quantize_matches_eager_fp32_ops():
