@@ -261,7 +261,10 @@ def gpu_paths(i2h, x, W, p, S, ZS, kc, R, k):
     return a, b
 
 
-def check_path(g, res, rows, xr, Wb, kc, k, label):
+FOLD2 = (32.0, 8.0, 2.0, 1.0)  # the int2 kernels' bias fold per quarter (mask dequant 1 + v/(4f))
+
+
+def check_path(g, res, rows, xr, Wb, kc, k, label, scales, fold=FOLD2):
     c = res["coarse"]
     yh, csh, cih = host(g["y"])[rows], host(g["cs"])[rows], host(g["ci"])[rows]
     ok = cih >= 0
@@ -270,15 +273,24 @@ def check_path(g, res, rows, xr, Wb, kc, k, label):
                           oracle.f32_to_bf16(csh[ok]))
     err = pu.check_coarse_values(yh, c)
     err32 = pu.coarse_fp32_error(csh, cih, c)
-    cand_ex, cand_tight = pu.check_candidates(csh, cih, c, kc)
+    mag = pu.fold_magnitude(cih, xr, scales[0], scales[1], fold)
+    fold_ratio = pu.fold_error_ratio(csh, cih, c, mag)
+    budget = pu.FOLD_C * pu.U32 * mag
+    cand_diff, cand_loose = pu.check_candidates(csh, cih, c, kc, budget=budget)
     g_sel = host(g["sel"])[rows]
-    sel_ex, sel_tight = pu.check_selection(g_sel, res["sel"], c)
+    sel_rows = pu.check_selection(g_sel, res["sel"], c, budget=budget)
     e_g, rerr = pu.check_rerank(host(g["ex"])[rows], xr, Wb, g_sel)
-    fin_ex = pu.check_final(host(g["oi"])[rows], host(g["ov"])[rows], e_g, g_sel, k)
+    fin_ex, fin_tight = pu.check_final(host(g["oi"])[rows], host(g["ov"])[rows], e_g, g_sel, k)
     match, sel_excused, tie_excused = pu.final_vs_oracle(host(g["oi"])[rows], res, g_sel, e_g)
     say(f"  [{label}] rows={len(rows)} coarse_err(bf16 Y)={err:.2e} coarse_err(fp32)={err32:.2e} "
-        f"cand_excused={cand_ex} (tight {cand_tight}) sel_excused_rows={sel_ex} (tight {sel_tight}) "
-        f"rerank_err={rerr:.2e} final match={match} sel_excused={sel_excused} tie_excused={tie_excused + fin_ex}")
+        f"cand_diff={cand_diff} sel_diff_rows={sel_rows} rerank_err={rerr:.2e} final match={match} "
+        f"sel_excused={sel_excused} tie_excused={tie_excused} (finalize ties {fin_ex}, tight {fin_tight})")
+    pu.record(path=label, rows=int(len(rows)), k=int(k), K=int(xr.shape[1]), N=int(c.shape[1]), coarse_err_y=err,
+              coarse_err_fp32=err32, fold_error_ratio=fold_ratio, tie_window=float(pu.tie_window(c, budget).max()
+                                                                                  / max(pu.row_scale(c).max(), 1e-300)),
+              cand_diff=cand_diff, cand_diff_within_coarse_tol=cand_loose, sel_diff_rows=sel_rows,
+              rerank_err=rerr, final_places=int(len(rows) * k), final_match=match, final_sel_excused=sel_excused,
+              final_tie_excused=tie_excused, finalize_ties=fin_ex, finalize_ties_tight=fin_tight)
     return match
 
 
@@ -295,8 +307,8 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     po, So, ZSo = packed_o
     xr = xb[rows]
     res = oracle.head(xr, Wb, po, So, ZSo, kcand=kc, R=R, k=k, coarse=None if coarse_o is None else coarse_o[rows])
-    match = check_path(a, res, rows, xr, Wb, kc, k, "head kernels")
-    check_path(b, res, rows, xr, Wb, kc, k, "separate calls")
+    match = check_path(a, res, rows, xr, Wb, kc, k, "head kernels", scales=(So, ZSo))
+    check_path(b, res, rows, xr, Wb, kc, k, "separate calls", scales=(So, ZSo))
     return dict(match=match, places=len(rows) * k, res=res, gpu_idx=host(a["oi"])[rows])
 
 
@@ -377,6 +389,8 @@ def test_head_graph_replay(i2h, M, N, K, k):
     (2, 5000, 512, 8, 5, 5),      # R below the split: one token per workgroup
     (1, 7000, 5120, 8, 64, 64),   # the largest R: 2 tokens per workgroup, every one returned
     (4, 3000, 1024, 1, 16, 16),   # one candidate per block
+    (4, 200003, 5120, 8, 32, 16), # four blocks per thread, 16 workgroups per row, ragged tail
+    (16, 248320, 5120, 8, 32, 16),  # the full vocabulary at 16 rows: four per row
 ])
 def test_head_split_tail(i2h, M, N, K, kc, R, k):
     """Up to 16 rows the head splits each row's exact rerank over several workgroups, with an
@@ -444,26 +458,30 @@ def full_vocab_head():
     Wb = si.bits(si.gen_weight(N, K))
     xb = si.bits(si.gen_x(72, K, outliers=cfg["outliers"]))
     say("oracle pack of the full vocabulary")
-    return xb, Wb, oracle.pack(Wb)
+    packed_o = oracle.pack(Wb)
+    say("oracle coarse, 72 rows of the full vocabulary")
+    coarse_o = oracle.coarse_logits(xb, *packed_o)
+    return xb, Wb, packed_o, coarse_o
 
 
 def test_full_vocab_pack_sampled(i2h, full_vocab_head):
     """The pack of the 248320-row head, bit-exact on sampled vocab rows."""
-    xb, Wb, packed_o = full_vocab_head
+    xb, Wb, packed_o, _ = full_vocab_head
     p, S, ZS = i2h.pack(dev_bf16(Wb))
     pick = np.sort(np.random.default_rng(0).choice(Wb.shape[0], 4096, replace=False))
     assert np.array_equal(host(p)[pick], packed_o[0][pick])
     assert np.array_equal(host(S)[pick], packed_o[1][pick]) and np.array_equal(host(ZS)[pick], packed_o[2][pick])
 
 
-# every row count of the full-vocabulary band (each takes a different kernel or chunking: the
-# M = 1 kernel, the 16-, 32- and 64-row tiles, 64 + 8 rows); the oracle checks sampled rows
-@pytest.mark.parametrize("M,rows", [(1, [0]), (2, [1]), (8, [0, 7]), (32, [5, 31]), (64, [0, 63]),
-                                    (72, [0, 31, 71])])
-def test_full_vocab_top16(i2h, full_vocab_head, M, rows):
-    xb, Wb, packed_o = full_vocab_head
-    say(f"full vocabulary M={M}, oracle rows {rows}")
-    out = run_and_check(i2h, xb[:M], Wb, k=16, packed_o=packed_o, rows=rows)
+# every row count of the full-vocabulary band (each takes a different kernel, chunking or split
+# of the tail: the M = 1 kernel, the 16-, 32- and 64-row tiles, 64 + 8 rows; four blocks per
+# thread in the tail, split over 16 workgroups per row at 4 rows and 4 at 16); every row is
+# checked against the oracle
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 16, 32, 64, 72])
+def test_full_vocab_top16(i2h, full_vocab_head, M):
+    xb, Wb, packed_o, coarse_o = full_vocab_head
+    say(f"full vocabulary M={M}")
+    out = run_and_check(i2h, xb[:M], Wb, k=16, packed_o=packed_o, coarse_o=coarse_o[:M])
     say(f"  top-16 match vs oracle: {out['match']}/{out['places']}")
 
 
@@ -629,7 +647,7 @@ def run_and_check4(i2h, xb, Wb, kc=1, R=32, k=1):
     g = dict(cs=cs, ci=ci, y=y, sel=sel, ex=ex, oi=oi, ov=ov)
     res = oracle.head4(xb, Wb, po, So, ZSo, kcand=kc, R=R, k=k)
     rows = np.arange(xb.shape[0])
-    return check_path(g, res, rows, xb, Wb, kc, k, "int4 head")
+    return check_path(g, res, rows, xb, Wb, kc, k, "int4 head", scales=(So, ZSo), fold=(1.0,))
 
 
 @pytest.mark.parametrize("M,N,K,kc,R,k", [(1, 4096, 512, 1, 32, 1), (3, 4133, 5120, 1, 32, 1),
