@@ -54,6 +54,7 @@ extern "C" const char* i2h_strerror(int status) {
     case I2H_ERR_LIMIT: return "kcand, R or k outside the supported limits";
     case I2H_ERR_WORKSPACE: return "workspace missing or too small";
     case I2H_ERR_HIP: return "HIP launch failed (see i2h_last_hip_error)";
+    case I2H_ERR_UNIMPLEMENTED: return "not implemented";
     default: return "unknown status";
   }
 }

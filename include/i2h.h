@@ -41,6 +41,8 @@ extern "C" {
 #define I2H_ERR_LIMIT (-4)      /* kcand, R or k outside their limits */
 #define I2H_ERR_WORKSPACE (-5)  /* workspace missing or smaller than i2h_workspace_bytes() */
 #define I2H_ERR_HIP (-6)        /* a HIP launch failed; see i2h_last_hip_error() */
+#define I2H_ERR_UNIMPLEMENTED (-7) /* reserved: every operation declared here is implemented, and
+                                      no call returns this code */
 
 #define I2H_GROUP 128
 #define I2H_BLOCK_N 64

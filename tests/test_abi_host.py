@@ -42,8 +42,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_last_error():
     lib = i2h.lib()
-    for code in (OK, ARG, SHAPE, ALIGN, LIMIT, WS, -6, -99):
+    for code in (OK, ARG, SHAPE, ALIGN, LIMIT, WS, -6, -7, -99):
         assert lib.i2h_strerror(code)
+    assert lib.i2h_strerror(-7) != lib.i2h_strerror(-99)
     assert lib.i2h_last_hip_error() == 0
 
 
