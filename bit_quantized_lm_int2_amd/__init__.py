@@ -17,6 +17,7 @@ import torch
 
 __all__ = ["I2HError", "lib", "library_path", "sizes", "pack", "xsum", "coarse_topk", "select",
            "rerank", "finalize", "rerank_topk", "select_rerank_topk", "coarse_sums_x", "workspace_bytes", "head",
+           "head_noalloc",
            "logits", "pack_fp8", "rerank_fp8", "select_rerank_topk_fp8", "pack4", "coarse4_topk",
            "select_tokens", "pack_variant", "xsum_group", "coarse_variant_topk", "GROUP",
            "BLOCK_N"]
@@ -48,6 +49,7 @@ _SIGNATURES = {
                                 _P], _INT),
     "i2h_head": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P,
                   _I64, _P], _INT),
+    "i2h_head_noalloc": ([_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _INT, _P, _P, _P, _P], _INT),
     "i2h_logits": ([_P, _I64, _I64, _P, _P, _INT, _INT, _P, _INT, _P, _INT, _P], _INT),
     "i2h_pack_fp8": ([_P, _P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
     "i2h_pack4": ([_P, _I64, _I64, _I64, _P, _P, _P, _P], _INT),
@@ -343,6 +345,39 @@ def head(x, packed, S, ZS, W, kcand: int = 8, R: int = 32, k: int = 1, want_y: b
                                       kcand, R, k, _ptr(oi), _ptr(ov), _ptr(y), _ptr(workspace),
                                       workspace.numel(), _stream(x)))
     return (oi, ov, y) if want_y else (oi, ov)
+
+
+def head_noalloc(x, packed, S, ZS, W, kcand: int = 8, R: int = 32, k: int = 1, out=None, y=None):
+    """head() through i2h_head_noalloc: the library's own device scratch instead of a workspace.
+    With out = (idx int32 [M, k], val fp32 [M, k]) given (and y, bf16 [M, N], if wanted) this
+    allocates nothing."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(packed, "packed", torch.uint8, 2)
+    for t, nm in ((x, "x"), (packed, "packed"), (S, "S"), (ZS, "ZS")):
+        _dense(t, nm)
+    M, N, K = _head_shapes(x, packed, S, ZS)
+    if tuple(W.shape) != (N, K):
+        raise ValueError(f"W must have shape {(N, K)}, got {tuple(W.shape)}")
+    if out is None:
+        oi = torch.empty(M, k, dtype=torch.int32, device=x.device)
+        ov = torch.empty(M, k, dtype=torch.float32, device=x.device)
+    else:
+        oi, ov = out
+        _need(oi, "idx", torch.int32, 2)
+        _need(ov, "val", torch.float32, 2)
+        _shape(oi, "idx", (M, k))
+        _shape(ov, "val", (M, k))
+        _dense(oi, "idx")
+        _dense(ov, "val")
+    if y is not None:
+        _need(y, "y", torch.bfloat16, 2)
+        _shape(y, "y", (M, N))
+        _dense(y, "y")
+    _check("i2h_head_noalloc", lib().i2h_head_noalloc(_ptr(x), M, _ptr(packed), _ptr(S), _ptr(ZS), _ptr(W),
+                                                      _rows(W, "W"), N, K, kcand, R, k, _ptr(oi), _ptr(ov),
+                                                      _ptr(y), _stream(x)))
+    return oi, ov
 
 
 def logits(y, sel, exact, topk_only: bool = False, bias: torch.Tensor | None = None,

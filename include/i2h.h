@@ -43,6 +43,7 @@ extern "C" {
 #define I2H_ERR_HIP (-6)        /* a HIP launch failed; see i2h_last_hip_error() */
 #define I2H_ERR_UNIMPLEMENTED (-7) /* reserved: every operation declared here is implemented, and
                                       no call returns this code */
+#define I2H_ERR_SCRATCH (-8)    /* i2h_head_noalloc: the call needs more than its device scratch */
 
 #define I2H_GROUP 128
 #define I2H_BLOCK_N 64
@@ -50,6 +51,7 @@ extern "C" {
 #define I2H_MAX_KCAND 64
 #define I2H_MAX_R 1024
 #define I2H_MAX_NBLK 8192       /* N <= 524288 for the candidate selection */
+#define I2H_NOALLOC_SCRATCH_BYTES (24 << 20) /* device scratch of i2h_head_noalloc, per GPU */
 
 /* Element types of the drop-in logits row (i2h_logits). */
 #define I2H_DTYPE_NONE 0        /* no embedding bias */
@@ -299,6 +301,25 @@ I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const 
                      const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
                      int kcand, int R, int k, int32_t* out_idx, float* out_val, uint16_t* y,
                      void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * i2h_head for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments without the workspace,
+ * the same kernels and results bit for bit. The intermediates live in a device array of
+ * I2H_NOALLOC_SCRATCH_BYTES (24 MiB) that the library holds on each GPU it runs on until the
+ * process ends; its address is looked up on the first call on a device (the GPU of `stream`),
+ * so make that first call outside graph capture. The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine. A call whose i2h_workspace_bytes() exceeds the scratch
+ * returns I2H_ERR_SCRATCH before anything is enqueued (the 124160-row slice at up to 128 rows, or
+ * the 248320-row vocabulary at up to 96 rows, fit at kcand = 8, R = 32). Every call on one GPU
+ * shares that GPU's scratch, and the scratch keeps the last call's contents (the call's first
+ * kernel zeroes the tail's arrival counters, so nothing needs clearing): calls that overlap on one
+ * GPU, on different streams or threads, race and must be ordered by the caller.
+ */
+I2H_API int i2h_head_noalloc(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t* S,
+                             const uint16_t* ZS, const uint16_t* W, int64_t ldw, int64_t N, int64_t K,
+                             int kcand, int R, int k, int32_t* out_idx, float* out_val, uint16_t* y,
+                             void* stream);
 
 /*
  * The drop-in logits row (radiance_drafthead.py, _apply_head_int2, after the exact rerank):

@@ -26,7 +26,7 @@ def test_header_declares_the_entry_points():
     names = set(declared())
     want = {"i2h_version", "i2h_strerror", "i2h_last_hip_error", "i2h_sizes", "i2h_pack", "i2h_xsum",
             "i2h_coarse_topk", "i2h_select", "i2h_rerank", "i2h_finalize", "i2h_workspace_bytes",
-            "i2h_head", "i2h_coarse_sums_x", "i2h_rerank_topk",
+            "i2h_head", "i2h_head_noalloc", "i2h_coarse_sums_x", "i2h_rerank_topk",
             "i2h_select_rerank_topk", "i2h_logits", "i2h_pack_fp8", "i2h_rerank_fp8",
             "i2h_select_rerank_topk_fp8", "i2h_pack4", "i2h_coarse4_topk",
             "i2h_select_tokens", "i2h_select_tokens_workspace_bytes", "i2h_pack_variant", "i2h_xsum_group", "i2h_coarse_variant_topk"}
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_last_error():
     lib = i2h.lib()
-    for code in (OK, ARG, SHAPE, ALIGN, LIMIT, WS, -6, -7, -99):
+    for code in (OK, ARG, SHAPE, ALIGN, LIMIT, WS, -6, -7, -8, -99):
         assert lib.i2h_strerror(code)
     assert lib.i2h_strerror(-7) != lib.i2h_strerror(-99)
     assert lib.i2h_last_hip_error() == 0
@@ -272,3 +272,17 @@ def test_variant_entry_points_reject_before_launch():
     assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 2, 8, P, P, None) == ARG
     assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 0, P, P, None) == LIMIT
     assert c(P + 8, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 8, P, P, None) == ALIGN
+
+
+def test_head_noalloc_statuses():
+    """i2h_head_noalloc takes i2h_head's checks, then rejects a call too large for its scratch;
+    all before any HIP call."""
+    h = i2h.lib().i2h_head_noalloc
+    SCRATCH = -8
+    assert h(P, 200, P, P, P, P, 5120, 248320, 5120, 8, 32, 1, P, P, None, None) == SCRATCH
+    assert h(P, 400, P, P, P, P, 5120, 124160, 5120, 8, 32, 1, P, P, None, None) == SCRATCH
+    assert h(None, 1, P, P, P, P, 5120, 124160, 5120, 8, 32, 1, P, P, None, None) == ARG
+    assert h(P, 1, P, P, P, P, 5120, 124160, 5000, 8, 32, 1, P, P, None, None) == SHAPE
+    assert h(P, 1, P, P, P, P, 5120, 124160, 5120, 8, 32, 33, P, P, None, None) == LIMIT
+    assert h(ODD, 1, P, P, P, P, 5120, 124160, 5120, 8, 32, 1, P, P, None, None) == ALIGN
+    assert i2h.workspace_bytes(96, 248320, 5120, 8, 32) <= 24 << 20 < i2h.workspace_bytes(200, 248320, 5120, 8, 32)
