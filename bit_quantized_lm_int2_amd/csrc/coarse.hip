@@ -576,13 +576,19 @@ bool small_sums_x(int64_t M, int64_t K) {
 
 }  // namespace
 
-// True when every launch coarse_launch makes for M rows of K sums the groups of x itself: the
-// small kernel with x in LDS, for one row, or for up to 4 rows of a K the tile kernel is not
-// built for (the tile kernels, which take the sums from i2h_xsum, are faster from 2 rows on).
+// True when every launch coarse_launch makes for M rows of K sums the groups of x itself: rows
+// go in chunks of kTileMaxRows, a one-row chunk runs the small kernel (which sums x when x fits in
+// its LDS), a larger chunk the tile kernel where it is built for K (which sums x up to 32 rows),
+// else the small kernel up to 4 rows (x in its LDS) or the generic kernel (which needs the sums).
 bool coarse_sums_x(int64_t M, int64_t K) {
-  if (M < 1 || M > 4 || check_k(K) != I2H_OK) return false;
-  if (M > 1 && tile_supported(M, K)) return false;
-  return small_sums_x(M, K);
+  if (M < 1 || check_k(K) != I2H_OK) return false;
+  auto chunk = [&](int64_t mc) {
+    if (mc == 1) return small_sums_x(1, K);
+    if (tile_supported(mc, K)) return tile_sums_x(mc, K);
+    return mc <= 4 && small_sums_x(mc, K);
+  };
+  if (M > kTileMaxRows && !chunk(kTileMaxRows)) return false;
+  return chunk((M - 1) % kTileMaxRows + 1);
 }
 
 namespace {
@@ -633,9 +639,9 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
   // only the small kernel zeroes counters: the caller passes them when every row runs there
   if (zero_cnt && (xs || !coarse_sums_x(M, K) || !aligned(zero_cnt, 4))) return I2H_ERR_ARG;
   const int64_t ld = nblk_of(N) * kcand;
-  // rows go in chunks of kTileMaxRows; a chunk of one row, or of at most 4 rows without xs or
-  // with a K the tile kernel is not built for, runs the small kernel; a larger one the tile kernel
-  // where it is built for K, else the generic kernel
+  // rows go in chunks of kTileMaxRows; a chunk of one row, or of at most 4 rows with a K the tile
+  // kernel is not built for, runs the small kernel; a larger one the tile kernel where it is built
+  // for K, else the generic kernel
   for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
     const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
     const uint16_t* xc = x + m0 * K;
@@ -643,14 +649,17 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     float* csc = cand_score + m0 * ld;
     int32_t* cic = cand_idx + m0 * ld;
     uint16_t* yc = y ? y + m0 * N : nullptr;
+    int32_t* zcc = zero_cnt ? zero_cnt + m0 : nullptr;
+    const bool tile_ok = tile_supported(mc, K);
     int st;
-    if (mc <= 4 && (mc == 1 || !xsc || !tile_supported(mc, K)) && (xsc || small_sums_x(mc, K)))
-      st = small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc,
-                      zero_cnt ? zero_cnt + m0 : nullptr, s);
+    if (mc == 1 || (mc <= 4 && !tile_ok))
+      st = xsc || small_sums_x(mc, K)
+               ? small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, zcc, s)
+               : I2H_ERR_ARG;
+    else if (tile_ok)
+      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, zcc, s);
     else if (!xsc)
       st = I2H_ERR_ARG;
-    else if (tile_supported(mc, K))
-      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, s);
     else
       st = generic_rows(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
     if (st != I2H_OK) return st;

@@ -12,8 +12,9 @@
 // only the scale of each group to the accumulator; the zero term, the sum over groups of
 // xs[m, g] z[n, g], is one more small contraction on the matrix cores after the loop, with both
 // factors split exactly into bf16 parts, so that the VALU does the dequant and one FMA per output
-// and group. The group sums xs come from i2h_xsum. The wave's S and ZS rows sit in LDS for the
-// whole K loop. The packed stream is loaded one span ahead, after the next stage of x, so that
+// and group. The group sums xs are given (i2h_xsum) or, with xs null, taken in the kernel: each
+// wave sums one part of one (quarter, row tile) per stage on the matrix cores, against a B operand
+// of ones, into LDS. The wave's S and ZS rows sit in LDS for the whole K loop. The packed stream is loaded one span ahead, after the next stage of x, so that
 // waiting for x never waits for packed bytes that are not needed yet (loads retire in order).
 // The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
 // sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions.
@@ -38,12 +39,19 @@ struct Tile {
   static constexpr int XBUF = MR * RS;                        // bytes of one x stage buffer
   static constexpr int UPT = MR * QS * 16 / THREADS;          // 16-byte x units per thread per stage
   static constexpr int P = MT == 1 ? 4 : (MT == 2 ? 2 : 1);   // emit lanes per row
+  // group sums of x in the kernel: each stage's QS quarters x MT row tiles are summed on the matrix
+  // cores (x fragments against a B operand of ones), SP waves per (quarter, row tile), each taking
+  // 4 / SP of its 4 slices; SP partial sums per group
+  static constexpr bool OWN_SUMS = MT <= 2;
+  static constexpr int SP = WAVES / (QS * MT);
+  static_assert(SP >= 1 && 4 % SP == 0 && SP * QS * MT == WAVES, "every wave sums one part of one group");
 };
 
 template <int MT, int WAVES>
 constexpr size_t tile_lds_bytes(int KG) {
   using T = Tile<MT, WAVES>;
-  const size_t loop = 2 * (size_t)T::XBUF + (size_t)WAVES * 64 * (KG | 1) * 4;
+  const size_t loop = 2 * (size_t)T::XBUF + (size_t)WAVES * 64 * (KG | 1) * 4 +
+                      (T::OWN_SUMS ? (size_t)T::SP * KG * T::MR * 4 : 0);
   const size_t emit = (size_t)WAVES * T::MR * kTRow * 4;
   return loop > emit ? loop : emit;
 }
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
   using T = Tile<MT, WAVES>;
   constexpr int K = NGC * 512, Q = K / 4, NG = NGC, KG = K / kGroup, KGP = KG | 1;
   constexpr int NST = NG * T::SPS;
@@ -67,10 +75,19 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xbuf = lds;                                             // [2][MR][RS]
   uint32_t* szl = reinterpret_cast<uint32_t*>(lds + 2 * T::XBUF);  // [WAVES][64][KGP]
+  float* xsl = reinterpret_cast<float*>(szl + WAVES * 64 * KGP);    // [SP][KG][MR]: parts of the group sums
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
   const int n0 = b * kBlockN;
+  // zc (may be null): one int per row, set to 0 (the arrival counters of the head's tail)
+  if (zc != nullptr && blockIdx.x == 0 && tid < M) zc[tid] = 0;
+  // xs null (tiles of up to 32 rows; the 64-row tile has no registers to spare): the group sums of
+  // x are taken here, this wave summing slices sq_s0 .. sq_s0 + 4/SP - 1 of quarter sq_q of each
+  // stage for row tile sq_mt
+  const bool own = T::OWN_SUMS && xs == nullptr;
+  const int sq_grp = wave / T::SP, sq_part = wave % T::SP;
+  const int sq_q = sq_grp / MT, sq_mt = sq_grp % MT, sq_s0 = sq_part * (4 / T::SP);
 
   // --- x stages: unit u = tid + THREADS i is 16 bytes (8 k) of row m, quarter t0 + q; the 16
   // units of a (row, quarter) group sit in 16 consecutive lanes. Every load is issued
@@ -196,6 +213,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const DqConst dqc = dq_const();
   const uint32_t* szc = szw + col * KGP;
+  f32x4 ps = {0.f, 0.f, 0.f, 0.f};  // this wave's part of a group sum of x (every column alike)
 
   auto compute = [&](int st, int slot, bool clamp) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
@@ -252,10 +270,22 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
             p[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt],
                                                                 0, 0, 0);
         }
+        if (own && qq == sq_q && (unsigned)(s - sq_s0) < (unsigned)(4 / T::SP)) {
+          const u32x4 as = *reinterpret_cast<const u32x4*>(xa + sq_mt * 16 * T::RS + qq * 256 + 16 * (s & 1) +
+                                                            128 * (s >> 1));
+          const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+          ps = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as), ones, ps, 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < kPerSlice; ++j) stage_load(st, slot, (qq * 4 + s) * kPerSlice + j, clamp);
         // the scheduler may not pull later slices (their x fragments and dequant) into this one
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (own && qq == sq_q) {
+        // ps[r]: this wave's part of the sum of group t NG + gb for row 16 sq_mt + 4 h + r
+        if (col == 0)
+          *reinterpret_cast<f32x4*>(xsl + (sq_part * KG + t * NG + gb) * T::MR + 16 * sq_mt + 4 * h) = ps;
+        ps = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       // the scale term of the group (the zero term is added after the loop)
       const int gi = t * NG + gb;
@@ -321,6 +351,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   // bf16 parts, -xs (fp32) into three and z (at most 16 significant bits for the scales the packer
   // writes) into two, and each group takes the 8 k-slots of one lane block: the six cross products
   // and two zeros. Step ks covers groups 4 ks + h.
+  if (own) __syncthreads();  // every part of every group sum is in LDS
 #pragma unroll 2
   for (int ks = 0; ks < KG / 4; ++ks) {
     const int g = 4 * ks + h, t = g / NG;
@@ -329,7 +360,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = 16 * mt + col;
-      const float v = -xs[(int64_t)(m < M ? m : M - 1) * KG + g];
+      float v;
+      if (own) {
+        float sm = xsl[g * T::MR + m];
+        if constexpr (T::SP > 1) sm += xsl[(KG + g) * T::MR + m];
+        v = -sm;
+      } else {
+        v = -xs[(int64_t)(m < M ? m : M - 1) * KG + g];
+      }
       const uint32_t p1 = __float_as_uint(v) & 0xffff0000u;
       const float r1 = v - __uint_as_float(p1);
       const uint32_t p2 = __float_as_uint(r1) & 0xffff0000u;
@@ -396,12 +434,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 
 template <int MT, int WAVES, int NGC>
 int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-                const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+                const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = tile_lds_bytes<MT, WAVES>(NGC * 4);
   hipLaunchKernelGGL((coarse_tile_kernel<MT, WAVES, NGC, I2H_TILE_XPF, I2H_TILE_RPF>),
                      dim3((unsigned)((nblk + WAVES - 1) / WAVES)), dim3(64 * WAVES), lds, s, x, xs, M, packed, S, ZS, N,
-                     kc, nblk, cs, ci, y);
+                     kc, nblk, cs, ci, y, zc);
   return check_launch();
 }
 
@@ -422,18 +460,19 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
 
 template <int NGC>
 int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-              const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
-  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+              const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc, hipStream_t s) {
+  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
   if constexpr (I2H_TILE_MAXMT >= 2)
-    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
-  if constexpr (I2H_TILE_MAXMT >= 4) return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, s);
+    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
+  if constexpr (I2H_TILE_MAXMT >= 4)
+    return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
   // rows in chunks of 16 through the 16-row tile (a build limited to it)
   const int64_t ld = nblk_of(N) * kc, KG = NGC * 4;
   for (int m0 = 0; m0 < M; m0 += 16) {
     const int mc = M - m0 < 16 ? M - m0 : 16;
     const int st = launch_tile<1, I2H_TILE_WAVES, NGC>(x + (int64_t)m0 * NGC * 512, xs ? xs + (int64_t)m0 * KG : nullptr,
                                                        mc, packed, S, ZS, N, kc, cs + m0 * ld, ci + m0 * ld,
-                                                       y ? y + (int64_t)m0 * N : nullptr, s);
+                                                       y ? y + (int64_t)m0 * N : nullptr, zc ? zc + m0 : nullptr, s);
     if (st != I2H_OK) return st;
   }
   return I2H_OK;
@@ -447,18 +486,20 @@ bool tile_supported(int64_t M, int64_t K) {
          (K == 512 || K == 1024 || K == 2048 || K == 3072 || K == 4096 || K == 5120);
 }
 
+bool tile_sums_x(int64_t M, int64_t K) { return tile_supported(M, K) && M <= 32; }
+
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
-                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
+                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
                 hipStream_t s) {
   if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
-  if (!xs) return I2H_ERR_ARG;
+  if (!xs && !tile_sums_x(M, K)) return I2H_ERR_ARG;
   switch (K / 512) {
-    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
-    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, s);
+    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
   }
 }
 

@@ -29,11 +29,13 @@ inline int64_t nblk_of(int64_t N) { return (N + I2H_BLOCK_N - 1) / I2H_BLOCK_N; 
 bool coarse_sums_x(int64_t M, int64_t K);
 
 // The many-row coarse kernel (coarse_tile.hip): up to kTileMaxRows rows of x per launch, for the
-// K it is built for; it takes the group sums xs (never null) from i2h_xsum.
+// K it is built for; it takes the group sums xs from i2h_xsum, or sums x itself when xs is null
+// and tile_sums_x (up to 32 rows). zc (may be null): M ints the launch sets to 0.
 constexpr int64_t kTileMaxRows = 64;
 bool tile_supported(int64_t M, int64_t K);
+bool tile_sums_x(int64_t M, int64_t K);
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
-                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y,
+                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
                 hipStream_t s);
 
 // The fused selection + exact rerank + top-k kernel (select_rerank.hip) and its limits.
@@ -48,7 +50,7 @@ int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64
                          int32_t* cnt = nullptr, float* exw = nullptr);
 
 // Entry points used by i2h_head (same checks and kernels as the exported calls). zero_cnt (may be
-// null): M ints the launch sets to 0; coarse_launch takes it only with xs null (the small kernel).
+// null): M ints the launch sets to 0; coarse_launch takes it only with xs null.
 int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s, int32_t* zero_cnt = nullptr);
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                   const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,

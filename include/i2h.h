@@ -119,10 +119,9 @@ I2H_API int i2h_xsum(const uint16_t* x, int64_t M, int64_t K, float* xs, void* s
  *   cand_score fp32 [M, NBLK*kcand] and cand_idx int32 [M, NBLK*kcand] (token index n);
  * slots past a tail block's real columns get (-inf, -1).
  *   x bf16 [M, K]; xs fp32 [M, K/128] from i2h_xsum; packed/S/ZS from i2h_pack. xs may be NULL
- *   when i2h_coarse_sums_x(M, K) is true (one row, or up to 4 rows at a K the many-row kernel
- *   is not built for): the kernel then holds x in LDS and sums its groups itself; otherwise a
- *   NULL xs is I2H_ERR_ARG. Results with xs given and with the kernel's own sums agree to fp32
- *   summation order.
+ *   when i2h_coarse_sums_x(M, K) is true: the kernels then sum the groups of x themselves;
+ *   otherwise a NULL xs is I2H_ERR_ARG. Results with xs given and with the kernels' own sums agree
+ *   to fp32 summation order.
  *   y   optional bf16 [M, N] (row stride N): the coarse logits rounded to nearest-even; NULL to skip.
  * Limits: M >= 1 (any size; rows are processed in chunks), 1 <= kcand <= 64.
  */
@@ -161,10 +160,11 @@ I2H_API int i2h_rerank(const uint16_t* x, int64_t M, const uint16_t* W, int64_t 
 I2H_API int i2h_finalize(const float* exact, const int32_t* sel, int64_t M, int R, int k,
                          int32_t* out_idx, float* out_val, void* stream);
 
-/* 1 if i2h_coarse_topk sums the groups of x itself for these sizes (xs may be NULL), else 0:
- * true for M = 1 (K up to 16384), and for 2 <= M <= 4 only where K is not one the many-row kernel
- * is built for (512, 1024, 2048, 3072, 4096, 5120: there it runs from 2 rows, with xs from
- * i2h_xsum). */
+/* 1 if i2h_coarse_topk sums the groups of x itself for these sizes (xs may be NULL), else 0.
+ * Rows go in chunks of 64; it is 1 when every chunk sums x itself: a one-row chunk when x fits in
+ * the one-row kernel's LDS (K up to 16384), a chunk of 2 to 32 rows at a K the many-row kernel is
+ * built for (512, 1024, 2048, 3072, 4096, 5120), and a chunk of 2 to 4 rows at another K when x
+ * fits in LDS. Chunks of 33 to 64 rows take xs from i2h_xsum. */
 I2H_API int i2h_coarse_sums_x(int64_t M, int64_t K);
 
 /*

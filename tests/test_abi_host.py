@@ -63,17 +63,20 @@ def test_coarse_sums_x():
     assert lib.i2h_coarse_sums_x(1, 5120) == 1
     assert lib.i2h_coarse_sums_x(1, 1024) == 1
     assert lib.i2h_coarse_sums_x(3, 1536) == 1    # no tile kernel for this K: the small kernel
-    assert lib.i2h_coarse_sums_x(3, 4096) == 0    # the 16-row tile is built for K = 4096
-    assert lib.i2h_coarse_sums_x(4, 5120) == 0    # from 2 rows the tile kernel, with xs from i2h_xsum
-    assert lib.i2h_coarse_sums_x(2, 512) == 0
-    assert lib.i2h_coarse_sums_x(5, 5120) == 0
-    assert lib.i2h_coarse_sums_x(16, 5120) == 0
+    assert lib.i2h_coarse_sums_x(3, 4096) == 1    # 2..32 rows: the 16- and 32-row tiles sum x themselves
+    assert lib.i2h_coarse_sums_x(2, 512) == 1
+    assert lib.i2h_coarse_sums_x(16, 5120) == 1
+    assert lib.i2h_coarse_sums_x(32, 5120) == 1
+    assert lib.i2h_coarse_sums_x(33, 5120) == 0   # the 64-row tile takes the sums from i2h_xsum
     assert lib.i2h_coarse_sums_x(64, 5120) == 0
+    assert lib.i2h_coarse_sums_x(65, 5120) == 0   # chunks of 64 and 1 rows
     assert lib.i2h_coarse_sums_x(130, 512) == 0   # chunks of 64, 64 and 2 rows
+    assert lib.i2h_coarse_sums_x(5, 1536) == 0    # no tile for this K and more than 4 rows
     assert lib.i2h_coarse_sums_x(4, 16384) == 0   # x does not fit in LDS
     assert lib.i2h_coarse_sums_x(1, 1000) == 0
     c = lib.i2h_coarse_topk
-    assert c(P, None, 16, P, P, P, 4096, 1024, 8, P, P, None, None) == ARG  # xs required here
+    assert c(P, None, 40, P, P, P, 4096, 1024, 8, P, P, None, None) == ARG  # xs required here
+    assert c(P, None, 16, P, P, P, 4096, 1536, 8, P, P, None, None) == ARG  # generic kernel: xs required
     r = lib.i2h_rerank_topk
     assert r(P, 1, P, 512, 4096, 512, P, 32, 33, None, P, P, None) == LIMIT
     assert r(P, 1, P, 512, 4096, 512, P, 65, 1, None, P, P, None) == ARG     # exact needed for R > 64
