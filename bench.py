@@ -87,7 +87,7 @@ def head_bytes(M, N, K, kc=KC, R_=R, k=1, own_sums=False):
     return b
 
 
-COARSE_SOURCES = ("coarse.hip", "coarse_tile.hip", "dequant.h", "device_util.h")
+COARSE_SOURCES = ("coarse.hip", "coarse_tile.hip", "dequant.h", "device_util.h", "block_emit.h")
 
 
 def coarse_source_hash():
@@ -345,6 +345,67 @@ def traffic_probe(torch, i2h, si, dev):
     print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(), "M": [1, 16, 32, 64]}), flush=True)
 
 
+# Windows within which a final place that differs from the oracle's is excused: two reranked tokens
+# whose exact scores (fp64) tie within EXACT_TIE, or a selected set that differs from the oracle's
+# only by tokens whose coarse scores lie within COARSE_TIE * max|c| of the oracle's R-th best. The
+# tight windows are counted beside them.
+EXACT_TIE, EXACT_TIE_TIGHT = 1e-3, 1e-5
+COARSE_TIE, COARSE_TIE_TIGHT = 2e-3, 1e-4
+
+
+def gpu_batches(i2h, torch, np, x, packed, S, ZS, W, M, k):
+    """(idx [rows, k], sel [rows, R]) for the rows of x in calls of M rows: i2h_head's answer, and
+    the selection from the same kernels called through their entry points (the coarse pass and the
+    fused tail with its selection), whose answer must equal i2h_head's."""
+    K = x.shape[1]
+    idx, sel = [], []
+    for r0 in range(0, x.shape[0], M):
+        xb = x[r0:r0 + M].contiguous()
+        hi, _ = i2h.head(xb, packed, S, ZS, W, kcand=KC, R=R, k=k)
+        xs = None if i2h.coarse_sums_x(xb.shape[0], K) else i2h.xsum(xb)
+        cs, ci, _ = i2h.coarse_topk(xb, xs, packed, S, ZS, kcand=KC)
+        oi, _, sl, _ = i2h.select_rerank_topk(cs, ci, KC, R, xb, W, k, want_sel=True)
+        if not torch.equal(hi, oi):
+            raise RuntimeError("i2h_head differs from its kernels called through their entry points")
+        idx.append(hi.cpu().numpy())
+        sel.append(sl.cpu().numpy())
+    return np.concatenate(idx), np.concatenate(sel)
+
+
+def classify(oracle, np, gpu_idx, gpu_sel, res, xb, Wb):
+    """Final places of the GPU against the oracle's: equal, excused (an exact-score tie inside an
+    equal selection, or a selection that differs at its edge), or unexcused."""
+    c, so, io = res["coarse"], res["sel"], res["idx"]
+    rows, k = gpu_idx.shape
+    scale = np.abs(c).max(axis=1)
+    n = dict(rows=int(rows), places=int(rows * k), match=0, exact_tie=0, exact_tie_tight=0, selection_edge=0,
+             selection_edge_tight=0, unexcused=0)
+    for m in range(rows):
+        go = set(int(t) for t in gpu_sel[m] if t >= 0)
+        oo = set(int(t) for t in so[m] if t >= 0)
+        for j in range(k):
+            a, b = int(gpu_idx[m, j]), int(io[m, j])
+            if a == b:
+                n["match"] += 1
+                continue
+            if go == oo:
+                e = oracle.rerank_exact(xb[m:m + 1], Wb, np.array([[a, b]], np.int32))[0]
+                gap = abs(e[0] - e[1])
+                key, tight = ("exact_tie", gap <= EXACT_TIE_TIGHT) if gap <= EXACT_TIE else (None, False)
+            else:
+                thr = c[m, so[m][len(oo) - 1]]
+                gap = max(abs(c[m, t] - thr) for t in go ^ oo) / scale[m]
+                key, tight = ("selection_edge", gap <= COARSE_TIE_TIGHT) if gap <= COARSE_TIE else (None, False)
+            if key is None:
+                n["unexcused"] += 1
+            else:
+                n[key] += 1
+                n[key + "_tight"] += int(tight)
+    n["match_pct"] = round(100.0 * n["match"] / n["places"], 3)
+    n["match_or_excused_pct"] = round(100.0 * (n["places"] - n["unexcused"]) / n["places"], 3)
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,7 +416,10 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the coarse kernel 6 times per M in (1, 16, 32, 64) on cold weight copies, "
                          "then copy a 512 MiB buffer 4 times (the calibration kernel for HBM byte counters)")
-    ap.add_argument("--match-rows", type=int, default=32)
+    ap.add_argument("--match-rows", type=int, default=1024,
+                    help="rows of x compared with the oracle at M = 1, 16 and 64 (and the tiny head)")
+    ap.add_argument("--match-rows-full-vocab", type=int, default=128,
+                    help="rows of x compared with the oracle on the full vocabulary (top-16, calls of 16 rows)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
@@ -381,7 +445,7 @@ def main():
     Wc = si.gen_weight(N, K)
     W = Wc.to(dev)
     nrows = max(args.match_rows, 64)
-    x_all_c = si.gen_x(nrows, K, outliers=cfg["outliers"])
+    x_all_c = si.gen_x(nrows, K, outliers=cfg["outliers"])  # the match rows (and the timed batches' rows)
     x_all = x_all_c.to(dev)
 
     # load-time pack, timed on its own
@@ -612,7 +676,8 @@ def main():
         reranked tokens) at each M of the band list, on 6 rotated packed copies (2.1 GB)."""
         cfg = si.WORKLOADS["full_vocab_top16_k5120_n248320"]
         Nf, Kf, kf = cfg["N"], cfg["K"], cfg["topk"]
-        Wf = si.gen_weight(Nf, Kf).to(dev)
+        Wf_c = si.gen_weight(Nf, Kf)
+        Wf = Wf_c.to(dev)
         pf = i2h.pack(Wf)
         pk = []
         for _ in range(5):
@@ -624,7 +689,8 @@ def main():
             pk.append(a.elapsed_time(b) * 1e3)
         pbytes = Nf * Kf * 2 + Nf * Kf // 4 + 2 * Nf * (Kf // 128) * 2
         cps = [pf] + [(pf[0].clone(), pf[1].clone(), pf[2].clone()) for _ in range(5)]
-        xf = si.gen_x(max(cfg["M"]), Kf, outliers=cfg["outliers"]).to(dev)
+        xf_c = si.gen_x(max(max(cfg["M"]), args.match_rows_full_vocab), Kf, outliers=cfg["outliers"])
+        xf = xf_c.to(dev)
         P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         s = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         L = i2h.lib()
@@ -635,10 +701,10 @@ def main():
             ov = torch.empty(Mf, kf, dtype=torch.float32, device=dev)
             wsn = i2h.workspace_bytes(Mf, Nf, Kf, KC, R)
             ws = torch.empty(max(wsn, 1), dtype=torch.uint8, device=dev)
-            args = [(P(x), Mf, P(p), P(S_), P(Z_), P(Wf), Wf.stride(0), Nf, Kf, KC, R, kf, P(oi), P(ov), None,
-                     P(ws), wsn, s) for (p, S_, Z_) in cps]
+            a_head = [(P(x), Mf, P(p), P(S_), P(Z_), P(Wf), Wf.stride(0), Nf, Kf, KC, R, kf, P(oi), P(ov), None,
+                       P(ws), wsn, s) for (p, S_, Z_) in cps]
             it = iter(range(1 << 30))
-            us_f = back_to_back_us(torch, lambda: L.i2h_head(*args[next(it) % len(args)]), steps, warmup)
+            us_f = back_to_back_us(torch, lambda: L.i2h_head(*a_head[next(it) % len(a_head)]), steps, warmup)
             hb_f = head_bytes(Mf, Nf, Kf, k=kf, own_sums=i2h.coarse_sums_x(Mf, Kf))
             fl = 2.0 * Mf * Kf * Nf
             rows.append(dict(M=Mf, us_per_call=round(us_f, 2), gbps=round(hb_f["total"] / us_f / 1e3, 1),
@@ -650,9 +716,45 @@ def main():
                    pack_gbps=round(pbytes / (float(np.median(pk)) * 1e-6) / 1e9, 1),
                    pack_hbm_frac=round(pbytes / (float(np.median(pk)) * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    calls=rows)
+        match = None
+        if not args.no_cpu_baseline:
+            # top-16 of the match rows in calls of 16 rows, for the comparison with the oracle
+            gi, gs = gpu_batches(i2h, torch, np, xf[:args.match_rows_full_vocab], *pf, Wf, 16, kf)
+            match = dict(W=Wf_c, x=xf_c[:args.match_rows_full_vocab], idx=gi, sel=gs, k=kf)
         del Wf, pf, cps
         torch.cuda.synchronize()
-        return res
+        return res, match
+
+    def measure_tiny(steps, warmup):
+        """The tiny head (M = 1, K = 512, N = 4096; 0.63 MB, resident in L2): i2h_head per call back
+        to back, the spread over single calls, and the GPU answers on the match rows."""
+        cfg = si.WORKLOADS["tiny_head_m1_k512_n4096"]
+        Nt, Kt = cfg["N"], cfg["K"]
+        Wt_c = si.gen_weight(Nt, Kt)
+        xt_c = si.gen_x(max(args.match_rows, 1), Kt, outliers=cfg["outliers"])
+        Wt, xt = Wt_c.to(dev), xt_c.to(dev)
+        pt = i2h.pack(Wt)
+        x1 = xt[:1].contiguous()
+        wsn = i2h.workspace_bytes(1, Nt, Kt, KC, R)
+        ws = torch.empty(wsn, dtype=torch.uint8, device=dev)
+        oi = torch.empty(1, 1, dtype=torch.int32, device=dev)
+        ov = torch.empty(1, 1, dtype=torch.float32, device=dev)
+        P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        s_ = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        a = (P(x1), 1, P(pt[0]), P(pt[1]), P(pt[2]), P(Wt), Wt.stride(0), Nt, Kt, KC, R, 1, P(oi), P(ov), None,
+             P(ws), wsn, s_)
+        L = i2h.lib()
+        us_t = back_to_back_us(torch, lambda: L.i2h_head(*a), steps, warmup)
+        pct_t = call_percentiles(torch, np, lambda i: L.i2h_head(*a), steps, warmup)
+        hb_t = head_bytes(1, Nt, Kt, own_sums=i2h.coarse_sums_x(1, Kt))
+        res = dict(workload="tiny_head_m1_k512_n4096", M=1, K=Kt, N=Nt, us_per_call=round(us_t, 2),
+                   us_per_call_p10_p50_p90=pct_t, bytes_per_call=hb_t["total"],
+                   note="0.63 MB of algorithmic bytes stay in L2: a latency figure, not a bandwidth one")
+        match = None
+        if not args.no_cpu_baseline:
+            gi, gs = gpu_batches(i2h, torch, np, xt[:args.match_rows], *pt, Wt, 1, 1)
+            match = dict(W=Wt_c, x=xt_c[:args.match_rows], idx=gi, sel=gs, k=1)
+        return res, match
 
     def measure_dropin(h, steps, warmup):
         """The drop-in logits row (argmax and top-k callers): per-call time and the write-back alone."""
@@ -690,10 +792,13 @@ def main():
     dropin = measure_dropin(h, args.steps, args.warmup)
     dropin["logits_bytes"] = {"argmax": M * N * 2 * 2 + M * R * 8, "topk": M * N * 2 + M * R * 8}
 
-    full_vocab = None
+    log("[bench] tiny head (M=1, K=512, N=4096)")
+    tiny, tiny_match = measure_tiny(args.steps, args.warmup)
+
+    full_vocab, fv_match = None, None
     if not args.no_bands:
         log("[bench] full vocabulary (248320 rows), top-16 caller: pack and one call per M")
-        full_vocab = measure_full_vocab(max(20, args.steps // 4), max(5, args.warmup // 2))
+        full_vocab, fv_match = measure_full_vocab(max(20, args.steps // 4), max(5, args.warmup // 2))
 
     bands = []
     if not args.no_bands:
@@ -707,48 +812,75 @@ def main():
                               us_per_call_graph=round(measure_graph(Mb, max(10, args.steps // 24)), 2),
                               coarse_us=round(cmsb * 1e3, 2),
                               gbps=round(hbb["total"] / dtfb / 1e9, 1),
+                              gbps_packed_only=round(N * K / 4 / dtfb / 1e9, 1),
+                              hbm_frac=round(hbb["total"] / dtfb / 1e9 / HBM_PEAK_GBS, 4),
                               coarse_gbps=round(hbb["coarse"] / (cmsb * 1e-3) / 1e9, 1),
+                              coarse_gbps_packed_only=round(N * K / 4 / (cmsb * 1e-3) / 1e9, 1),
                               coarse_hbm_frac=round(hbb["coarse"] / (cmsb * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               coarse_tflops_useful=round(flops / (cmsb * 1e-3) / 1e12, 2),
                               mfma_util_useful=round(flops / (cmsb * 1e-3) / 1e12 / BF16_PEAK_TFS, 4),
-                              coarse_traffic_bytes=traffic_for(Mb)))
+                              coarse_traffic_bytes=traffic_for(Mb), group_sums_in_kernel=hbh.own_sums))
 
-    # argmax match against the oracle on the first rows, one call per row as in the timed step
+    # The CPU leg: the oracle timed on the host cores, and the GPU answers compared with the
+    # oracle's on every configuration (the tiny head; the draft slot at M = 1, 16, 64 on the same
+    # rows; the full vocabulary's top-16)
     result = {}
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        log(f"[bench] argmax match on {args.match_rows} rows (GPU calls of M=1)")
-        got = []
-        for r in range(args.match_rows):
-            idx, _ = i2h.head(x_all[r:r + 1].contiguous(), packed, S, ZS, W, kcand=KC, R=R, k=1)
-            got.append(int(idx.item()))
+        log(f"[bench] GPU answers on {args.match_rows} rows in calls of 1, 16 and 64 rows")
+        xm = x_all[:args.match_rows]
+        gpu_rows = {Mb: gpu_batches(i2h, torch, np, xm, packed, S, ZS, W, Mb, 1) for Mb in (1, 16, 64)}
         Wb, xb = si.bits(Wc), si.bits(x_all_c[:args.match_rows])
+        threads = oracle.int2_head._threads()
+        try:
+            affinity = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            affinity = os.cpu_count() or 1
         log("[bench] oracle pack (untimed, load-time step)")
         po, So, ZSo = oracle.pack(Wb)
-        threads = oracle.int2_head._threads()
-        log("[bench] oracle head, one call of the timed workload (timed)")
-        t0 = time.perf_counter()
-        r1 = oracle.head(xb[:1], Wb, po, So, ZSo, kcand=KC, R=R, k=1)
-        cpu_s = time.perf_counter() - t0
-        log("[bench] oracle head on the match rows")
+        log("[bench] oracle head, single calls of the timed workload (timed, median of 5)")
+        ts_ = []
+        for r in range(5):
+            t0 = time.perf_counter()
+            r1 = oracle.head(xb[r:r + 1], Wb, po, So, ZSo, kcand=KC, R=R, k=1)
+            ts_.append(time.perf_counter() - t0)
+        cpu_s = float(np.median(ts_))
+        log(f"[bench] oracle head on the {args.match_rows} match rows")
         ro = oracle.head(xb, Wb, po, So, ZSo, kcand=KC, R=R, k=1)
-        want = [int(v) for v in ro["idx"][:, 0]]
-        match = sum(int(a == b) for a, b in zip(got, want))
-        ex = oracle.exact_logits(xb, Wb)
-        recall = sum(int(a == b) for a, b in zip(want, ex.argmax(1)))
-        dense = ex.argmax(1)
-        result = dict(argmax_match_pct=round(100.0 * match / len(want), 2), argmax_rows=len(want),
+        assert int(r1["idx"][0, 0]) == int(ro["idx"][4, 0])
+        match = {}
+        for Mb, name in ((1, "draft_slot_m1"), (16, "draft_band_m16"), (64, "draft_band_m64")):
+            match[name] = classify(oracle, np, gpu_rows[Mb][0], gpu_rows[Mb][1], ro, xb, Wb)
+        want = ro["idx"][:, 0]
+        dense = oracle.exact_logits(xb, Wb).argmax(1)
+        recall = int((want == dense).sum())
+        log("[bench] oracle on the tiny head")
+        po_t = oracle.pack(si.bits(tiny_match["W"]))
+        xtb = si.bits(tiny_match["x"])
+        rt = oracle.head(xtb, si.bits(tiny_match["W"]), *po_t, kcand=KC, R=R, k=1)
+        match["tiny_head_m1"] = classify(oracle, np, tiny_match["idx"], tiny_match["sel"], rt, xtb,
+                                         si.bits(tiny_match["W"]))
+        if fv_match is not None:
+            log(f"[bench] oracle on the full vocabulary, {fv_match['x'].shape[0]} rows (top-16)")
+            Wfb, xfb = si.bits(fv_match["W"]), si.bits(fv_match["x"])
+            rf = oracle.head(xfb, Wfb, *oracle.pack(Wfb), kcand=KC, R=R, k=fv_match["k"])
+            match["full_vocab_top16_m16"] = classify(oracle, np, fv_match["idx"], fv_match["sel"], rf, xfb, Wfb)
+            del Wfb, rf
+        result = dict(argmax_match_pct=match["draft_slot_m1"]["match_pct"], argmax_rows=len(want),
+                      argmax_match=match,
+                      argmax_match_windows=dict(exact_tie=EXACT_TIE, exact_tie_tight=EXACT_TIE_TIGHT,
+                                                selection_edge=COARSE_TIE, selection_edge_tight=COARSE_TIE_TIGHT),
                       recall_vs_dense_bf16_pct=round(100.0 * recall / len(want), 2))
+        nr = min(len(want), len(selab["argmax_rows"]))
         selab["token_level_recall_vs_dense_bf16_pct"] = round(
-            100.0 * sum(int(a == b) for a, b in zip(selab["argmax_rows"], dense)) / len(want), 2)
+            100.0 * sum(int(a == b) for a, b in zip(selab["argmax_rows"][:nr], dense[:nr])) / nr, 2)
         int4["recall_vs_dense_bf16_pct"] = round(
-            100.0 * sum(int(a == b) for a, b in zip(int4["argmax_rows"], dense)) / len(want), 2)
-        assert int(r1["idx"][0, 0]) == want[0]
+            100.0 * sum(int(a == b) for a, b in zip(int4["argmax_rows"][:nr], dense[:nr])) / nr, 2)
         cpu = dict(value=round(hb["total"] / cpu_s / 1e9, 4), unit="GB/s", us_per_call=round(cpu_s * 1e6, 1),
-                   cores=threads, kind="oracle",
-                   sample=f"one call of the {WORKLOAD} head (coarse over all {N} rows, emit, select, rerank, "
-                          f"argmax) on the numpy oracle with {threads} threads; pack excluded")
+                   cores=threads, affinity_cores=affinity, kind="oracle",
+                   sample=f"5 single-row calls of the {WORKLOAD} head (coarse over all {N} rows, emit, select, "
+                          f"rerank, argmax) on the numpy oracle with {threads} threads, median; pack excluded")
 
     out = {
         "metric": METRIC,
@@ -787,6 +919,7 @@ def main():
         **result,
         "bands": bands,
         "full_vocab_top16": full_vocab,
+        "tiny_head": tiny,
         "device": device_info(torch),
         "cpu_baseline": cpu,
     }

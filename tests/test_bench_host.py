@@ -53,3 +53,36 @@ def test_gpus_other_than_one_exit_with_a_message(capsys, monkeypatch):
     else:  # pragma: no cover
         raise AssertionError("bench.py --gpus 2 did not exit")
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_match_classification_on_oracle_outputs():
+    """The bench's comparison of final places with the oracle: identical answers match, a token
+    far from the oracle's is unexcused, and a selection that swaps the oracle's R-th token for the
+    (R+1)-th is excused at the selection edge when their coarse scores are close."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs as si
+    N, K = 4096, 512
+    Wb = si.bits(si.gen_weight(N, K, seed=91))
+    xb = si.bits(si.gen_x(6, K, seed=92))
+    res = oracle.head(xb, Wb, *oracle.pack(Wb), kcand=8, R=32, k=1)
+    n = bench.classify(oracle, np, res["idx"].copy(), res["sel"].copy(), res, xb, Wb)
+    assert n["match"] == 6 and n["unexcused"] == 0 and n["match_pct"] == 100.0
+    idx = res["idx"].copy()
+    worst = np.argsort(res["coarse"][0])[0]           # the row's lowest coarse logit: far below the winner
+    idx[0, 0] = worst
+    n = bench.classify(oracle, np, idx, res["sel"].copy(), res, xb, Wb)
+    assert n["match"] == 5 and n["unexcused"] == 1
+    # row 1: swap the oracle's 32nd selected token for the best unselected candidate
+    c = res["coarse"][1]
+    cand = [t for t in res["cand_idx"][1] if t >= 0 and t not in set(res["sel"][1])]
+    nxt = max(cand, key=lambda t: (c[t], -t))
+    sel = res["sel"].copy()
+    sel[1, -1] = nxt
+    idx = res["idx"].copy()
+    idx[1, 0] = nxt
+    n = bench.classify(oracle, np, idx, sel, res, xb, Wb)
+    gap = abs(c[nxt] - c[res["sel"][1, -1]]) / np.abs(c).max()
+    assert (n["selection_edge"] == 1) == (gap <= bench.COARSE_TIE)
+    assert n["match"] == 5
