@@ -325,8 +325,15 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     }
   } else {
     // more rows: a runtime loop over groups of kSlots spans, each span's stages unrolled with
-    // its ring slot fixed
+    // its ring slot fixed. The 32-bit x and packed-row offsets are re-pinned every iteration, so
+    // that the compiler recomputes each load's address in the loop rather than hoisting 64-bit
+    // addresses out of it (at K = 4096 and 3072 those spilled to scratch, and each reload waited
+    // for every load in flight)
     for (int g0 = 0; g0 < NG; g0 += kSlots) {
+#pragma unroll
+      for (int i = 0; i < T::UPT; ++i) asm volatile("" : "+v"(xo[i]));
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) asm volatile("" : "+v"(poff[nt]));
 #pragma unroll
       for (int sl = 0; sl < kSlots; ++sl) {
         const int gb = g0 + sl;
