@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-bands]
     python bench.py --traffic-probe    # short run for rocprofv3 counter passes (see below)
+    python bench.py --variant-probe    # the same for the design alternatives
 
 A step is one call of the head's per-call entry point i2h_head over one batch: the coarse int2
 pass with its fused block top-8 emit (which sums the groups of x itself), then the top-32
@@ -36,9 +37,10 @@ how often its argmax equals the dense bf16 argmax on the match rows (beside the 
 `ablations.selection` sets the block candidates against a token-level top-R over the whole bf16
 coarse row (i2h_select_tokens, then the exact rerank and argmax): per call, the tail alone and the
 selection alone, with the token-level path's argmax agreement with the dense bf16 argmax.
-`ablations.coarse_variants` times one coarse kernel family in four forms that differ in one
-property each (the design: group 128, quarter-split, scale on the accumulator; group 64;
-contiguous-4 bytes; dequantised weight tile) at M = 1 and 16 on cold copies, with each pack.
+`ablations.coarse_variants` times the production coarse kernels in four forms that differ in one
+property each (the design itself: group 128, quarter-split, scale on the accumulator; group 64;
+contiguous-4 bytes; dequantised weight tile) at M = 1 (the one-row kernel) and 16 (the 16-row
+tile), group sums taken in the kernel as the head does, on cold copies, with each pack.
 `bands` times the per-call path and the coarse kernel alone at M = 16, 32, 64 on the same slice;
 `full_vocab_top16` the unsharded 248320-row vocabulary with the top-16 caller: the GPU pack of its
 bf16 weight, and one i2h_head call at each M in (1, 2, 4, 8, 16, 32, 64, 72) on cold copies.
@@ -345,6 +347,29 @@ def traffic_probe(torch, i2h, si, dev):
     print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(), "M": [1, 16, 32, 64]}), flush=True)
 
 
+def variant_probe(torch, i2h, si, dev):
+    """Launches for rocprofv3 counter passes over the design alternatives: each of the four forms
+    (design, group 64, contiguous-4, weight tile) packed from the timed workload's weight, then its
+    coarse kernel at M = 1 and 16 on 4 cold copies, 6 launches each."""
+    cfg = si.WORKLOADS[WORKLOAD]
+    K, N = cfg["K"], cfg["N"]
+    W = si.gen_weight(N, K).to(dev)
+    x_all = si.gen_x(16, K, outliers=cfg["outliers"]).to(dev)
+    combos = ((128, "quarter", "accumulator"), (64, "quarter", "accumulator"), (128, "contiguous", "accumulator"),
+              (128, "quarter", "tile"))
+    for g, lay, sc in combos:
+        pk = i2h.pack_variant(W, g, lay)
+        cps = [pk] + [tuple(u.clone() for u in pk) for _ in range(3)]
+        for M in (1, 16):
+            x = x_all[:M].contiguous()
+            for i in range(6):
+                p, a, b = cps[i % 4]
+                i2h.coarse_variant_topk(x, None, p, a, b, g, lay, sc, KC)
+            torch.cuda.synchronize()
+        del cps, pk
+    print(json.dumps({"variant_probe": True, "M": [1, 16]}), flush=True)
+
+
 # Windows within which a final place that differs from the oracle's is excused: two reranked tokens
 # whose exact scores (fp64) tie within EXACT_TIE, or a selected set that differs from the oracle's
 # only by tokens whose coarse scores lie within COARSE_TIE * max|c| of the oracle's R-th best. The
@@ -413,6 +438,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bands", action="store_true")
+    ap.add_argument("--variant-probe", action="store_true",
+                    help="launch each design alternative at M = 1 and 16 (for rocprofv3 counter passes) and exit")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the coarse kernel 6 times per M in (1, 16, 32, 64) on cold weight copies, "
                          "then copy a 512 MiB buffer 4 times (the calibration kernel for HBM byte counters)")
@@ -434,6 +461,9 @@ def main():
 
     i2h.lib()
     dev = torch.device("cuda:0")
+    if args.variant_probe:
+        variant_probe(torch, i2h, si, dev)
+        return
     if args.traffic_probe:
         traffic_probe(torch, i2h, si, dev)
         return
@@ -651,7 +681,7 @@ def main():
                      weight_bytes=N * K // 4 + 2 * N * (K // g) * 2)
             for Mv in (1, 16):
                 xv = x_all[:Mv].contiguous()
-                xs = i2h.xsum_group(xv, g) if sc == "accumulator" else None
+                xs = None  # group sums taken in the kernel, as the head's calls do
                 cs = torch.empty(Mv, nblk * KC, dtype=torch.float32, device=dev)
                 ci = torch.empty(Mv, nblk * KC, dtype=torch.int32, device=dev)
                 lay_c, sc_c = (0 if lay == "quarter" else 1), (0 if sc == "accumulator" else 1)

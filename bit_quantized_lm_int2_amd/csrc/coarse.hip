@@ -19,6 +19,7 @@
 // lets the x fragment be one contiguous 16-byte load.
 #include <type_traits>
 
+#include "ablation.h"
 #include "dequant.h"
 #include "host_util.h"
 
@@ -208,11 +209,10 @@ constexpr int kHalfOff = I2H_SMALL_SECTOR ? 64 : 16;  // byte offset of its seco
 #define I2H_COARSE_SLICE_FENCE 1
 #endif  // 128-byte spans of the packed stream in flight per lane
 
-// LDS footprint of coarse_small_kernel in bytes: S|ZS for the block's rows, xs transposed, the
-// block's 64-bit ranking keys, and (xrows > 0) x itself.
-__host__ __device__ constexpr size_t small_lds_bytes(int K, int xrows) {
-  return (size_t)64 * (K / kGroup) * 4 + (size_t)(K / kGroup) * 16 * 4 + (size_t)16 * kBlockN * 8 +
-         (size_t)xrows * K * 2;
+// LDS footprint of coarse_small_kernel in bytes: S|ZS for the block's rows, xs transposed (G: the
+// quantisation group), the block's 64-bit ranking keys, and (xrows > 0) x itself.
+__host__ __device__ constexpr size_t small_lds_bytes(int K, int xrows, int G = kGroup) {
+  return (size_t)64 * (K / G) * 4 + (size_t)(K / G) * 16 * 4 + (size_t)16 * kBlockN * 8 + (size_t)xrows * K * 2;
 }
 
 // Ranking key of a coarse logit in its block: higher value first, then lower column.
@@ -252,18 +252,26 @@ __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, in
 // NGC > 0: the number of 128-byte spans per packed row (K / 512) is a compile-time constant and
 // the span loop is unrolled completely, so every wait for a prefetched span is exact; NGC = 0
 // runs the loop at run time (the compiler then waits for all loads at each loop header).
-template <int MAXR, bool XLDS, int NGC>
+// VAR (ablation.h): the design, or one alternative (one row, x in LDS, NGC > 0 only): group 64
+// splits each quarter's partial sum in two at k = 64 (the lane's second 16-byte load starts
+// there); contiguous-4 takes four 8-byte runs per span, 32 consecutive k of each of the span's
+// four groups, with x in LDS in natural order; the weight tile feeds the dequantised weights to
+// the matrix cores and needs no group sums.
+template <int MAXR, bool XLDS, int NGC, int VAR = kVarDesign>
 __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
     int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
   constexpr int RR = MAXR < 4 ? MAXR : 4;  // accumulator rows per lane that can be real
+  static_assert(VAR == kVarDesign || (MAXR == 1 && XLDS && NGC > 0), "alternatives: one row, x in LDS");
+  constexpr int GV = VAR == kVarG64 ? 64 : kGroup;  // quantisation group along k
+  constexpr bool kSums = VAR != kVarWTile;           // the accumulator form needs the group sums
   // zc (may be null): one int per row, set to 0 (the arrival counters of the head's tail)
   if (zc != nullptr && blockIdx.x == 0 && (int)threadIdx.x < M) zc[threadIdx.x] = 0;
   extern __shared__ __align__(16) uint32_t lds[];
   if constexpr (NGC > 0) K = NGC * 512;
-  const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / kGroup;
+  const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / GV;
   uint32_t* sz = lds;                                        // [64][KG]: S | ZS << 16
   float* xsT = reinterpret_cast<float*>(sz + 64 * KG);       // [KG][16]
   uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * 16);  // [16][64] ranking keys
@@ -288,7 +296,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       xr[i] = u < xunits ? ld16(x + 8 * u) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  constexpr int kSzW = NGC > 0 ? (NGC + 7) / 8 : 4;  // 16-byte S units per lane: 16 rows * KG / 8 / 64 (KG <= 128)
+  // 16-byte S units per lane: 16 rows * KG / 8 / 64 (KG <= 128)
+  constexpr int kSzW = NGC > 0 ? (2 * NGC * 4 * (kGroup / GV) + 63) / 64 : 4;
   const int rows_valid = N - n0 < kBlockN ? N - n0 : kBlockN;
   const int tot = rows_valid * KG;                   // valid elements of the block's S
   const int wbase = wave * 16 * KG;                  // this wave's rows start here
@@ -313,20 +322,34 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
       }
     }
   }
-  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + kLaneOff * h;
+  // contiguous-4: lane h reads 8 bytes of each of the span's four groups (at 32 i + 8 h)
+  const uint8_t* prow = packed + (int64_t)(nvalid ? n : 0) * Q + (VAR == kVarC4 ? 8 : kLaneOff) * h;
   u32x4 ring[kPf][2];
+  auto span_load = [&](int g, u32x4 (&r)[2]) {
+    if constexpr (VAR == kVarC4) {
+      typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+      u32x2 v[4];
 #pragma unroll
-  for (int p = 0; p < kPf; ++p) {
-    const int g = p < NG ? p : NG - 1;
-    ring[p][0] = ld16(prow + g * kGroup);
-    ring[p][1] = ld16(prow + g * kGroup + kHalfOff);
-  }
+      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x2*>(prow + g * kGroup + 32 * i);
+      r[0] = u32x4{v[0][0], v[0][1], v[1][0], v[1][1]};
+      r[1] = u32x4{v[2][0], v[2][1], v[3][0], v[3][1]};
+    } else {
+      r[0] = ld16(prow + g * kGroup);
+      r[1] = ld16(prow + g * kGroup + kHalfOff);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < kPf; ++p) span_load(p < NG ? p : NG - 1, ring[p]);
 
   // x rows in LDS, laid out by span: xl[m][gb][t][j] holds x[m][t Q + 128 gb + j], so the four
   // quarters of span gb sit 128 apart and every fragment offset is an immediate; each group of
   // four k is stored as (0, 2, 1, 3), the order in which the mask dequant of a raw packed dword
   // yields its weights, so the packed bytes need no permute
   auto put_x = [&](int u, const u32x4& v) {
+    if constexpr (VAR == kVarC4) {  // natural order, the layout of x itself
+      *reinterpret_cast<u32x4*>(xl + 8 * u) = v;
+      return;
+    }
     const u32x4 o = x_pair_order(v);
     const int m = (8 * u) / K, k = 8 * u - m * K;
     const int t = k / Q, r = k - t * Q;
@@ -337,33 +360,33 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     for (int i = 0; i < kXU; ++i) {
       const int u = tid + i * kCoarseThreads;
       if (u < xunits) put_x(u, xr[i]);
-      if (xs == nullptr) {
-        // the 16 units of a group of 128 k sit in 16 consecutive lanes
+      if (kSums && xs == nullptr) {
+        // the GV / 8 units of a group sit in consecutive lanes
         float sm = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sm += bf16_lo(xr[i][e]) + bf16_hi(xr[i][e]);
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o);
-        if ((tid & 15) == 0 && u < xunits) {
-          const int m = (8 * u) / K, g = (8 * u - m * K) / kGroup;
+        for (int o = 1; o < GV / 8; o <<= 1) sm += __shfl_xor(sm, o);
+        if ((tid & (GV / 8 - 1)) == 0 && u < xunits) {
+          const int m = (8 * u) / K, g = (8 * u - m * K) / GV;
           xsT[g * 16 + m] = sm;
         }
       }
     }
-    if (xs == nullptr)
+    if (kSums && xs == nullptr)
       for (int i = tid; i < KG * 16; i += kCoarseThreads)
         if ((i & 15) >= M) xsT[i] = 0.f;
   } else if constexpr (XLDS) {
     for (int u = tid; u < xunits; u += kCoarseThreads) put_x(u, ld16(x + 8 * u));
   }
-  if (xs != nullptr) {
+  if (kSums && xs != nullptr) {
     for (int i = tid; i < KG * 16; i += kCoarseThreads) {
       const int g = i >> 4, m = i & 15;
       xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
     }
   }
   __syncthreads();
-  if (!kXReg && xs == nullptr) {
+  if (!kXReg && kSums && xs == nullptr) {
     // group sums from the LDS copy of x (only launched so with x in LDS): one thread per group
     for (int i = tid; i < KG * 16; i += kCoarseThreads) {
       const int g = i >> 4, m = i & 15;
@@ -408,6 +431,37 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
   const DqConst dqc = dq_const();
 
   auto body = [&](int gb, const u32x4& c0, const u32x4& c1) {
+    if constexpr (VAR == kVarC4) {
+      // group i of the span (4 gb + i): run i is dwords 2 i, 2 i + 1 of (c0, c1); slice s reads
+      // its bytes 2 s, 2 s + 1 (k = 128 (4 gb + i) + 32 h + 8 s .. + 7)
+      const uint32_t rd[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      f32x4 p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* xa = xl + arow * K + gb * 512 + 32 * h;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 bw = dequant8_c4((rd[2 * i + (s >> 1)] >> (16 * (s & 1))) & 0xffffu);
+          const u32x4 a = *reinterpret_cast<const u32x4*>(xa + 128 * i + 8 * s);
+          p[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[i], 0, 0, 0);
+        }
+#if I2H_COARSE_SLICE_FENCE
+        __builtin_amdgcn_sched_barrier(0);
+#endif
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // codes read at D = 4: the scale and zero as they are
+        const int gi = 4 * gb + i;
+        const uint32_t w = szr[gi];
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
+#pragma unroll
+        for (int r = 0; r < RR; ++r)
+          acc[r] = fmaf(-xv[r], __uint_as_float(w & 0xffff0000u), fmaf(__uint_as_float(w << 16), p[i][r], acc[r]));
+      }
+      return;
+    }
     uint32_t dw[8], hw[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -416,9 +470,40 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) hw[i] = dw[i] >> 8;
+    // group 64: each quarter's group ends at k = 64 (after slice 1) and at k = 128 (after slice 3),
+    // and each is scaled and folded into the result where it ends
+    constexpr int HV = VAR == kVarG64 ? 2 : 1;
     f32x4 p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) p[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto fold = [&](int hf) {  // scale and zero of the groups that end here
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int gi = HV * (t * NG + gb) + hf;
+        const uint32_t w = szr[gi];
+        const float sv = __uint_as_float(w << 16);
+        const float zv = __uint_as_float(w & 0xffff0000u);
+        const float s2 = kBiasF[t] * sv;
+        const float z2 = fmaf(kBiasF[t] - 1.f, sv, zv);
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
+#pragma unroll
+        for (int r = 0; r < RR; ++r) {
+          const float a = fmaf(s2, p[t][r], acc[r]);
+          acc[r] = fmaf(-xv[r], z2, a);
+        }
+        p[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    };
+    // weight tile: each quarter's f S and (f - 1) S + ZS, which the dequantised weights take
+    float s1[4], z1[4];
+    if constexpr (VAR == kVarWTile) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t w = szr[t * NG + gb];
+        s1[t] = kBiasF[t] * __uint_as_float(w << 16);
+        z1[t] = fmaf(kBiasF[t] - 1.f, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+      }
+    }
     const uint16_t* xa = XLDS ? xl + arow * K + gb * 512 + kLaneOff * h : x + (int64_t)arow * K + gb * kGroup + kLaneOff * h;
     // k offset of slice s within lane h's part of the group
     auto soff = [](int s_) { return I2H_SMALL_SECTOR ? 8 * (s_ & 1) + 64 * (s_ >> 1) : 8 * s_; };
@@ -435,28 +520,22 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
         u32x4 a;
         if constexpr (XLDS) a = *reinterpret_cast<const u32x4*>(xa + t * kGroup + soff(s));
         else a = ld16(xa + t * Q + soff(s));
-        p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
+        if constexpr (VAR == kVarWTile)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), tile8_fold(bw, s1[t], z1[t]),
+                                                        acc, 0, 0, 0);
+        else
+          p[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), bw, p[t], 0, 0, 0);
       }
 #if I2H_COARSE_SLICE_FENCE
       // keep the next slice's x fragments from being hoisted: 4 live fragments instead of 16
       __builtin_amdgcn_sched_barrier(0);
 #endif
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int gi = t * NG + gb;
-      const uint32_t w = szr[gi];
-      const float sv = __uint_as_float(w << 16);
-      const float zv = __uint_as_float(w & 0xffff0000u);
-      const float s2 = kBiasF[t] * sv;
-      const float z2 = fmaf(kBiasF[t] - 1.f, sv, zv);
-      const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
-#pragma unroll
-      for (int r = 0; r < RR; ++r) {
-        const float a = fmaf(s2, p[t][r], acc[r]);
-        acc[r] = fmaf(-xv[r], z2, a);
+      if (HV == 2 && s == 1) {
+        fold(0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (VAR != kVarWTile) fold(HV - 1);
   };
 
   // ring of I2H_COARSE_PF spans in flight: slot p is consumed in place, then refilled with the
@@ -466,10 +545,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
 #pragma unroll
     for (int gb = 0; gb < NGC; ++gb) {
       body(gb, ring[gb % kPf][0], ring[gb % kPf][1]);
-      if (gb + kPf < NGC) {
-        ring[gb % kPf][0] = ld16(prow + (gb + kPf) * kGroup);
-        ring[gb % kPf][1] = ld16(prow + (gb + kPf) * kGroup + kHalfOff);
-      }
+      if (gb + kPf < NGC) span_load(gb + kPf, ring[gb % kPf]);
     }
   } else {
     for (int gb0 = 0; gb0 < NG; gb0 += kPf) {
@@ -478,9 +554,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
         const int gb = gb0 + p;
         if (gb < NG) {
           body(gb, ring[p][0], ring[p][1]);
-          const int nx = gb + kPf < NG ? gb + kPf : NG - 1;
-          ring[p][0] = ld16(prow + nx * kGroup);
-          ring[p][1] = ld16(prow + nx * kGroup + kHalfOff);
+          span_load(gb + kPf < NG ? gb + kPf : NG - 1, ring[p]);
         }
       }
     }
@@ -569,6 +643,21 @@ int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packe
   return check_launch();
 }
 
+// One design alternative (ablation.h) through the one-row kernel, at K = 512 or 5120.
+template <int VAR>
+int launch_small_variant(const uint16_t* x, const float* xs, const uint8_t* packed, const uint16_t* S,
+                         const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, hipStream_t s) {
+  const int nblk = (int)nblk_of(N);
+  const size_t lds = small_lds_bytes(K, 1, VAR == kVarG64 ? 64 : kGroup);
+  auto go = [&](auto ngc) {
+    hipLaunchKernelGGL((coarse_small_kernel<1, true, decltype(ngc)::value, VAR>), dim3(nblk), dim3(kCoarseThreads), lds,
+                       s, x, xs, 1, packed, S, ZS, N, K, kc, nblk, cs, ci, nullptr, nullptr);
+  };
+  if (K == 5120) go(std::integral_constant<int, 10>{});
+  else go(std::integral_constant<int, 1>{});
+  return check_launch();
+}
+
 // True when the small kernel keeps x in LDS for M rows of K (and then sums the groups itself).
 bool small_sums_x(int64_t M, int64_t K) {
   return (M == 1 && small_lds_bytes((int)K, 1) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4) <= 65536);
@@ -614,6 +703,18 @@ int generic_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packe
 }
 
 }  // namespace
+
+int small_variant_launch(int var, const uint16_t* x, const float* xs, const uint8_t* packed, const uint16_t* S,
+                         const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, hipStream_t s) {
+  if (K != 512 && K != 5120) return I2H_ERR_SHAPE;
+  switch (var) {
+    case kVarDesign: return coarse_launch(x, xs, 1, packed, S, ZS, N, K, kc, cs, ci, nullptr, s);
+    case kVarG64: return launch_small_variant<kVarG64>(x, xs, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    case kVarC4: return launch_small_variant<kVarC4>(x, xs, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    case kVarWTile: return launch_small_variant<kVarWTile>(x, xs, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    default: return I2H_ERR_ARG;
+  }
+}
 
 int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t s, int32_t* zero_cnt) {
   if (!x || !xs) return I2H_ERR_ARG;

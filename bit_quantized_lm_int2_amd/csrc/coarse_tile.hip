@@ -18,6 +18,9 @@
 // waiting for x never waits for packed bytes that are not needed yet (loads retire in order).
 // The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
 // sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions.
+#include <type_traits>
+
+#include "ablation.h"
 #include "block_emit.h"
 #include "dequant.h"
 #include "host_util.h"
@@ -62,14 +65,22 @@ constexpr size_t tile_lds_bytes(int KG) {
 // XPF: x stages loaded ahead of the one being stored; RPF: packed spans loaded ahead of the one in
 // use. Vector loads return in order, so a load of x (resident in L2) issued behind loads from HBM
 // arrives with HBM latency: within a stage x is therefore issued before the packed span.
-template <int MT, int WAVES, int NGC, int XPF, int RPF>
+// VAR (ablation.h): the design, or one alternative (16 rows, NGC spans): group 64 splits each
+// quarter's partial sum (and its group sum) in two at k = 64 and doubles the LDS scale table;
+// contiguous-4 stages 512 consecutive k of x per span in natural order and reads four 8-byte runs
+// per tile and span (32 consecutive k of each of the span's four groups); the weight tile feeds
+// the dequantised weights to the matrix cores, with no group sums and no zero term.
+template <int MT, int WAVES, int NGC, int XPF, int RPF, int VAR = kVarDesign>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
     int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
   using T = Tile<MT, WAVES>;
-  constexpr int K = NGC * 512, Q = K / 4, NG = NGC, KG = K / kGroup, KGP = KG | 1;
+  static_assert(VAR == kVarDesign || MT == 1, "alternatives: the 16-row tile");
+  constexpr int GV = VAR == kVarG64 ? 64 : kGroup;  // quantisation group along k
+  constexpr int HV = kGroup / GV;                   // groups per quarter and span
+  constexpr int K = NGC * 512, Q = K / 4, NG = NGC, KG = K / GV, KGP = KG | 1;
   constexpr int NST = NG * T::SPS;
   constexpr int SZU = (64 * KG / 8 + 63) / 64;  // 16-byte units of the wave's S rows per lane
   extern __shared__ __align__(16) uint8_t lds[];
@@ -85,7 +96,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   // xs null (tiles of up to 32 rows; the 64-row tile has no registers to spare): the group sums of
   // x are taken here, this wave summing slices sq_s0 .. sq_s0 + 4/SP - 1 of quarter sq_q of each
   // stage for row tile sq_mt
-  const bool own = T::OWN_SUMS && xs == nullptr;
+  const bool own = T::OWN_SUMS && VAR != kVarWTile && xs == nullptr;
   const int sq_grp = wave / T::SP, sq_part = wave % T::SP;
   const int sq_q = sq_grp / MT, sq_mt = sq_grp % MT, sq_s0 = sq_part * (4 / T::SP);
 
@@ -100,11 +111,11 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   for (int i = 0; i < T::UPT; ++i) {
     const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
     const int q = gq % T::QS, m = gq / T::QS;
-    xo[i] = (uint32_t)((m < M ? m : M - 1) * K + q * Q + 8 * j);
+    xo[i] = (uint32_t)((m < M ? m : M - 1) * K + q * (VAR == kVarC4 ? kGroup : Q) + 8 * j);
   }
   auto x_load_one = [&](int st, int i) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
-    xr[st % XPF][i] = ld16(x + (xo[i] + (uint32_t)(t0 * Q + gb * kGroup)));
+    xr[st % XPF][i] = ld16(x + (xo[i] + (uint32_t)(VAR == kVarC4 ? gb * 512 : t0 * Q + gb * kGroup)));
   };
   auto x_load = [&](int st) {
 #pragma unroll
@@ -116,7 +127,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     for (int i = 0; i < T::UPT; ++i) {
       const int u = tid + i * T::THREADS, j = u & 15, gq = u >> 4;
       const int q = gq % T::QS, m = gq / T::QS;
-      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) = x_pair_order(xr[st % XPF][i]);
+      *reinterpret_cast<u32x4*>(xb + m * T::RS + q * 256 + 16 * j) =
+          VAR == kVarC4 ? xr[st % XPF][i] : x_pair_order(xr[st % XPF][i]);
     }
   };
 
@@ -128,14 +140,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int n = n0 + 16 * nt + col;
-    poff[nt] = (uint32_t)((n < N ? n : N - 1) - nb) * Q + 16 * h;
+    poff[nt] = (uint32_t)((n < N ? n : N - 1) - nb) * Q + (VAR == kVarC4 ? 8 : 16) * h;
   }
   constexpr int kSlots = RPF + 1;  // spans RPF ahead of the one in use
   u32x4 ring[kSlots][kNT][2];
   // slot: the ring entry, gb % kSlots, passed separately so that it is a compile-time constant
   // wherever the span loop is not fully unrolled (a runtime index would put the ring in scratch)
   auto ring_load_one = [&](int gb, int slot, int k) {  // k = 2 nt + half
-    ring[slot][k >> 1][k & 1] = ld16(pbase + (poff[k >> 1] + gb * kGroup + 64 * (k & 1)));
+    if constexpr (VAR == kVarC4) {  // runs 2 half and 2 half + 1 (8 bytes each, 32 apart)
+      typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+      const uint8_t* at = pbase + (poff[k >> 1] + gb * kGroup + 64 * (k & 1));
+      const u32x2 r0 = *reinterpret_cast<const u32x2*>(at), r1 = *reinterpret_cast<const u32x2*>(at + 32);
+      ring[slot][k >> 1][k & 1] = u32x4{r0[0], r0[1], r1[0], r1[1]};
+    } else {
+      ring[slot][k >> 1][k & 1] = ld16(pbase + (poff[k >> 1] + gb * kGroup + 64 * (k & 1)));
+    }
   };
   auto ring_load = [&](int gb) {
 #pragma unroll
@@ -213,14 +232,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const DqConst dqc = dq_const();
   const uint32_t* szc = szw + col * KGP;
-  f32x4 ps = {0.f, 0.f, 0.f, 0.f};  // this wave's part of a group sum of x (every column alike)
+  f32x4 ps[HV];  // this wave's part of a group sum of x (every column alike), per group of the quarter
+#pragma unroll
+  for (int hf = 0; hf < HV; ++hf) ps[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the group of quarter (contiguous-4: group in the span) t, span gb, half hf
+  auto gidx = [](int t, int gb, int hf) { return VAR == kVarC4 ? 4 * gb + t : HV * (t * NG + gb) + hf; };
 
   auto compute = [&](int st, int slot, bool clamp) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
-    const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + 32 * h;
+    // lane h's k in a group: 16 h + 8 (s & 1) + 64 (s >> 1) (its two 16-byte loads), contiguous-4
+    // 32 h + 8 s (its 8-byte run)
+    const uint8_t* xa = xbuf + (st & 1) * T::XBUF + col * T::RS + (VAR == kVarC4 ? 64 : 32) * h;
+    auto xoff = [](int qq, int s) { return VAR == kVarC4 ? qq * 256 + 16 * s : qq * 256 + 16 * (s & 1) + 128 * (s >> 1); };
     // dw: the span's packed dwords per tile; hw = dw >> 8, kept for the whole stage when the
     // registers allow (16 rows), else formed at each use
-    constexpr bool kKeepHw = MT == 1;
+    constexpr bool kKeepHw = MT == 1 && VAR != kVarC4;
     uint32_t dw[kNT][8], hw[kNT][8];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
@@ -235,18 +261,29 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
       }
 #pragma unroll
     for (int qq = 0; qq < T::QS; ++qq) {
-      const int t = t0 + qq;
-      f32x4 p[MT][kNT];
+      const int t = t0 + qq;  // the quarter (contiguous-4: the group of the span)
+      f32x4 p[MT][kNT][HV];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) p[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+          for (int hf = 0; hf < HV; ++hf) p[mt][nt][hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // weight tile: f S and (f - 1) S + ZS of each tile's column, which the weights take
+      float s1[kNT], z1[kNT];
+      if constexpr (VAR == kVarWTile) {
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          const uint32_t w = szc[16 * nt * KGP + t * NG + gb];
+          s1[nt] = kBiasF[t] * __uint_as_float(w << 16);
+          z1[nt] = fmaf(kBiasF[t] - 1.f, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+        }
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 a[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + qq * 256 + 16 * (s & 1) + 128 * (s >> 1));
+        for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + xoff(qq, s));
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           pin(dw[nt][2 * s]);
@@ -258,23 +295,33 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
         }
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
-          const uint32_t d0 = dw[nt][2 * s], d1 = dw[nt][2 * s + 1];
-          const uint32_t h0 = kKeepHw ? hw[nt][2 * s] : d0 >> 8, h1 = kKeepHw ? hw[nt][2 * s + 1] : d1 >> 8;
           bf16x8 bw;
-          if (t == 0) bw = dequant8_mask<0>(d0, d1, h0, h1, dqc);
-          else if (t == 1) bw = dequant8_mask<1>(d0, d1, h0, h1, dqc);
-          else if (t == 2) bw = dequant8_mask<2>(d0, d1, h0, h1, dqc);
-          else bw = dequant8_mask<3>(d0, d1, h0, h1, dqc);
+          if constexpr (VAR == kVarC4) {
+            bw = dequant8_c4((dw[nt][2 * qq + (s >> 1)] >> (16 * (s & 1))) & 0xffffu);
+          } else {
+            const uint32_t d0 = dw[nt][2 * s], d1 = dw[nt][2 * s + 1];
+            const uint32_t h0 = kKeepHw ? hw[nt][2 * s] : d0 >> 8, h1 = kKeepHw ? hw[nt][2 * s + 1] : d1 >> 8;
+            if (t == 0) bw = dequant8_mask<0>(d0, d1, h0, h1, dqc);
+            else if (t == 1) bw = dequant8_mask<1>(d0, d1, h0, h1, dqc);
+            else if (t == 2) bw = dequant8_mask<2>(d0, d1, h0, h1, dqc);
+            else bw = dequant8_mask<3>(d0, d1, h0, h1, dqc);
+          }
+          if constexpr (VAR == kVarWTile) bw = tile8_fold(bw, s1[nt], z1[nt]);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            p[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt],
-                                                                0, 0, 0);
+          for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (VAR == kVarWTile)
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[mt]), bw, acc[mt][nt],
+                                                                    0, 0, 0);
+            else
+              p[mt][nt][HV == 2 ? s >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt][HV == 2 ? s >> 1 : 0], 0, 0, 0);
+          }
         }
         if (own && qq == sq_q && (unsigned)(s - sq_s0) < (unsigned)(4 / T::SP)) {
-          const u32x4 as = *reinterpret_cast<const u32x4*>(xa + sq_mt * 16 * T::RS + qq * 256 + 16 * (s & 1) +
-                                                            128 * (s >> 1));
+          const u32x4 as = *reinterpret_cast<const u32x4*>(xa + sq_mt * 16 * T::RS + xoff(qq, s));
           const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-          ps = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as), ones, ps, 0, 0, 0);
+          ps[HV == 2 ? s >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as), ones,
+                                                                           ps[HV == 2 ? s >> 1 : 0], 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < kPerSlice; ++j) stage_load(st, slot, (qq * 4 + s) * kPerSlice + j, clamp);
@@ -282,22 +329,32 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
       if (own && qq == sq_q) {
-        // ps[r]: this wave's part of the sum of group t NG + gb for row 16 sq_mt + 4 h + r
-        if (col == 0)
-          *reinterpret_cast<f32x4*>(xsl + (sq_part * KG + t * NG + gb) * T::MR + 16 * sq_mt + 4 * h) = ps;
-        ps = f32x4{0.f, 0.f, 0.f, 0.f};
+        // ps[hf][r]: this wave's part of the sum of group gidx(t, gb, hf) for row 16 sq_mt + 4 h + r
+#pragma unroll
+        for (int hf = 0; hf < HV; ++hf) {
+          if (col == 0)
+            *reinterpret_cast<f32x4*>(xsl + (sq_part * KG + gidx(t, gb, hf)) * T::MR + 16 * sq_mt + 4 * h) = ps[hf];
+          ps[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
-      // the scale term of the group (the zero term is added after the loop)
-      const int gi = t * NG + gb;
-      float s2[kNT];
+      if constexpr (VAR != kVarWTile) {
+        // the scale term of the group (the zero term is added after the loop); contiguous-4 reads
+        // its codes at D = 4, so the scale is S itself
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) s2[nt] = kBiasF[t] * __uint_as_float(szc[16 * nt * KGP + gi] << 16);
+        for (int hf = 0; hf < HV; ++hf) {
+          const int gi = gidx(t, gb, hf);
+          const float fq = VAR == kVarC4 ? 1.f : kBiasF[t];
+          float s2[kNT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+          for (int nt = 0; nt < kNT; ++nt) s2[nt] = fq * __uint_as_float(szc[16 * nt * KGP + gi] << 16);
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(s2[nt], p[mt][nt][r], acc[mt][nt][r]);
+            for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[mt][nt][r] = fmaf(s2[nt], p[mt][nt][hf][r], acc[mt][nt][r]);
+        }
+      }
       // the accumulators are complete here: without this the compiler sinks the scaling of every
       // quarter towards the epilogue and keeps all partial sums alive until then
 #pragma unroll
@@ -307,8 +364,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     }
   };
 
-  if constexpr (MT == 1) {
-    // 16 rows: the whole K loop unrolled
+  if constexpr (MT == 1 && VAR == kVarDesign) {
+    // 16 rows: the whole K loop unrolled (the alternatives' longer span bodies take the loop below,
+    // which keeps every ring slot a compile-time index)
 #pragma unroll
     for (int gb = 0; gb < NG; ++gb) {
 #pragma unroll
@@ -360,9 +418,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   // and two zeros. Step ks covers groups 4 ks + h.
   if (own) __syncthreads();  // every part of every group sum is in LDS
 #pragma unroll 2
-  for (int ks = 0; ks < KG / 4; ++ks) {
-    const int g = 4 * ks + h, t = g / NG;
-    const float fm1 = t == 0 ? 31.f : (t == 1 ? 7.f : (t == 2 ? 1.f : 0.f));  // kBiasF[t] - 1
+  for (int ks = 0; ks < (VAR == kVarWTile ? 0 : KG / 4); ++ks) {
+    const int g = 4 * ks + h, t = g / (HV * NG);
+    // kBiasF[t] - 1 (contiguous-4: codes at D = 4, no fold)
+    const float fm1 = VAR == kVarC4 ? 0.f : (t == 0 ? 31.f : (t == 1 ? 7.f : (t == 2 ? 1.f : 0.f)));
     u32x4 za[MT], zb[kNT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -485,7 +544,37 @@ int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, 
   return I2H_OK;
 }
 
+// One design alternative (ablation.h) through the 16-row tile, at K = 512 or 5120.
+template <int VAR>
+int launch_tile_variant(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
+                        const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, hipStream_t s) {
+  const int nblk = (int)nblk_of(N);
+  constexpr int HV = VAR == kVarG64 ? 2 : 1;
+  auto go = [&](auto ngc) {
+    constexpr int NGC = decltype(ngc)::value;
+    const size_t lds = tile_lds_bytes<1, 4>(NGC * 4 * HV);
+    hipLaunchKernelGGL((coarse_tile_kernel<1, 4, NGC, I2H_TILE_XPF, I2H_TILE_RPF, VAR>), dim3((unsigned)((nblk + 3) / 4)),
+                       dim3(256), lds, s, x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, nullptr, nullptr);
+  };
+  if (K == 5120) go(std::integral_constant<int, 10>{});
+  else go(std::integral_constant<int, 1>{});
+  return check_launch();
+}
+
 }  // namespace
+
+int tile_variant_launch(int var, const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                        const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci,
+                        hipStream_t s) {
+  if (M < 1 || M > 16 || (K != 512 && K != 5120)) return I2H_ERR_SHAPE;
+  switch (var) {
+    case kVarDesign: return tile_launch(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, nullptr, nullptr, s);
+    case kVarG64: return launch_tile_variant<kVarG64>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    case kVarC4: return launch_tile_variant<kVarC4>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    case kVarWTile: return launch_tile_variant<kVarWTile>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
+    default: return I2H_ERR_ARG;
+  }
+}
 
 // K of the head's family the tile kernel is built for (the span loop is unrolled at compile time)
 bool tile_supported(int64_t M, int64_t K) {

@@ -38,6 +38,15 @@ int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* pa
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
                 hipStream_t s);
 
+// The design alternatives (ablation.h: var) through the production kernels, for the checks of
+// i2h_coarse_variant_topk: one row through the one-row kernel, 1..16 rows through the 16-row
+// tile, K = 512 or 5120; var = design runs the production entry point itself.
+int small_variant_launch(int var, const uint16_t* x, const float* xs, const uint8_t* packed, const uint16_t* S,
+                         const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, hipStream_t s);
+int tile_variant_launch(int var, const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
+                        const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci,
+                        hipStream_t s);
+
 // The fused selection + exact rerank + top-k kernel (select_rerank.hip) and its limits.
 bool select_rerank_supported(int64_t nblk, int kc, int R, int64_t N, int64_t K);
 // G > 1 workgroups per row split the exact rerank: each publishes its scores to exw [M, R] and

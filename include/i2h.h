@@ -275,9 +275,14 @@ I2H_API int i2h_xsum_group(const uint16_t* x, int64_t M, int64_t K, int group, f
 /*
  * Coarse logits and block candidates of a head packed by i2h_pack_variant with the same group
  * and layout, scaled per I2H_SCALE_*: c[m, n] = sum_g S * sum_{k in g} x (1 + v/4) - xs ZS
- * (accumulator; xs from i2h_xsum_group required) or sum_k x[m, k] w~[n, k] with the rounded tile
- * w~ (xs unused, may be NULL); fp32 accumulation; the block top-kcand as in i2h_coarse_topk.
- * Limits: 1 <= M <= 16, 1 <= kcand <= 64, K a multiple of 4 * group up to I2H_MAX_K, N <= 2^30.
+ * (accumulator) or sum_k x[m, k] w~[n, k] with the rounded tile w~ (xs unused); fp32
+ * accumulation; the block top-kcand as in i2h_coarse_topk. Each alternative runs through the
+ * production kernels (one row: the one-row kernel; 2..16 rows: the 16-row tile) with one property
+ * changed: (group, layout, scaling) is one of (128, QUARTER, ACC) (the design itself, the
+ * i2h_coarse_topk path), (64, QUARTER, ACC), (128, CONTIG, ACC) or (128, QUARTER, TILE); any
+ * other combination is I2H_ERR_ARG. xs (accumulator): the sums from i2h_xsum_group, or NULL for
+ * sums taken in the kernel. Limits: 1 <= M <= 16, K = 512 or 5120 (else I2H_ERR_SHAPE),
+ * 1 <= kcand <= 64, N <= 2^30; x, packed, S, ZS 16-byte aligned.
  */
 I2H_API int i2h_coarse_variant_topk(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                                     const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int group,

@@ -270,11 +270,17 @@ def test_variant_entry_points_reject_before_launch():
     assert g(P, 1, 5100, 64, P, None) == SHAPE
     # x, xs, M, packed, S, ZS, N, K, group, layout, scaling, kcand, cand_score, cand_idx, stream
     c = lib.i2h_coarse_variant_topk
-    assert c(P, None, 1, P, P, P, 1000, 5120, 128, 0, 0, 8, P, P, None) == ARG      # xs for the accumulator
+    assert c(None, None, 1, P, P, P, 1000, 5120, 128, 0, 0, 8, P, P, None) == ARG
     assert c(P, P, 17, P, P, P, 1000, 5120, 128, 0, 0, 8, P, P, None) == SHAPE      # M <= 16
-    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 2, 8, P, P, None) == ARG
-    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 0, P, P, None) == LIMIT
-    assert c(P + 8, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 8, P, P, None) == ALIGN
+    assert c(P, P, 1, P, P, P, 1000, 1024, 128, 0, 0, 8, P, P, None) == SHAPE       # K = 512 or 5120
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 2, 8, P, P, None) == ARG          # scaling 0 or 1
+    # one property changed at a time: group 64 with contiguous-4, or with the weight tile
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 1, 0, 8, P, P, None) == ARG
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 0, 1, 8, P, P, None) == ARG
+    assert c(P, P, 1, P, P, P, 1000, 5120, 128, 1, 1, 8, P, P, None) == ARG
+    assert c(P, P, 1, P, P, P, 1000, 5120, 64, 0, 0, 0, P, P, None) == LIMIT
+    assert c(P + 8, P, 1, P, P, P, 1000, 5120, 64, 0, 0, 8, P, P, None) == ALIGN
+    assert c(P, P, 1, P, P + 2, P, 1000, 5120, 128, 1, 0, 8, P, P, None) == ALIGN   # S 16-byte aligned
 
 
 def test_head_noalloc_statuses():
