@@ -350,7 +350,8 @@ def traffic_probe(torch, i2h, si, dev):
 def variant_probe(torch, i2h, si, dev):
     """Launches for rocprofv3 counter passes over the design alternatives: each of the four forms
     (design, group 64, contiguous-4, weight tile) packed from the timed workload's weight, then its
-    coarse kernel at M = 1 and 16 on 4 cold copies, 6 launches each."""
+    coarse kernel at M = 1 and 16 on 4 cold copies, 6 launches each; then the plain 512 MiB device
+    copy of traffic_probe (4 launches) that calibrates the byte counters."""
     cfg = si.WORKLOADS[WORKLOAD]
     K, N = cfg["K"], cfg["N"]
     W = si.gen_weight(N, K).to(dev)
@@ -367,7 +368,13 @@ def variant_probe(torch, i2h, si, dev):
                 i2h.coarse_variant_topk(x, None, p, a, b, g, lay, sc, KC)
             torch.cuda.synchronize()
         del cps, pk
-    print(json.dumps({"variant_probe": True, "M": [1, 16]}), flush=True)
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"variant_probe": True, "M": [1, 16], "copy_bytes": src.numel()}), flush=True)
 
 
 # Windows within which a final place that differs from the oracle's is excused: two reranked tokens

@@ -54,7 +54,7 @@ template <int MT, int WAVES>
 constexpr size_t tile_lds_bytes(int KG) {
   using T = Tile<MT, WAVES>;
   const size_t loop = 2 * (size_t)T::XBUF + (size_t)WAVES * 64 * (KG | 1) * 4 +
-                      (T::OWN_SUMS ? (size_t)T::SP * KG * T::MR * 4 : 0);
+                      (size_t)(T::OWN_SUMS ? T::SP : 1) * KG * T::MR * 4;
   const size_t emit = (size_t)WAVES * T::MR * kTRow * 4;
   return loop > emit ? loop : emit;
 }
@@ -86,7 +86,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xbuf = lds;                                             // [2][MR][RS]
   uint32_t* szl = reinterpret_cast<uint32_t*>(lds + 2 * T::XBUF);  // [WAVES][64][KGP]
-  float* xsl = reinterpret_cast<float*>(szl + WAVES * 64 * KGP);    // [SP][KG][MR]: parts of the group sums
+  // [SP][KG][MR]: parts of the group sums taken here, or the given ones (part 0)
+  float* xsl = reinterpret_cast<float*>(szl + WAVES * 64 * KGP);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
@@ -203,11 +204,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
         }
     }
   }
+  // the given group sums, for the zero term after the loop: into LDS here (read from global in the
+  // zero term they would wait behind the packed stream). Loaded unconditionally (from S[0] when
+  // xs is null) so that no load sits under a branch.
+  constexpr int XSU = (KG * T::MR + T::THREADS - 1) / T::THREADS;
+  const float* xsp = xs != nullptr ? xs : reinterpret_cast<const float*>(S);
+  float xg[XSU];
+#pragma unroll
+  for (int i = 0; i < XSU; ++i) {
+    const int e = tid + i * T::THREADS, g = e / T::MR, m = e - g * T::MR;
+    xg[i] = xsp[xs != nullptr && e < KG * T::MR ? (int64_t)(m < M ? m : M - 1) * KG + g : 0];
+  }
 #pragma unroll
   for (int g = 0; g < RPF && g < NG; ++g) ring_load(g);
 #pragma unroll
   for (int st = 1; st < XPF && st < NST; ++st) x_load(st);
   x_put(0);
+  if (xs != nullptr) {
+#pragma unroll
+    for (int i = 0; i < XSU; ++i)
+      if (tid + i * T::THREADS < KG * T::MR) xsl[tid + i * T::THREADS] = xg[i];
+  }
   uint32_t* szw = szl + wave * 64 * KGP;  // this wave's rows: [64][KGP], S | ZS << 16
 #pragma unroll
   for (int i = 0; i < SZU; ++i) {
@@ -426,14 +443,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = 16 * mt + col;
-      float v;
-      if (own) {
-        float sm = xsl[g * T::MR + m];
-        if constexpr (T::SP > 1) sm += xsl[(KG + g) * T::MR + m];
-        v = -sm;
-      } else {
-        v = -xs[(int64_t)(m < M ? m : M - 1) * KG + g];
-      }
+      float sm = xsl[g * T::MR + m];  // the given sums, or the parts of those taken here
+      if (T::SP > 1 && own) sm += xsl[(KG + g) * T::MR + m];
+      const float v = -sm;
       const uint32_t p1 = __float_as_uint(v) & 0xffff0000u;
       const float r1 = v - __uint_as_float(p1);
       const uint32_t p2 = __float_as_uint(r1) & 0xffff0000u;
