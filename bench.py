@@ -89,7 +89,7 @@ def head_bytes(M, N, K, kc=KC, R_=R, k=1, own_sums=False):
     return b
 
 
-COARSE_SOURCES = ("coarse.hip", "coarse_tile.hip", "dequant.h", "device_util.h", "block_emit.h")
+COARSE_SOURCES = ("coarse.hip", "coarse_tile.hip", "ablation.h", "dequant.h", "device_util.h", "block_emit.h")
 
 
 def coarse_source_hash():
@@ -944,7 +944,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "copy_gbps_measured": copy_gbps(torch, dev),
-                     "kernel": "coarse_small_kernel<1, true, 10>", "kernel_us": round(coarse_us, 2),
+                     "kernel": "coarse_small_kernel<1, true, 10, 0>", "kernel_us": round(coarse_us, 2),
                      "algorithmic_bytes": hb["coarse"]},
         "pack": {"us": round(pack_us, 1), "gbps": round(pack_bytes / (pack_us * 1e-6) / 1e9, 1),
                  "hbm_frac": round(pack_bytes / (pack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "N": N, "K": K},
