@@ -7,15 +7,18 @@
 // Layout on gfx950. A workgroup of WAVES waves covers WAVES consecutive 64-column blocks; wave w
 // owns block WAVES blockIdx.x + w whole, as four 16-column MFMA tiles (v_mfma_f32_16x16x32_bf16)
 // for each 16 rows, so each A fragment of x read from LDS feeds four MFMAs and the block's emit
-// needs no other wave. x is streamed through LDS in stages of 16 KB (all rows, QS quarters of one
-// 128-byte span of the packed rows), double-buffered and shared by the waves. The loop applies
-// only the scale of each group to the accumulator; the zero term, the sum over groups of
-// xs[m, g] z[n, g], is one more small contraction on the matrix cores after the loop, with both
-// factors split exactly into bf16 parts, so that the VALU does the dequant and one FMA per output
-// and group. The group sums xs are given (i2h_xsum) or, with xs null, taken in the kernel: each
-// wave sums one part of one (quarter, row tile) per stage on the matrix cores, against a B operand
-// of ones, into LDS. The wave's S and ZS rows sit in LDS for the whole K loop. The packed stream is loaded one span ahead, after the next stage of x, so that
-// waiting for x never waits for packed bytes that are not needed yet (loads retire in order).
+// needs no other wave. x is streamed through LDS in stages (all rows, QS quarters of one 128-byte
+// span of the packed rows: the whole span up to 32 rows, one quarter at 64), double-buffered and
+// shared by the waves. The loop applies only the scale of each group to the accumulator; the zero
+// term, the sum over groups of xs[m, g] z[n, g], is one more small contraction on the matrix
+// cores after the loop, with both factors split exactly into bf16 parts, so that the VALU does the
+// dequant and one FMA per output and group. The group sums xs are given (i2h_xsum; staged in LDS
+// before the loop) or, with xs null, taken in the kernel: each wave sums one part of one
+// (quarter, row tile) per stage on the matrix cores, against a B operand of ones, into LDS. The
+// wave's S and ZS rows sit in LDS for the whole K loop. The packed stream is loaded one span ahead,
+// after the next stage of x, so that waiting for x never waits for packed bytes that are not
+// needed yet (loads retire in order); with more than one stage per span (64 rows) the later
+// stages' x loads do queue behind the next span's packed loads.
 // The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
 // sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions.
 #include <type_traits>
@@ -36,7 +39,10 @@ template <int MT, int WAVES>
 struct Tile {
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int MR = 16 * MT;                          // rows of x held per launch
-  static constexpr int QS = MT == 1 ? 4 : (MT == 2 ? 2 : 1);  // quarters per x stage
+  // quarters per x stage: a whole span up to 32 rows (one stage per span: the x loads for the next
+  // stage never queue behind the next span's packed loads, which complete after them), one quarter
+  // at 64 rows (LDS)
+  static constexpr int QS = MT <= 2 ? 4 : 1;
   static constexpr int SPS = 4 / QS;                          // x stages per 128-byte span
   static constexpr int RS = QS * 256 + 16;                    // LDS bytes per staged x row (padded)
   static constexpr int XBUF = MR * RS;                        // bytes of one x stage buffer
@@ -521,10 +527,15 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
   return check_launch();
 }
 
-// up to 32 rows: workgroups of 4 waves, two per CU (measured 3-5% faster than one of 8 waves:
+// up to 16 rows: workgroups of 4 waves, two per CU (measured 3-5% faster than one of 8 waves:
 // each x stage barrier waits for fewer waves)
 #ifndef I2H_TILE_WAVES
 #define I2H_TILE_WAVES 4
+#endif
+// 17..32 rows: 8 waves, one workgroup per CU, so that a whole span of x (32 rows x 512 k) fits
+// in an LDS stage (two 4-wave workgroups with two stages per span: 10% slower)
+#ifndef I2H_TILE_WAVES32
+#define I2H_TILE_WAVES32 8
 #endif
 // 33..64 rows: 8 waves of 64 rows x 64 columns, two per SIMD (a few address registers spill to
 // scratch outside the inner loop; measured faster than 4 waves with no spills, one per SIMD)
@@ -541,7 +552,7 @@ int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, 
               const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc, hipStream_t s) {
   if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
   if constexpr (I2H_TILE_MAXMT >= 2)
-    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
+    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES32, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
   if constexpr (I2H_TILE_MAXMT >= 4)
     return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
   // rows in chunks of 16 through the 16-row tile (a build limited to it)
