@@ -9,10 +9,10 @@
 // blocks; a block's list is best first, so the R best entries of the row lie in the R best
 // blocks), then the entries of the R best blocks are gathered and ranked, and the R weight rows
 // are gathered with every load in flight.
-// Ranking works on fp64-coded keys (wave_rank.h), unique within a row. Both rankings are a radix
-// select: the bits every key shares with the largest are skipped, then 4-bit digits are counted
-// with wave ballots (no atomics) until at most 64 keys can still be among the R best; those are
-// gathered and one wave sorts them.
+// Ranking works on fp64-coded keys (wave_rank.h), unique within a row. Each ranking gathers the
+// keys at or above a lower bound of the R-th best (up to 256 of them) and ranks them by counting
+// (a key's place is the number of keys above it); where more clear the bound, a radix select
+// (4-bit digits counted with wave ballots) first narrows them to at most 64.
 // The exact dot products use the same lane mapping and summation order as rerank.hip, so both
 // paths give the same bits.
 // One workgroup pulls the R weight rows at what one CU can keep in flight, well below HBM rate,
@@ -33,7 +33,7 @@ constexpr int kSrMaxR = 64, kSrMaxKc = 8;
 constexpr int kSrChunk = 10;  // 512-k steps of the two weight rows a wave has in flight at once
 
 struct SrLds {
-  uint64_t list[128];       // keys gathered for the final sort of a selection
+  uint64_t list[256];       // keys gathered for the final ranking of a selection
   double top[64];           // a selection, best first, 0-padded
   uint64_t cand[64];        // per-wave t-th best keys (lower bound of the R-th best)
   uint32_t cnt[kSrWaves][16];  // per-wave digit counts of one radix pass
@@ -181,14 +181,18 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
 //
 // Fast path: a lower bound T of the R-th largest key (if not given: the smallest of the waves'
 // t-th best keys, t = ceil(R / 16), since the 16 t keys at or above it are distinct); if at most
-// 128 keys are at or above T they are gathered and ranked, and the best R kept. Otherwise
+// 256 keys are at or above T they are gathered and ranked, and the best R kept. Otherwise
 // radix_narrow leaves at most 64 to gather and rank. Ranking is by counting over the whole
-// workgroup (8 threads per gathered key, 16 comparisons each): the keys are unique, so a key's
-// place is the number of keys above it, and no sorting network is needed.
+// workgroup (8 threads per gathered key and 16 comparisons each up to 128 keys, 4 threads and 64
+// comparisons above): the keys are unique, so a key's place is the number of keys above it, and
+// no sorting network is needed. On independent block scores at R = 32 the bound leaves ~90 keys,
+// over 128 for about one row in ten and over 256 for about one in a thousand; with a gather cap
+// of 128 those rows took the radix passes (~3 us), and at 4 to 16 rows one of them held up most
+// launches.
 template <int BPT>
 __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
-  constexpr int kCap = 128;
+  constexpr int kCap = 256;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
   if (lower != 0) __syncthreads();
@@ -232,21 +236,32 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
     __syncthreads();
     n = L.dec[3];  // at most 64
   }
-  // rank by counting: gathered key i (n <= 128) is compared by threads 8i .. 8i + 7, thread part
-  // p with keys p, p + 8, ... (the 8 parts read 8 consecutive keys: no LDS bank conflict); places
-  // at or past min(n, R) are 0
+  // rank by counting: gathered key i is compared by threads P i .. P i + P - 1 (P = 8 up to 128
+  // keys, else 4), thread part p with keys p, p + P, ... (the P parts read P consecutive keys: no
+  // LDS bank conflict); places at or past min(n, R) are 0. n is the same in every thread.
   {
-    const int i = tid >> 3, part = tid & 7;
+    const bool wide = n > 128;
+    const int i = wide ? tid >> 2 : tid >> 3, part = wide ? tid & 3 : tid & 7;
     const uint64_t me = i < n ? L.list[i] : 0ull;
     uint32_t above = 0;
+    if (!wide) {
 #pragma unroll
-    for (int q = 0; q < kCap / 8; ++q) {
-      const int j = 8 * q + part;
-      above += (j < n && L.list[j] > me) ? 1u : 0u;
+      for (int q = 0; q < 16; ++q) {
+        const int j = 8 * q + part;
+        above += (j < n && L.list[j] > me) ? 1u : 0u;
+      }
+      above += lane_xor<1>(above);
+      above += lane_xor<2>(above);
+      above += lane_xor<4>(above);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kCap / 4; ++q) {
+        const int j = 4 * q + part;
+        above += (j < n && L.list[j] > me) ? 1u : 0u;
+      }
+      above += lane_xor<1>(above);
+      above += lane_xor<2>(above);
     }
-    above += lane_xor<1>(above);
-    above += lane_xor<2>(above);
-    above += lane_xor<4>(above);
     if (part == 0 && i < n && (int)above < R) L.top[above] = __builtin_bit_cast(double, me);
     const int filled = n < R ? n : R;
     if (tid >= filled && tid < 64) L.top[tid] = 0.0;

@@ -166,6 +166,62 @@ def test_select_rerank_fused(i2h, M, N, K, kc, R, k, grid):
         pu.check_rerank(host(fex), si.bits(x), si.bits(W), host(fsel))
 
 
+def _first_gather(cs_row, kc, R):
+    """Keys the fused tail gathers on its first pass over a row's blocks: those at or above the
+    smallest of its 16 waves' ceil(R / 16)-th best block keys (thread t holds blocks t, t + 1024,
+    ...; wave t // 64); a key is (best score descending, block ascending)."""
+    nblk = cs_row.shape[0] // kc
+    best = cs_row[::kc].astype(np.float64)
+    order = np.lexsort((np.arange(nblk), -best))
+    rank = np.empty(nblk, np.int64)
+    rank[order] = np.arange(nblk)
+    t, worst = (R + 15) // 16, -1
+    for w in range(16):
+        r = np.sort(rank[(np.arange(nblk) % 1024) // 64 == w])
+        if r.size < t:
+            return nblk
+        worst = max(worst, int(r[t - 1]))
+    return worst + 1
+
+
+def test_select_rerank_gather_paths(i2h):
+    """Rows built so that the first gather of the block ranking holds 32 keys (every wave has two
+    far-ahead blocks), about 200 (one wave's second best sits low: the 4-threads-per-key ranking)
+    and nearly every block (one wave holds no high block: the radix passes). Each row's count is
+    checked on the host first; the fused tail must still equal the separate calls and the
+    oracle's selection."""
+    N, K, kc, R, k = 124160, 1024, 8, 32, 4
+    sc = si.gen_scores(3, N, seed=5).numpy().astype(np.float64)
+    nb = N // 64
+    wave_of = (np.arange(nb) % 1024) // 64
+    for w in range(16):
+        b0, b1 = np.flatnonzero(wave_of == w)[:2]
+        sc[0, 64 * b0] = 10.0 + w / 64
+        sc[0, 64 * b1 + 5] = 9.0 + w / 64
+    for b in np.flatnonzero(wave_of == 15):
+        sc[1, 64 * b:64 * b + 64] = -5.0
+        sc[2, 64 * b:64 * b + 64] = -100.0
+    b0, b1 = np.flatnonzero(wave_of == 15)[:2]
+    sc[1, 64 * b0] = 3.0
+    sc[1, 64 * b1] = 2.95
+    cs, ci = oracle.block_emit(sc, kc)
+    counts = [_first_gather(cs[m], kc, R) for m in range(3)]
+    assert counts[0] == 32 and 128 < counts[1] <= 256 and counts[2] > 256, counts
+    want_sel = oracle.select_top_r(cs, ci, R)
+    cs_d, ci_d = torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV)
+    g = torch.Generator(device=DEV).manual_seed(91)
+    W = (0.02 * torch.randn(N, K, generator=g, device=DEV)).to(torch.bfloat16)
+    x = torch.randn(3, K, generator=g, device=DEV).to(torch.bfloat16)
+    sel = i2h.select(cs_d, ci_d, kc, R)
+    ex = i2h.rerank(x, W, sel)
+    oi, ov = i2h.finalize(ex, sel, k)
+    fi, fv, fsel, fex = i2h.select_rerank_topk(cs_d, ci_d, kc, R, x, W, k, want_sel=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fsel), want_sel)
+    assert torch.equal(fsel, sel) and torch.equal(fex, ex), "fused selection / exact scores differ"
+    assert torch.equal(fi, oi) and torch.equal(fv, ov), "fused top-k differs"
+
+
 @pytest.mark.parametrize("M,R,k,grid", [(3, 32, 1, 0), (3, 32, 16, 2), (2, 100, 100, 1), (4, 1024, 16, 4),
                                         (1, 1, 1, 0)])
 def test_finalize_bit_exact(i2h, M, R, k, grid):
