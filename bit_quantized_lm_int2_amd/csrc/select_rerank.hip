@@ -42,7 +42,6 @@ struct SrLds {
   int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
   int32_t last;             // this workgroup is the last of its row's G to finish
   uint64_t lower;
-  int32_t sel[kSrMaxR];
   float ex[kSrMaxR];
 };
 constexpr size_t kSrLdsHead = (sizeof(SrLds) + 15) / 16 * 16;
@@ -177,7 +176,9 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
 // The R (<= 64) largest of the keys the block's threads hold (BPT each, 0 = none), best first
 // and 0-padded, into L.top. Keys are the bit patterns of the fp64 ranking keys: valid ones share
 // their top 12 bits, so the 52 low bits order them, and they are unique. `lower`, if not 0, is
-// at most the R-th largest key (0: unknown). Every thread of the block calls it.
+// at most the R-th largest key (0: unknown). Every thread of the block calls it. `ready`: the
+// caller has set the gather counter L.dec[3] to 0 before a barrier that every thread has passed
+// since (saves this call the barrier that orders its own reset before the gather).
 //
 // Fast path: a lower bound T of the R-th largest key (if not given: the smallest of the waves'
 // t-th best keys, t = ceil(R / 16), since the 16 t keys at or above it are distinct); if at most
@@ -190,12 +191,14 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
 // of 128 those rows took the radix passes (~3 us), and at 4 to 16 rows one of them held up most
 // launches.
 template <int BPT>
-__device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower) {
+__device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower, bool ready = false) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
   constexpr int kCap = 256;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
-  if (lower != 0) __syncthreads();
+  if (!ready) {
+    if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
+    if (lower != 0) __syncthreads();
+  }
   if (lower == 0) {
     const int t = (R + kSrWaves - 1) / kSrWaves;  // 1..4
     uint64_t kk[BPT];
@@ -348,6 +351,7 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     const uint32_t last = (uint32_t)token_key_token(L.top[R - 1]) * kBlockN + (kBlockN - 1);
     lower_e = (lower_e & ~0xFFFFFull) | (0xFFFFFu - last);
   }
+  if (tid == 0) L.dec[3] = 0;  // the entry gather's counter (select_top has read it for the blocks)
   const bool redo = __syncthreads_or(bad);
   if (redo) {
 #pragma unroll
@@ -359,9 +363,10 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     gather_entries(true);
     lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
   }
-  select_top<1>(L, ek, R, lower_e);
-  if (tid < R) L.sel[tid] = token_key_token(L.top[tid]);
-  __syncthreads();
+  select_top<1>(L, ek, R, lower_e, !redo);
+  // the selection: L.top[j] holds the j-th selected token's key (0: none, token -1); nothing
+  // rewrites L.top after this
+  auto sel_at = [&](int j) { return token_key_token(L.top[j]); };
 
   // --- exact rerank of this workgroup's share, the selected tokens g, g + G, ...: wave w scores
   // the w-th, (w + 16)-th, ... of them two at a time, with the loads of both rows (up to kSrChunk
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   const int steps = K / 512;
   for (int i0 = wave; g + G * i0 < R; i0 += 2 * kSrWaves) {
     const int j0 = g + G * i0, j1 = g + G * (i0 + kSrWaves);
-    const int n0 = L.sel[j0], n1 = j1 < R ? L.sel[j1] : -1;
+    const int n0 = sel_at(j0), n1 = j1 < R ? sel_at(j1) : -1;
     const bool v0 = n0 >= 0 && n0 < N, v1 = n1 >= 0 && n1 < N;
     float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
     if constexpr (FP8) {
@@ -464,15 +469,23 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
 
   // --- outputs: the selection and its exact scores (optional), the k best by exact score
   if (tid < R) {
-    if (sel_out != nullptr) sel_out[(int64_t)m * R + tid] = L.sel[tid];
+    if (sel_out != nullptr) sel_out[(int64_t)m * R + tid] = sel_at(tid);
     if (ex_out != nullptr) ex_out[(int64_t)m * R + tid] = L.ex[tid];
   }
   if (wave == 0) {
-    double fk[1] = {lane < R ? token_key(L.ex[lane], L.sel[lane]) : 0.0};
-    wave_sort_f64<1>(fk);
-    if (lane < k) {
-      oi[(int64_t)m * k + lane] = token_key_token(fk[0]);
-      ov[(int64_t)m * k + lane] = token_key_score(fk[0]);
+    double fk[1] = {lane < R ? token_key(L.ex[lane], sel_at(lane)) : 0.0};
+    if (k == 1) {  // the argmax: the largest key, no sort
+      const double best = __builtin_bit_cast(double, wave_max_u64(__builtin_bit_cast(uint64_t, fk[0])));
+      if (lane == 0) {
+        oi[m] = token_key_token(best);
+        ov[m] = token_key_score(best);
+      }
+    } else {
+      wave_sort_f64<1>(fk);
+      if (lane < k) {
+        oi[(int64_t)m * k + lane] = token_key_token(fk[0]);
+        ov[(int64_t)m * k + lane] = token_key_score(fk[0]);
+      }
     }
   }
 }
