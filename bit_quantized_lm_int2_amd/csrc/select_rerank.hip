@@ -5,10 +5,12 @@
 // rows, and the final argmax or top-k is drawn from those exact scores only.
 //
 // For small M this tail is latency-bound (one row per workgroup, a chain of dependent steps).
-// The x row goes to LDS while the best entry of every block is ranked (each thread holds up to 4
+// The x row goes to LDS while the best entry of every block is loaded (each thread holds up to 4
 // blocks; a block's list is best first, so the R best entries of the row lie in the R best
-// blocks), then the entries of the R best blocks are gathered and ranked, and the R weight rows
-// are gathered with every load in flight.
+// blocks). A lower bound of the R-th best block then selects the blocks whose lists are read: the
+// entries at or above the matching entry bound are gathered and ranked once (the general path,
+// for caller lists it cannot take, ranks the blocks first and then their entries), and the R
+// weight rows are gathered with every load in flight.
 // Ranking works on fp64-coded keys (wave_rank.h), unique within a row. Each ranking gathers the
 // keys at or above a lower bound of the R-th best (up to 256 of them) and ranks them by counting
 // (a key's place is the number of keys above it); where more clear the bound, a radix select
@@ -33,7 +35,7 @@ constexpr int kSrMaxR = 64, kSrMaxKc = 8;
 constexpr int kSrChunk = 10;  // 512-k steps of the two weight rows a wave has in flight at once
 
 struct SrLds {
-  uint64_t list[256];       // keys gathered for the final ranking of a selection
+  uint64_t list[256];       // keys gathered for the ranking of a selection (kSrCap)
   double top[64];           // a selection, best first, 0-padded
   uint64_t cand[64];        // per-wave t-th best keys (lower bound of the R-th best)
   uint32_t cnt[kSrWaves][16];  // per-wave digit counts of one radix pass
@@ -41,6 +43,7 @@ struct SrLds {
   int32_t wnum[kSrWaves];
   int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
   int32_t last;             // this workgroup is the last of its row's G to finish
+  int32_t ob[kSrWaves][64 * 4];  // per wave: its blocks whose key clears the block bound
   uint64_t lower;
   float ex[kSrMaxR];
 };
@@ -173,61 +176,105 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
   *prefix_out = prefix;
 }
 
+constexpr int kSrCap = 256;  // keys gathered for a counting rank
+
+// A lower bound of the R-th largest of the keys the block's threads hold (BPT each, 0 = none):
+// the smallest of the 16 waves' t-th best keys, t = ceil(R / 16), since the 16 t keys at or above
+// it are distinct (0: some wave holds fewer than t keys). Also sets the gather counter L.dec[3]
+// to 0 before the barrier it ends with. Every thread of the block calls it.
+template <int BPT>
+__device__ __forceinline__ uint64_t block_lower(SrLds& L, const uint64_t (&k)[BPT], int R) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) L.dec[3] = 0;
+  const int t = (R + kSrWaves - 1) / kSrWaves;  // 1..4
+  uint64_t kk[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) kk[j] = k[j];
+  uint64_t mx = 0;
+  for (int i = 0; i < t; ++i) {
+    mx = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) mx = kk[j] > mx ? kk[j] : mx;
+    mx = wave_max_u64(mx);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) kk[j] = kk[j] == mx ? 0ull : kk[j];  // keys are unique
+  }
+  if (lane == 0) L.wmax[wave] = mx;  // this wave's t-th best (0: fewer than t keys)
+  __syncthreads();
+  uint64_t lower = L.wmax[0];
+#pragma unroll
+  for (int w = 1; w < kSrWaves; ++w) lower = L.wmax[w] < lower ? L.wmax[w] : lower;
+  return lower;
+}
+
+// The n (<= 256) unique keys gathered in L.list ranked by counting over the whole workgroup: a
+// key's place is the number of keys above it, so no sorting network is needed. Gathered key i is
+// compared by threads P i .. P i + P - 1 (P = 8 up to 128 keys, 16 comparisons each; else 4 and
+// 64), thread part p with keys p, p + P, ... (the P parts read P consecutive keys: no LDS bank
+// conflict). The best R go to L.top, best first; places at or past min(n, R) are 0. n is the
+// same in every thread; ends with a barrier.
+__device__ __forceinline__ void rank_gathered(SrLds& L, int n, int R) {
+  const int tid = threadIdx.x;
+  const bool wide = n > 128;
+  const int i = wide ? tid >> 2 : tid >> 3, part = wide ? tid & 3 : tid & 7;
+  const uint64_t me = i < n ? L.list[i] : 0ull;
+  uint32_t above = 0;
+  if (!wide) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = 8 * q + part;
+      above += (j < n && L.list[j] > me) ? 1u : 0u;
+    }
+    above += lane_xor<1>(above);
+    above += lane_xor<2>(above);
+    above += lane_xor<4>(above);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kSrCap / 4; ++q) {
+      const int j = 4 * q + part;
+      above += (j < n && L.list[j] > me) ? 1u : 0u;
+    }
+    above += lane_xor<1>(above);
+    above += lane_xor<2>(above);
+  }
+  if (part == 0 && i < n && (int)above < R) L.top[above] = __builtin_bit_cast(double, me);
+  const int filled = n < R ? n : R;
+  if (tid >= filled && tid < 64) L.top[tid] = 0.0;
+  __syncthreads();
+}
+
 // The R (<= 64) largest of the keys the block's threads hold (BPT each, 0 = none), best first
 // and 0-padded, into L.top. Keys are the bit patterns of the fp64 ranking keys: valid ones share
 // their top 12 bits, so the 52 low bits order them, and they are unique. `lower`, if not 0, is
-// at most the R-th largest key (0: unknown). Every thread of the block calls it. `ready`: the
-// caller has set the gather counter L.dec[3] to 0 before a barrier that every thread has passed
-// since (saves this call the barrier that orders its own reset before the gather).
+// at most the R-th largest key (0: unknown: block_lower's bound). Every thread of the block calls
+// it. `ready`: the caller has set the gather counter L.dec[3] to 0 before a barrier that every
+// thread has passed since (saves this call the barrier that orders its own reset before the
+// gather).
 //
-// Fast path: a lower bound T of the R-th largest key (if not given: the smallest of the waves'
-// t-th best keys, t = ceil(R / 16), since the 16 t keys at or above it are distinct); if at most
-// 256 keys are at or above T they are gathered and ranked, and the best R kept. Otherwise
-// radix_narrow leaves at most 64 to gather and rank. Ranking is by counting over the whole
-// workgroup (8 threads per gathered key and 16 comparisons each up to 128 keys, 4 threads and 64
-// comparisons above): the keys are unique, so a key's place is the number of keys above it, and
-// no sorting network is needed. On independent block scores at R = 32 the bound leaves ~90 keys,
-// over 128 for about one row in ten and over 256 for about one in a thousand; with a gather cap
-// of 128 those rows took the radix passes (~3 us), and at 4 to 16 rows one of them held up most
-// launches.
+// Every key at or above the bound is gathered; if at most 256 they are ranked by counting, and the
+// best R kept. Otherwise radix_narrow leaves at most 64 to gather and rank. On independent block
+// scores at R = 32 block_lower's bound leaves ~90 keys, over 128 for about one row in ten and over
+// 256 for about one in a thousand; with a gather cap of 128 those rows took the radix passes
+// (~3 us), and at 4 to 16 rows one of them held up most launches.
 template <int BPT>
 __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t lower, bool ready = false) {
   constexpr uint64_t kLow = (1ull << 52) - 1;
-  constexpr int kCap = 256;
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (!ready) {
-    if (tid == 0) L.dec[3] = 0;  // the gather counter; a barrier follows on both paths below
-    if (lower != 0) __syncthreads();
-  }
+  const int tid = threadIdx.x;
   if (lower == 0) {
-    const int t = (R + kSrWaves - 1) / kSrWaves;  // 1..4
-    uint64_t kk[BPT];
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) kk[j] = k[j];
-    uint64_t mx = 0;
-    for (int i = 0; i < t; ++i) {
-      mx = 0;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) mx = kk[j] > mx ? kk[j] : mx;
-      mx = wave_max_u64(mx);
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) kk[j] = kk[j] == mx ? 0ull : kk[j];  // keys are unique
-    }
-    if (lane == 0) L.wmax[wave] = mx;  // this wave's t-th best (0: fewer than t keys)
+    lower = block_lower<BPT>(L, k, R);  // resets the counter before its barrier
+  } else if (!ready) {
+    if (tid == 0) L.dec[3] = 0;  // the gather counter
     __syncthreads();
-    lower = L.wmax[0];
-#pragma unroll
-    for (int w = 1; w < kSrWaves; ++w) lower = L.wmax[w] < lower ? L.wmax[w] : lower;
   }
   // gather every key at or above the bound while there is room, counting all of them
   const uint64_t lo = lower != 0 ? lower : 1ull;
   bool take[BPT];
 #pragma unroll
   for (int j = 0; j < BPT; ++j) take[j] = k[j] >= lo;
-  wave_append<BPT>(L, k, take, kCap);
+  wave_append<BPT>(L, k, take, kSrCap);
   __syncthreads();
   int n = L.dec[3];
-  if (n > kCap) {  // block-uniform: narrow down by digits, then gather again
+  if (n > kSrCap) {  // block-uniform: narrow down by digits, then gather again
     int shift = 0;
     uint64_t prefix = 0;
     radix_narrow<BPT>(L, k, R, &shift, &prefix);
@@ -235,41 +282,11 @@ __device__ void select_top(SrLds& L, const uint64_t (&k)[BPT], int R, uint64_t l
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < BPT; ++j) take[j] = k[j] != 0 && ((k[j] & kLow) >> shift) >= (prefix >> shift);
-    wave_append<BPT>(L, k, take, kCap);
+    wave_append<BPT>(L, k, take, kSrCap);
     __syncthreads();
     n = L.dec[3];  // at most 64
   }
-  // rank by counting: gathered key i is compared by threads P i .. P i + P - 1 (P = 8 up to 128
-  // keys, else 4), thread part p with keys p, p + P, ... (the P parts read P consecutive keys: no
-  // LDS bank conflict); places at or past min(n, R) are 0. n is the same in every thread.
-  {
-    const bool wide = n > 128;
-    const int i = wide ? tid >> 2 : tid >> 3, part = wide ? tid & 3 : tid & 7;
-    const uint64_t me = i < n ? L.list[i] : 0ull;
-    uint32_t above = 0;
-    if (!wide) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int j = 8 * q + part;
-        above += (j < n && L.list[j] > me) ? 1u : 0u;
-      }
-      above += lane_xor<1>(above);
-      above += lane_xor<2>(above);
-      above += lane_xor<4>(above);
-    } else {
-#pragma unroll
-      for (int q = 0; q < kCap / 4; ++q) {
-        const int j = 4 * q + part;
-        above += (j < n && L.list[j] > me) ? 1u : 0u;
-      }
-      above += lane_xor<1>(above);
-      above += lane_xor<2>(above);
-    }
-    if (part == 0 && i < n && (int)above < R) L.top[above] = __builtin_bit_cast(double, me);
-    const int filled = n < R ? n : R;
-    if (tid >= filled && tid < 64) L.top[tid] = 0.0;
-  }
-  __syncthreads();
+  rank_gathered(L, n, R);
 }
 
 // FP8: the weight rows are e4m3 bytes (Wv) with a per-row fp32 scale (wscale); else bf16 rows.
@@ -322,48 +339,111 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     srt[j] = b < nblk ? __builtin_bit_cast(uint64_t, token_key(bs[j], b)) : 0ull;
   }
 
-  // --- the R best blocks, by their best entry
-  select_top<BPT>(L, srt, R, 0ull);
-
-  // --- every entry of those blocks (thread t: entry t % kc of block rank t / kc), ranked. The
-  // best entry of a block is valid whenever the block has a real column; a caller's list whose
-  // best entry has index < 0 makes the block ranking redo itself with the entries' tokens.
-  const int nsel = R * kc;
-  uint64_t ek[1] = {0ull};
-  bool bad = false;
-  auto gather_entries = [&](bool by_token) {
-    const double bkey = tid < nsel ? L.top[tid / kc] : 0.0;
-    const int t = token_key_token(bkey);  // -1 when there is no block
-    const int blk = t < 0 ? 0 : (by_token ? t / kBlockN : t);
-    const int64_t at = (int64_t)blk * kc + (tid < nsel ? tid % kc : 0);
-    const int32_t tok = c[at];
-    const float sc = s[at];
-    const bool use = t >= 0;
-    bad = bad || (use && tid % kc == 0 && tok < 0);
-    ek[0] = use ? __builtin_bit_cast(uint64_t, token_key(sc, tok)) : 0ull;
-  };
-  gather_entries(false);
-  // The R block maxima are R distinct entries at or above the R-th block's score with that
-  // block's last token, which bounds the R-th best entry from below. select_top rewrites L.top
-  // only after barriers that follow every read of it here.
-  uint64_t lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
-  if (lower_e != 0) {
-    const uint32_t last = (uint32_t)token_key_token(L.top[R - 1]) * kBlockN + (kBlockN - 1);
-    lower_e = (lower_e & ~0xFFFFFull) | (0xFFFFFu - last);
-  }
-  if (tid == 0) L.dec[3] = 0;  // the entry gather's counter (select_top has read it for the blocks)
-  const bool redo = __syncthreads_or(bad);
-  if (redo) {
+  // --- the row's R best entries, in one ranking. T, a lower bound of the R-th best block key,
+  // gives Te = (T's score, the last token of T's block), a lower bound of the R-th best entry: the
+  // R best block maxima are R distinct entries at or above it. Every entry at or above Te lies in
+  // a block whose key is at or above T (an entry never beats its block's best, and on equal scores
+  // a later block holds later tokens), so the threads that hold such a block (~R + 60 of them at
+  // R = 32 on independent scores) load its list and gather the entries at or above Te, and one
+  // counting rank orders them. When T is unknown, a block's best entry is invalid (a caller's
+  // list; the ranking must then follow tokens) or more than 256 entries clear Te, the row takes
+  // the general path: the R best blocks, then their entries.
+  const uint64_t T = block_lower<BPT>(L, srt, R);  // the gather counter is 0 past its barrier
+  bool done = false;
+  if (T != 0) {  // block-uniform
+    const uint32_t bT = 0xFFFFFu - (uint32_t)(T & 0xFFFFFull);
+    const uint64_t Te = (T & ~0xFFFFFull) | (0xFFFFFu - (bT * kBlockN + (kBlockN - 1)));
+    // each wave lists its blocks at or above T (L.ob[wave]; a wave's LDS writes precede its own
+    // later reads), then takes them 16 at a time: lane l loads entry l % 8 of listed blocks l / 8
+    // and 8 + l / 8 (8 consecutive entries per block), and appends the entries at or above Te
+    bool bad = false;
+    int no = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
-      const int b = tid + kSrThreads * j;
-      srt[j] = b < nblk ? __builtin_bit_cast(uint64_t, token_key(s[(int64_t)b * kc], c[(int64_t)b * kc])) : 0ull;
+      const bool own = srt[j] >= T;  // 0 (no block) is below T
+      const uint64_t ob = __builtin_amdgcn_ballot_w64(own);
+      if (own)
+        L.ob[wave][no + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ob >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ob, 0u))] =
+            tid + kSrThreads * j;
+      no += __builtin_popcountll(ob);
     }
-    select_top<BPT>(L, srt, R, 0ull);
-    gather_entries(true);
-    lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
+    __builtin_amdgcn_wave_barrier();
+    const int e = lane & 7;
+    for (int q0 = 0; q0 < no; q0 += 16) {  // wave-uniform; one round for up to 16 listed blocks
+      int32_t tok[2];
+      float sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // every load issued before any is used; in bounds for every lane
+        const int q = q0 + 8 * h + (lane >> 3);
+        const int blk = q < no ? L.ob[wave][q] : 0;
+        const int64_t at = (int64_t)blk * kc + (e < kc ? e : kc - 1);
+        tok[h] = c[at];
+        sc[h] = s[at];
+      }
+      uint64_t ek[2];
+      bool take[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bool in = q0 + 8 * h + (lane >> 3) < no && e < kc;
+        bad = bad || (in && e == 0 && tok[h] < 0);
+        ek[h] = in ? __builtin_bit_cast(uint64_t, token_key(sc[h], tok[h])) : 0ull;  // 0 for a token < 0
+        take[h] = ek[h] >= Te;
+      }
+      wave_append<2>(L, ek, take, kSrCap);
+    }
+    const bool any_bad = __syncthreads_or(bad);
+    const int n = L.dec[3];
+    if (!any_bad && n <= kSrCap) {
+      rank_gathered(L, n, R);
+      done = true;
+    } else {
+      __syncthreads();  // every thread has read the counter before the general path resets it
+    }
   }
-  select_top<1>(L, ek, R, lower_e, !redo);
+  if (!done) {
+    // --- the general path: the R best blocks, by their best entry
+    select_top<BPT>(L, srt, R, T);
+
+    // --- every entry of those blocks (thread t: entry t % kc of block rank t / kc), ranked. The
+    // best entry of a block is valid whenever the block has a real column; a caller's list whose
+    // best entry has index < 0 makes the block ranking redo itself with the entries' tokens.
+    const int nsel = R * kc;
+    uint64_t ek[1] = {0ull};
+    bool bad = false;
+    auto gather_entries = [&](bool by_token) {
+      const double bkey = tid < nsel ? L.top[tid / kc] : 0.0;
+      const int t = token_key_token(bkey);  // -1 when there is no block
+      const int blk = t < 0 ? 0 : (by_token ? t / kBlockN : t);
+      const int64_t at = (int64_t)blk * kc + (tid < nsel ? tid % kc : 0);
+      const int32_t tok = c[at];
+      const float sc = s[at];
+      const bool use = t >= 0;
+      bad = bad || (use && tid % kc == 0 && tok < 0);
+      ek[0] = use ? __builtin_bit_cast(uint64_t, token_key(sc, tok)) : 0ull;
+    };
+    gather_entries(false);
+    // The R block maxima are R distinct entries at or above the R-th block's score with that
+    // block's last token, which bounds the R-th best entry from below. select_top rewrites L.top
+    // only after barriers that follow every read of it here.
+    uint64_t lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
+    if (lower_e != 0) {
+      const uint32_t last = (uint32_t)token_key_token(L.top[R - 1]) * kBlockN + (kBlockN - 1);
+      lower_e = (lower_e & ~0xFFFFFull) | (0xFFFFFu - last);
+    }
+    if (tid == 0) L.dec[3] = 0;  // the entry gather's counter (select_top has read it for the blocks)
+    const bool redo = __syncthreads_or(bad);
+    if (redo) {
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        const int b = tid + kSrThreads * j;
+        srt[j] = b < nblk ? __builtin_bit_cast(uint64_t, token_key(s[(int64_t)b * kc], c[(int64_t)b * kc])) : 0ull;
+      }
+      select_top<BPT>(L, srt, R, 0ull);
+      gather_entries(true);
+      lower_e = __builtin_bit_cast(uint64_t, L.top[R - 1]);
+    }
+    select_top<1>(L, ek, R, lower_e, !redo);
+  }
   // the selection: L.top[j] holds the j-th selected token's key (0: none, token -1); nothing
   // rewrites L.top after this
   auto sel_at = [&](int j) { return token_key_token(L.top[j]); };
