@@ -166,10 +166,11 @@ def test_select_rerank_fused(i2h, M, N, K, kc, R, k, grid):
         pu.check_rerank(host(fex), si.bits(x), si.bits(W), host(fsel))
 
 
-def _first_gather(cs_row, kc, R):
-    """Keys the fused tail gathers on its first pass over a row's blocks: those at or above the
+def _bound_counts(cs_row, ci_row, kc, R):
+    """What the fused tail's ranking bound lets through on a row: the blocks at or above the
     smallest of its 16 waves' ceil(R / 16)-th best block keys (thread t holds blocks t, t + 1024,
-    ...; wave t // 64); a key is (best score descending, block ascending)."""
+    ...; wave t // 64; a block key is (best score descending, block ascending)), and the valid
+    entries of those blocks at or above (that bound's score, the last token of its block)."""
     nblk = cs_row.shape[0] // kc
     best = cs_row[::kc].astype(np.float64)
     order = np.lexsort((np.arange(nblk), -best))
@@ -178,18 +179,23 @@ def _first_gather(cs_row, kc, R):
     t, worst = (R + 15) // 16, -1
     for w in range(16):
         r = np.sort(rank[(np.arange(nblk) % 1024) // 64 == w])
-        if r.size < t:
-            return nblk
+        assert r.size >= t
         worst = max(worst, int(r[t - 1]))
-    return worst + 1
+    bT = int(order[worst])
+    sT = best[bT]
+    own = (best > sT) | ((best == sT) & (np.arange(nblk) <= bT))
+    sc, tk = cs_row.reshape(nblk, kc).astype(np.float64), ci_row.reshape(nblk, kc)
+    above = (sc > sT) | ((sc == sT) & (tk <= 64 * bT + 63))
+    return int(own.sum()), int((above & own[:, None] & (tk >= 0)).sum())
 
 
 def test_select_rerank_gather_paths(i2h):
-    """Rows built so that the first gather of the block ranking holds 32 keys (every wave has two
-    far-ahead blocks), about 200 (one wave's second best sits low: the 4-threads-per-key ranking)
-    and nearly every block (one wave holds no high block: the radix passes). Each row's count is
-    checked on the host first; the fused tail must still equal the separate calls and the
-    oracle's selection."""
+    """Rows built so that the ranking bound lets through 32 entries (every wave has two far-ahead
+    blocks: one ranking, 8 threads per key), about 200 (one wave's second best sits low: one
+    ranking, 4 threads per key) and nearly every block (one wave holds no high block: more than
+    256 entries, so the general path, whose block ranking takes the radix passes). Each row's
+    counts are checked on the host first; the fused tail must still equal the separate calls and
+    the oracle's selection."""
     N, K, kc, R, k = 124160, 1024, 8, 32, 4
     sc = si.gen_scores(3, N, seed=5).numpy().astype(np.float64)
     nb = N // 64
@@ -205,8 +211,9 @@ def test_select_rerank_gather_paths(i2h):
     sc[1, 64 * b0] = 3.0
     sc[1, 64 * b1] = 2.95
     cs, ci = oracle.block_emit(sc, kc)
-    counts = [_first_gather(cs[m], kc, R) for m in range(3)]
-    assert counts[0] == 32 and 128 < counts[1] <= 256 and counts[2] > 256, counts
+    counts = [_bound_counts(cs[m], ci[m], kc, R) for m in range(3)]
+    (_, e0), (_, e1), (b2, e2) = counts
+    assert e0 == 32 and 128 < e1 <= 256 and e2 > 256 and b2 > 256, counts
     want_sel = oracle.select_top_r(cs, ci, R)
     cs_d, ci_d = torch.from_numpy(cs.astype(np.float32)).to(DEV), torch.from_numpy(ci).to(DEV)
     g = torch.Generator(device=DEV).manual_seed(91)
