@@ -69,7 +69,8 @@ __device__ __forceinline__ double dpp_f64(double v) {
 // top-8 lists meet through DPP quad permutes.
 template <int MR, int P>
 __device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, int kc, int64_t ld,
-                                          float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+                                          float* __restrict__ cand_score, int32_t* __restrict__ cand_idx,
+                                          float* __restrict__ bmax) {
   constexpr int V = 64 / P;
   const int lane = threadIdx.x & 63;
   const int row = lane / P, part = lane % P;
@@ -104,6 +105,7 @@ __device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, 
         const bool ok = tok < N;
         cand_score[at + i] = ok ? key_value(k[i]) : -__builtin_inff();
         cand_idx[at + i] = ok ? tok : -1;
+        if (i == 0 && bmax != nullptr) bmax[(int64_t)row * (ld / kc) + b] = ok ? key_value(k[i]) : -__builtin_inff();
       }
     }
   }
@@ -112,7 +114,8 @@ __device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, 
 // Block top-kc for any kc <= 64: lane c counts the columns of its row that rank before it.
 template <int MR>
 __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64_t ld,
-                             float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+                             float* __restrict__ cand_score, int32_t* __restrict__ cand_idx,
+                             float* __restrict__ bmax) {
   const int lane = threadIdx.x & 63;
   for (int m = 0; m < M && m < MR; ++m) {
     const float* tr = tw + m * kTRow;
@@ -128,6 +131,7 @@ __device__ void emit_counted(const float* tw, int M, int b, int N, int kc, int64
       const int64_t at = (int64_t)m * ld + (int64_t)b * kc + rank;
       cand_score[at] = ok ? v : -__builtin_inff();
       cand_idx[at] = ok ? tok : -1;
+      if (rank == 0 && bmax != nullptr) bmax[(int64_t)m * (ld / kc) + b] = ok ? v : -__builtin_inff();
     }
   }
 }

@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, float* __restrict__ bmax) {
   constexpr int MR = 16 * MT;
   extern __shared__ float smem[];
   const int Q = K >> 2, NG = Q / kGroup, KG = K / kGroup;
@@ -180,6 +180,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
       const int64_t at = (int64_t)m * ld + (int64_t)b * kc + lane;
       cand_score[at] = ok ? v : -__builtin_inff();
       cand_idx[at] = ok ? tok : -1;
+      if (lane == 0 && bmax != nullptr) bmax[(int64_t)m * nblk + b] = ok ? v : -__builtin_inff();
     }
   }
 }
@@ -225,7 +226,8 @@ __device__ __forceinline__ uint64_t block_key(float v, int col_in_block) {
 // keys of each row, four lanes per key (lane = 4 i + q compares key 16 wave + i with keys
 // 16 q .. 16 q + 15), and the four partial counts are summed across the quad.
 __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, int N, int kc, int64_t ld,
-                                            float* __restrict__ cand_score, int32_t* __restrict__ cand_idx) {
+                                            float* __restrict__ cand_score, int32_t* __restrict__ cand_idx,
+                                            float* __restrict__ bmax) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane & 3, i = wave * 16 + (lane >> 2);
   for (int m = 0; m < M; ++m) {
@@ -245,6 +247,8 @@ __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, in
       const int64_t at = (int64_t)m * ld + (int64_t)b * kc + rank;
       cand_score[at] = ok ? from_ordered_key((uint32_t)(mine >> 32)) : -__builtin_inff();
       cand_idx[at] = ok ? tok : -1;
+      if (rank == 0 && bmax != nullptr)
+        bmax[(int64_t)m * (ld / kc) + b] = ok ? from_ordered_key((uint32_t)(mine >> 32)) : -__builtin_inff();
     }
   }
 }
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, float* __restrict__ bmax, int32_t* __restrict__ zc) {
   constexpr int RR = MAXR < 4 ? MAXR : 4;  // accumulator rows per lane that can be real
   static_assert(VAR == kVarDesign || (MAXR == 1 && XLDS && NGC > 0), "alternatives: one row, x in LDS");
   constexpr int GV = VAR == kVarG64 ? 64 : kGroup;  // quantisation group along k
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
   for (int r = 0; r < RR; ++r)
     ck[(4 * h + r) * kBlockN + wave * 16 + col] = block_key(nvalid ? acc[r] : -__builtin_inff(), wave * 16 + col);
   __syncthreads();
-  emit_ranked(ck, M, b, N, kc, (int64_t)nblk * kc, cand_score, cand_idx);
+  emit_ranked(ck, M, b, N, kc, (int64_t)nblk * kc, cand_score, cand_idx, bmax);
 }
 
 // One wave per row of x: lane l sums elements 8l..8l+7 of each 512-element chunk (one 16-byte
@@ -612,24 +616,24 @@ __global__ __launch_bounds__(256) void xsum_kernel(const uint16_t* __restrict__ 
 template <int MT>
 int launch_coarse(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                   const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y,
-                  hipStream_t s) {
+                  float* bmax, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = (size_t)(K / kGroup) * 16 * MT * 4 + (size_t)16 * MT * kBlockN * 4;
   hipLaunchKernelGGL(coarse_kernel<MT>, dim3(nblk), dim3(kCoarseThreads), lds, s, x, xs, M, packed, S,
-                     ZS, N, K, kc, nblk, cs, ci, y);
+                     ZS, N, K, kc, nblk, cs, ci, y, bmax);
   return check_launch();
 }
 
 template <int MAXR, bool XLDS>
 int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
-                 hipStream_t s) {
+                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax,
+                 int32_t* zc, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
   // the span loop unrolled for the K of the head's family, a run-time loop otherwise
   auto go = [&](auto ngc) {
     hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, decltype(ngc)::value>), dim3(nblk), dim3(kCoarseThreads), lds,
-                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y, zc);
+                       s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y, bmax, zc);
   };
   switch (K) {
     case 5120: go(std::integral_constant<int, 10>{}); break;
@@ -651,7 +655,7 @@ int launch_small_variant(const uint16_t* x, const float* xs, const uint8_t* pack
   const size_t lds = small_lds_bytes(K, 1, VAR == kVarG64 ? 64 : kGroup);
   auto go = [&](auto ngc) {
     hipLaunchKernelGGL((coarse_small_kernel<1, true, decltype(ngc)::value, VAR>), dim3(nblk), dim3(kCoarseThreads), lds,
-                       s, x, xs, 1, packed, S, ZS, N, K, kc, nblk, cs, ci, nullptr, nullptr);
+                       s, x, xs, 1, packed, S, ZS, N, K, kc, nblk, cs, ci, nullptr, nullptr, nullptr);
   };
   if (K == 5120) go(std::integral_constant<int, 10>{});
   else go(std::integral_constant<int, 1>{});
@@ -684,22 +688,23 @@ namespace {
 
 // M <= 4 rows.
 int small_band(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-               const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
+               const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
                hipStream_t s) {
   if (M == 1 && small_lds_bytes(K, 1) <= 65536)
-    return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
+    return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
   if (M <= 4 && small_lds_bytes(K, 4) <= 65536)
-    return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
-  return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, zc, s);
+    return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
+  return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
 }
 
 // The generic kernel (global A loads, any K) for up to kTileMaxRows rows; needs xs.
 int generic_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, hipStream_t s) {
+                 const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax,
+                 hipStream_t s) {
   if (!xs) return I2H_ERR_ARG;
-  if (M <= 16) return launch_coarse<1>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
-  if (M <= 32) return launch_coarse<2>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
-  return launch_coarse<4>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, s);
+  if (M <= 16) return launch_coarse<1>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, s);
+  if (M <= 32) return launch_coarse<2>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, s);
+  return launch_coarse<4>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, s);
 }
 
 }  // namespace
@@ -729,7 +734,8 @@ int xsum_launch(const uint16_t* x, int64_t M, int64_t K, float* xs, hipStream_t 
 
 int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed,
                   const uint16_t* S, const uint16_t* ZS, int64_t N, int64_t K, int kcand,
-                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s, int32_t* zero_cnt) {
+                  float* cand_score, int32_t* cand_idx, uint16_t* y, hipStream_t s, int32_t* zero_cnt,
+                  float* bmax) {
   if (!x || !packed || !S || !ZS || !cand_score || !cand_idx) return I2H_ERR_ARG;
   if (!xs && !coarse_sums_x(M, K)) return I2H_ERR_ARG;  // in-kernel group sums need x in LDS
   if (M < 1 || N < 1 || N > ((int64_t)1 << 30) || check_k(K) != I2H_OK) return I2H_ERR_SHAPE;
@@ -749,20 +755,21 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     const float* xsc = xs ? xs + m0 * (K / kGroup) : nullptr;
     float* csc = cand_score + m0 * ld;
     int32_t* cic = cand_idx + m0 * ld;
+    float* bmc = bmax ? bmax + m0 * nblk_of(N) : nullptr;
     uint16_t* yc = y ? y + m0 * N : nullptr;
     int32_t* zcc = zero_cnt ? zero_cnt + m0 : nullptr;
     const bool tile_ok = tile_supported(mc, K);
     int st;
     if (mc == 1 || (mc <= 4 && !tile_ok))
       st = xsc || small_sums_x(mc, K)
-               ? small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, zcc, s)
+               ? small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, bmc, zcc, s)
                : I2H_ERR_ARG;
     else if (tile_ok)
-      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, zcc, s);
+      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, bmc, zcc, s);
     else if (!xsc)
       st = I2H_ERR_ARG;
     else
-      st = generic_rows(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, s);
+      st = generic_rows(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, bmc, s);
     if (st != I2H_OK) return st;
   }
   return I2H_OK;

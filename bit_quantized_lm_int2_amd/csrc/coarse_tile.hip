@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, int32_t* __restrict__ zc) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, float* __restrict__ bmax, int32_t* __restrict__ zc) {
   using T = Tile<MT, WAVES>;
   static_assert(VAR == kVarDesign || MT == 1, "alternatives: the 16-row tile");
   constexpr int GV = VAR == kVarG64 ? 64 : kGroup;  // quantisation group along k
@@ -503,9 +503,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   if (b >= nblk) return;
   const int64_t ld = (int64_t)nblk * kc;
   if (kc <= 8)
-    emit_top8<T::MR, T::P>(tw, M, b, N, kc, ld, cand_score, cand_idx);
+    emit_top8<T::MR, T::P>(tw, M, b, N, kc, ld, cand_score, cand_idx, bmax);
   else
-    emit_counted<T::MR>(tw, M, b, N, kc, ld, cand_score, cand_idx);
+    emit_counted<T::MR>(tw, M, b, N, kc, ld, cand_score, cand_idx, bmax);
 }
 
 // Loads ahead: x one stage, the packed stream one span (measured best at 16, 32 and 64 rows).
@@ -518,12 +518,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 
 template <int MT, int WAVES, int NGC>
 int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-                const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc, hipStream_t s) {
+                const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
+                hipStream_t s) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = tile_lds_bytes<MT, WAVES>(NGC * 4);
   hipLaunchKernelGGL((coarse_tile_kernel<MT, WAVES, NGC, I2H_TILE_XPF, I2H_TILE_RPF>),
                      dim3((unsigned)((nblk + WAVES - 1) / WAVES)), dim3(64 * WAVES), lds, s, x, xs, M, packed, S, ZS, N,
-                     kc, nblk, cs, ci, y, zc);
+                     kc, nblk, cs, ci, y, bmax, zc);
   return check_launch();
 }
 
@@ -549,19 +550,22 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
 
 template <int NGC>
 int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
-              const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc, hipStream_t s) {
-  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
+              const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
+              hipStream_t s) {
+  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
   if constexpr (I2H_TILE_MAXMT >= 2)
-    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES32, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
+    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES32, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
   if constexpr (I2H_TILE_MAXMT >= 4)
-    return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, zc, s);
+    return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
   // rows in chunks of 16 through the 16-row tile (a build limited to it)
   const int64_t ld = nblk_of(N) * kc, KG = NGC * 4;
   for (int m0 = 0; m0 < M; m0 += 16) {
     const int mc = M - m0 < 16 ? M - m0 : 16;
     const int st = launch_tile<1, I2H_TILE_WAVES, NGC>(x + (int64_t)m0 * NGC * 512, xs ? xs + (int64_t)m0 * KG : nullptr,
                                                        mc, packed, S, ZS, N, kc, cs + m0 * ld, ci + m0 * ld,
-                                                       y ? y + (int64_t)m0 * N : nullptr, zc ? zc + m0 : nullptr, s);
+                                                       y ? y + (int64_t)m0 * N : nullptr,
+                                                       bmax ? bmax + (int64_t)m0 * nblk_of(N) : nullptr,
+                                                       zc ? zc + m0 : nullptr, s);
     if (st != I2H_OK) return st;
   }
   return I2H_OK;
@@ -577,7 +581,7 @@ int launch_tile_variant(const uint16_t* x, const float* xs, int M, const uint8_t
     constexpr int NGC = decltype(ngc)::value;
     const size_t lds = tile_lds_bytes<1, 4>(NGC * 4 * HV);
     hipLaunchKernelGGL((coarse_tile_kernel<1, 4, NGC, I2H_TILE_XPF, I2H_TILE_RPF, VAR>), dim3((unsigned)((nblk + 3) / 4)),
-                       dim3(256), lds, s, x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, nullptr, nullptr);
+                       dim3(256), lds, s, x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, nullptr, nullptr, nullptr);
   };
   if (K == 5120) go(std::integral_constant<int, 10>{});
   else go(std::integral_constant<int, 1>{});
@@ -591,7 +595,7 @@ int tile_variant_launch(int var, const uint16_t* x, const float* xs, int64_t M, 
                         hipStream_t s) {
   if (M < 1 || M > 16 || (K != 512 && K != 5120)) return I2H_ERR_SHAPE;
   switch (var) {
-    case kVarDesign: return tile_launch(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, nullptr, nullptr, s);
+    case kVarDesign: return tile_launch(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, nullptr, nullptr, nullptr, s);
     case kVarG64: return launch_tile_variant<kVarG64>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
     case kVarC4: return launch_tile_variant<kVarC4>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
     case kVarWTile: return launch_tile_variant<kVarWTile>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
@@ -608,17 +612,17 @@ bool tile_supported(int64_t M, int64_t K) {
 bool tile_sums_x(int64_t M, int64_t K) { return tile_supported(M, K) && M <= 32; }
 
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
-                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, int32_t* zc,
+                const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
                 hipStream_t s) {
   if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
   if (!xs && !tile_sums_x(M, K)) return I2H_ERR_ARG;
   switch (K / 512) {
-    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
-    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
-    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
-    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
-    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
-    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, zc, s);
+    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
   }
 }
 

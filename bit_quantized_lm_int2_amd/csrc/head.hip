@@ -27,7 +27,7 @@ constexpr int64_t kAlign = 256;
 int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Workspace {
-  int64_t xs, cand_score, cand_idx, sel, exact, cnt, total;
+  int64_t xs, cand_score, cand_idx, sel, exact, cnt, bmax, total;
 };
 
 Workspace layout(int64_t M, int64_t N, int64_t K, int kcand, int R) {
@@ -39,7 +39,8 @@ Workspace layout(int64_t M, int64_t N, int64_t K, int kcand, int R) {
   w.sel = up(w.cand_idx + M * ncand * 4);
   w.exact = up(w.sel + M * (int64_t)R * 4);
   w.cnt = up(w.exact + M * (int64_t)R * 4);
-  w.total = up(w.cnt + M * 4);
+  w.bmax = up(w.cnt + M * 4);
+  w.total = up(w.bmax + M * nblk_of(N) * 4);
   return w;
 }
 
@@ -109,6 +110,7 @@ int head_run(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t
   int32_t* sel = reinterpret_cast<int32_t*>(base + w.sel);
   float* ex = reinterpret_cast<float*>(base + w.exact);
   int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt);
+  float* bmax = reinterpret_cast<float*>(base + w.bmax);
   const bool fused = select_rerank_supported(nblk_of(N), kcand, R, N, K);
   const int G = fused ? select_rerank_split(M, R) : 1;
   int32_t* zc = G > 1 ? cnt : nullptr;
@@ -116,11 +118,12 @@ int head_run(const uint16_t* x, int64_t M, const uint8_t* packed, const uint16_t
   const bool own_sums = coarse_sums_x(M, K);
   int st = own_sums ? I2H_OK : xsum_launch(x, M, K, xs, s, zc);
   if (st == I2H_OK)
-    st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s, own_sums ? zc : nullptr);
+    st = coarse_launch(x, own_sums ? nullptr : xs, M, packed, S, ZS, N, K, kcand, cs, ci, y, s, own_sums ? zc : nullptr,
+                       fused ? bmax : nullptr);
   if (st != I2H_OK) return st;
   if (fused)
     return select_rerank_launch(cs, ci, M, nblk_of(N), kcand, R, x, W, ldw, N, K, k, nullptr, nullptr, out_idx,
-                                out_val, s, G, zc, ex);
+                                out_val, s, G, zc, ex, bmax);
   st = select_launch(cs, ci, M, nblk_of(N), kcand, R, sel, s);
   if (st == I2H_OK) st = rerank_finalize_launch(x, M, W, ldw, N, K, sel, R, k, ex, out_idx, out_val, s);
   return st;

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
     const float* __restrict__ cs, const int32_t* __restrict__ ci, int nblk, int kc, int R,
     const uint16_t* __restrict__ x, const void* __restrict__ Wv, const float* __restrict__ wscale, int64_t ldw,
     int N, int K, int k, int32_t* __restrict__ sel_out, float* __restrict__ ex_out, int32_t* __restrict__ oi,
-    float* __restrict__ ov, int G, int32_t* __restrict__ cnt, float* __restrict__ exw) {
+    float* __restrict__ ov, int G, int32_t* __restrict__ cnt, float* __restrict__ exw, const float* __restrict__ bmax) {
   extern __shared__ __align__(16) uint8_t smem[];
   SrLds& L = *reinterpret_cast<SrLds*>(smem);
   uint16_t* xl = reinterpret_cast<uint16_t*>(smem + kSrLdsHead);
@@ -311,11 +311,14 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   // block's rank among blocks needs only its best score and the block index: blocks hold
   // consecutive token ranges, so the lower block holds the lower token on equal scores.
   // every load is issued before any is used (clamped indices; unused values are dropped)
+  // (from bmax when given: the same values, contiguous, so 8 times fewer lines at kcand = 8)
+  const float* bsrc = bmax != nullptr ? bmax + (int64_t)m * nblk : s;
+  const int bstride = bmax != nullptr ? 1 : kc;
   float bs[BPT];
 #pragma unroll
   for (int j = 0; j < BPT; ++j) {
     const int b = tid + kSrThreads * j;
-    bs[j] = s[(int64_t)(b < nblk ? b : nblk - 1) * kc];
+    bs[j] = bsrc[(int64_t)(b < nblk ? b : nblk - 1) * bstride];
   }
   const uint16_t* xr = x + (int64_t)m * K;
   constexpr int kXU = 2;  // 16-byte units of x per thread per round (K <= 16384)
@@ -598,7 +601,7 @@ template <bool FP8>
 int select_rerank_launch_t(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
                            const uint16_t* x, const void* W, const float* wscale, int64_t ldw, int64_t N, int64_t K,
                            int k, int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s,
-                           int G, int32_t* cnt, float* exw) {
+                           int G, int32_t* cnt, float* exw, const float* bmax) {
   if (!cand_score || !cand_idx || !x || !W || !out_idx || !out_val || (FP8 && !wscale)) return I2H_ERR_ARG;
   if (G < 1 || G > R || (G > 1 && (!cnt || !exw || M * G > ((int64_t)1 << 30)))) return I2H_ERR_ARG;
   if (M < 1 || M > (1 << 30) || nblk != nblk_of(N) || ldw < K) return I2H_ERR_SHAPE;
@@ -607,19 +610,19 @@ int select_rerank_launch_t(const float* cand_score, const int32_t* cand_idx, int
   if (!aligned(cand_score, 4) || !aligned(cand_idx, 4) || !aligned(x, 16) || !aligned(W, FP8 ? 8 : 16) ||
       ldw % 8 != 0 || (FP8 && !aligned(wscale, 4)) || !aligned(out_idx, 4) || !aligned(out_val, 4) ||
       (sel && !aligned(sel, 4)) || (exact && !aligned(exact, 4)) || (cnt && !aligned(cnt, 4)) ||
-      (exw && !aligned(exw, 4)))
+      (exw && !aligned(exw, 4)) || (bmax && !aligned(bmax, 4)))
     return I2H_ERR_ALIGN;
   const size_t lds = kSrLdsHead + (size_t)K * 2;
   const dim3 grid((unsigned)(M * G)), block(kSrThreads);
   if (nblk <= kSrThreads)
     hipLaunchKernelGGL((select_rerank_kernel<1, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw, bmax);
   else if (nblk <= 2 * kSrThreads)
     hipLaunchKernelGGL((select_rerank_kernel<2, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw, bmax);
   else
     hipLaunchKernelGGL((select_rerank_kernel<4, FP8>), grid, block, lds, s, cand_score, cand_idx, (int)nblk, kc, R, x,
-                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw);
+                       W, wscale, ldw, (int)N, (int)K, k, sel, exact, out_idx, out_val, G, cnt, exw, bmax);
   return check_launch();
 }
 }  // namespace
@@ -627,9 +630,9 @@ int select_rerank_launch_t(const float* cand_score, const int32_t* cand_idx, int
 int select_rerank_launch(const float* cand_score, const int32_t* cand_idx, int64_t M, int64_t nblk, int kc, int R,
                          const uint16_t* x, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, int k,
                          int32_t* sel, float* exact, int32_t* out_idx, float* out_val, hipStream_t s, int G,
-                         int32_t* cnt, float* exw) {
+                         int32_t* cnt, float* exw, const float* bmax) {
   return select_rerank_launch_t<false>(cand_score, cand_idx, M, nblk, kc, R, x, W, nullptr, ldw, N, K, k, sel, exact,
-                                       out_idx, out_val, s, G, cnt, exw);
+                                       out_idx, out_val, s, G, cnt, exw, bmax);
 }
 
 }  // namespace i2h
@@ -647,5 +650,5 @@ extern "C" int i2h_select_rerank_topk_fp8(const float* cand_score, const int32_t
                                           int64_t ldw, int64_t N, int64_t K, int k, int32_t* sel, float* exact,
                                           int32_t* out_idx, float* out_val, void* stream) {
   return i2h::select_rerank_launch_t<true>(cand_score, cand_idx, M, nblk, kcand, R, x, W8, wscale, ldw, N, K, k, sel,
-                                           exact, out_idx, out_val, (hipStream_t)stream, 1, nullptr, nullptr);
+                                           exact, out_idx, out_val, (hipStream_t)stream, 1, nullptr, nullptr, nullptr);
 }

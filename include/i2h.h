@@ -51,7 +51,7 @@ extern "C" {
 #define I2H_MAX_KCAND 64
 #define I2H_MAX_R 1024
 #define I2H_MAX_NBLK 8192       /* N <= 524288 for the candidate selection */
-#define I2H_NOALLOC_SCRATCH_BYTES (24 << 20) /* device scratch of i2h_head_noalloc, per GPU */
+#define I2H_NOALLOC_SCRATCH_BYTES (26 << 20) /* device scratch of i2h_head_noalloc, per GPU */
 
 /* Element types of the drop-in logits row (i2h_logits). */
 #define I2H_DTYPE_NONE 0        /* no embedding bias */
@@ -311,7 +311,7 @@ I2H_API int i2h_head(const uint16_t* x, int64_t M, const uint8_t* packed, const 
  * i2h_head for callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): the same arguments without the workspace,
  * the same kernels and results bit for bit. The intermediates live in a device array of
- * I2H_NOALLOC_SCRATCH_BYTES (24 MiB) that the library holds on each GPU it runs on until the
+ * I2H_NOALLOC_SCRATCH_BYTES (26 MiB) that the library holds on each GPU it runs on until the
  * process ends; its address is looked up on the first call on a device (the GPU of `stream`),
  * so make that first call outside graph capture. The call allocates nothing: no hipMalloc,
  * hipFree or allocating library routine. A call whose i2h_workspace_bytes() exceeds the scratch
