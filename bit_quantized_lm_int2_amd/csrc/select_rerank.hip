@@ -32,19 +32,17 @@ namespace {
 constexpr int kSrThreads = 1024;
 constexpr int kSrWaves = kSrThreads / kWave;  // 16
 constexpr int kSrMaxR = 64, kSrMaxKc = 8;
+constexpr int kSrCap = 256;  // keys gathered for a counting rank
 constexpr int kSrChunk = 10;  // 512-k steps of the two weight rows a wave has in flight at once
 
 struct SrLds {
-  uint64_t list[256];       // keys gathered for the ranking of a selection (kSrCap)
+  uint64_t list[kSrCap];    // keys gathered for the ranking of a selection
   double top[64];           // a selection, best first, 0-padded
-  uint64_t cand[64];        // per-wave t-th best keys (lower bound of the R-th best)
   uint32_t cnt[kSrWaves][16];  // per-wave digit counts of one radix pass
   uint64_t wmax[kSrWaves], wor[kSrWaves];
-  int32_t wnum[kSrWaves];
   int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
   int32_t last;             // this workgroup is the last of its row's G to finish
-  int32_t ob[kSrWaves][64 * 4];  // per wave: its blocks whose key clears the block bound
-  uint64_t lower;
+  int32_t ob[kSrWaves][64 * 4];  // per wave: its blocks whose key clears the block bound (up to 4 per thread)
   float ex[kSrMaxR];
 };
 constexpr size_t kSrLdsHead = (sizeof(SrLds) + 15) / 16 * 16;
@@ -175,8 +173,6 @@ __device__ void radix_narrow(SrLds& L, const uint64_t (&k)[BPT], int R, int* shi
   *shift_out = shift;
   *prefix_out = prefix;
 }
-
-constexpr int kSrCap = 256;  // keys gathered for a counting rank
 
 // A lower bound of the R-th largest of the keys the block's threads hold (BPT each, 0 = none):
 // the smallest of the 16 waves' t-th best keys, t = ceil(R / 16), since the 16 t keys at or above
