@@ -461,55 +461,71 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
       // scaled in fp32 (the order of rerank_fp8_kernel)
       typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
       const uint8_t* W8 = static_cast<const uint8_t*>(Wv);
-      const uint8_t* w0 = W8 + (int64_t)(v0 ? n0 : 0) * ldw + 8 * lane;
-      const uint8_t* w1 = W8 + (int64_t)(v1 ? n1 : 0) * ldw + 8 * lane;
-      const float sc0 = wscale[v0 ? n0 : 0], sc1 = wscale[v1 ? n1 : 0];
+      const int64_t row0 = v0 ? n0 : 0, row1 = v1 ? n1 : row0;
+      const uint8_t* w0 = W8 + row0 * ldw + 8 * lane;
+      const uint8_t* w1 = W8 + row1 * ldw + 8 * lane;
+      const float sc0 = wscale[row0], sc1 = wscale[row1];
       for (int i0 = 0; i0 < steps; i0 += kSrChunk) {
         u32x2 r0[kSrChunk], r1[kSrChunk];
+        // every load issued unconditionally (a missing token reads a listed row; a step past the
+        // last re-reads the last step), so no branch orders them; only what is valid is summed
 #pragma unroll
         for (int i = 0; i < kSrChunk; ++i) {
-          const bool in = i0 + i < steps;
-          r0[i] = in && v0 ? *reinterpret_cast<const u32x2*>(w0 + 512 * (i0 + i)) : u32x2{0u, 0u};
-          r1[i] = in && v1 ? *reinterpret_cast<const u32x2*>(w1 + 512 * (i0 + i)) : u32x2{0u, 0u};
+          const int st = i0 + i < steps ? i0 + i : steps - 1;
+          r0[i] = *reinterpret_cast<const u32x2*>(w0 + 512 * st);
+          r1[i] = *reinterpret_cast<const u32x2*>(w1 + 512 * st);
         }
+        auto step = [&](int i) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
 #pragma unroll
-        for (int i = 0; i < kSrChunk; ++i) {
-          if (i0 + i < steps) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a00 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e)), sc0), a00);
-              a01 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e + 1)), sc0), a01);
-              a10 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e)), sc1), a10);
-              a11 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e + 1)), sc1), a11);
-            }
+          for (int e = 0; e < 4; ++e) {
+            a00 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e)), sc0), a00);
+            a01 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r0[i][0], r0[i][1], 2 * e + 1)), sc0), a01);
+            a10 = fmaf(bf16_lo(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e)), sc1), a10);
+            a11 = fmaf(bf16_hi(xv[e]), __fmul_rn(fp8_e4m3_value(byte_of(r1[i][0], r1[i][1], 2 * e + 1)), sc1), a11);
           }
+        };
+        if (i0 + kSrChunk <= steps) {  // a whole chunk (K = 5120: the only one), no per-step test
+#pragma unroll
+          for (int i = 0; i < kSrChunk; ++i) step(i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kSrChunk; ++i)
+            if (i0 + i < steps) step(i);
         }
       }
     } else {
       const uint16_t* W = static_cast<const uint16_t*>(Wv);
-      const uint16_t* w0 = W + (int64_t)(v0 ? n0 : 0) * ldw + 8 * lane;
-      const uint16_t* w1 = W + (int64_t)(v1 ? n1 : 0) * ldw + 8 * lane;
+      const int64_t row0 = v0 ? n0 : 0, row1 = v1 ? n1 : row0;
+      const uint16_t* w0 = W + row0 * ldw + 8 * lane;
+      const uint16_t* w1 = W + row1 * ldw + 8 * lane;
       for (int i0 = 0; i0 < steps; i0 += kSrChunk) {
         u32x4 r0[kSrChunk], r1[kSrChunk];
+        // every load issued unconditionally (a missing token reads a listed row; a step past the
+        // last re-reads the last step), so no branch orders them; only what is valid is summed
 #pragma unroll
         for (int i = 0; i < kSrChunk; ++i) {
-          const bool in = i0 + i < steps;
-          r0[i] = in && v0 ? ld16(w0 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
-          r1[i] = in && v1 ? ld16(w1 + 512 * (i0 + i)) : u32x4{0u, 0u, 0u, 0u};
+          const int st = i0 + i < steps ? i0 + i : steps - 1;
+          r0[i] = ld16(w0 + 512 * st);
+          r1[i] = ld16(w1 + 512 * st);
         }
+        auto step = [&](int i) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
 #pragma unroll
-        for (int i = 0; i < kSrChunk; ++i) {
-          if (i0 + i < steps) {
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xl + 8 * lane + 512 * (i0 + i));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              a00 = fmaf(bf16_lo(xv[e]), bf16_lo(r0[i][e]), a00);
-              a01 = fmaf(bf16_hi(xv[e]), bf16_hi(r0[i][e]), a01);
-              a10 = fmaf(bf16_lo(xv[e]), bf16_lo(r1[i][e]), a10);
-              a11 = fmaf(bf16_hi(xv[e]), bf16_hi(r1[i][e]), a11);
-            }
+          for (int e = 0; e < 4; ++e) {
+            a00 = fmaf(bf16_lo(xv[e]), bf16_lo(r0[i][e]), a00);
+            a01 = fmaf(bf16_hi(xv[e]), bf16_hi(r0[i][e]), a01);
+            a10 = fmaf(bf16_lo(xv[e]), bf16_lo(r1[i][e]), a10);
+            a11 = fmaf(bf16_hi(xv[e]), bf16_hi(r1[i][e]), a11);
           }
+        };
+        if (i0 + kSrChunk <= steps) {  // a whole chunk (K = 5120: the only one), no per-step test
+#pragma unroll
+          for (int i = 0; i < kSrChunk; ++i) step(i);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kSrChunk; ++i)
+            if (i0 + i < steps) step(i);
         }
       }
     }
