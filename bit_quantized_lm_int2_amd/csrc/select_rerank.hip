@@ -42,6 +42,7 @@ struct SrLds {
   uint64_t wmax[kSrWaves], wor[kSrWaves];
   int32_t dec[4];           // digit, keys still needed, keys in the digit's bin, gathered
   int32_t last;             // this workgroup is the last of its row's G to finish
+  int32_t bad;              // some listed block's best entry is invalid (a caller's list)
   int32_t ob[kSrWaves][64 * 4];  // per wave: its blocks whose key clears the block bound (up to 4 per thread)
   float ex[kSrMaxR];
 };
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
   // counting rank orders them. When T is unknown, a block's best entry is invalid (a caller's
   // list; the ranking must then follow tokens) or more than 256 entries clear Te, the row takes
   // the general path: the R best blocks, then their entries.
+  if (tid == 0) L.bad = 0;  // ordered before the flag's writes by block_lower's barrier
   const uint64_t T = block_lower<BPT>(L, srt, R);  // the gather counter is 0 past its barrier
   bool done = false;
   if (T != 0) {  // block-uniform
@@ -390,7 +392,9 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
       }
       wave_append<2>(L, ek, take, kSrCap);
     }
-    const bool any_bad = __syncthreads_or(bad);
+    if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) L.bad = 1;
+    __syncthreads();
+    const bool any_bad = L.bad != 0;
     const int n = L.dec[3];
     if (!any_bad && n <= kSrCap) {
       rank_gathered(L, n, R);
