@@ -580,7 +580,10 @@ __global__ __launch_bounds__(kSrThreads) void select_rerank_kernel(
         ov[m] = token_key_score(best);
       }
     } else {
-      wave_sort_f64<1>(fk);
+      if (R <= 32)
+        wave_sort_f64<1, 32>(fk);  // the R keys sit in lanes 0 .. 31
+      else
+        wave_sort_f64<1>(fk);
       if (lane < k) {
         oi[(int64_t)m * k + lane] = token_key_token(fk[0]);
         ov[(int64_t)m * k + lane] = token_key_score(fk[0]);

@@ -67,12 +67,14 @@ __device__ __forceinline__ double lane_xor_f64(double v, int s) {  // s a consta
 }
 
 // Descending bitonic sort of the 64 * KPL keys of a wave, KPL per lane, key index e * 64 + lane.
-template <int KPL>
+// With NMAX < 64 (KPL = 1) only the stages up to NMAX run: each aligned run of NMAX lanes is
+// sorted on its own, lanes 0 .. NMAX - 1 descending.
+template <int KPL, int NMAX = 64 * KPL>
 __device__ __forceinline__ void wave_sort_f64(double (&k)[KPL]) {
   const int lane = threadIdx.x & 63;
-  constexpr int n = 64 * KPL;
+  static_assert(NMAX == 64 * KPL || (KPL == 1 && NMAX >= 2 && (NMAX & (NMAX - 1)) == 0), "NMAX: a power of two");
 #pragma unroll
-  for (int size = 2; size <= n; size <<= 1) {
+  for (int size = 2; size <= NMAX; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       if (stride >= 64) {
