@@ -193,6 +193,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 //   * quarters 0-2 are dequantised with a mask alone (dequant.h), the high byte of each half
 //     brought down by one shift shared by the four quarters: 12 VALU ops per 16 weights;
 //   * only the accumulator rows that can hold a real row are scaled.
+// In the head it takes one or two rows (two rows: 112 VGPRs and 34 KB of LDS keep four
+// workgroups per CU; from three rows x in LDS costs occupancy and the tile kernel is faster).
 // ---------------------------------------------------------------------------------------------
 
 #ifndef I2H_COARSE_PF
@@ -211,9 +213,10 @@ constexpr int kHalfOff = I2H_SMALL_SECTOR ? 64 : 16;  // byte offset of its seco
 #endif  // 128-byte spans of the packed stream in flight per lane
 
 // LDS footprint of coarse_small_kernel in bytes: S|ZS for the block's rows, xs transposed (G: the
-// quantisation group), the block's 64-bit ranking keys, and (xrows > 0) x itself.
-__host__ __device__ constexpr size_t small_lds_bytes(int K, int xrows, int G = kGroup) {
-  return (size_t)64 * (K / G) * 4 + (size_t)(K / G) * 16 * 4 + (size_t)16 * kBlockN * 8 + (size_t)xrows * K * 2;
+// quantisation group), the block's 64-bit ranking keys for its maxr rows, and x itself when xlds.
+__host__ __device__ constexpr size_t small_lds_bytes(int K, int maxr, bool xlds, int G = kGroup) {
+  return (size_t)64 * (K / G) * 4 + (size_t)(K / G) * 16 * 4 + (size_t)maxr * kBlockN * 8 +
+         (xlds ? (size_t)maxr * K * 2 : 0);
 }
 
 // Ranking key of a coarse logit in its block: higher value first, then lower column.
@@ -262,7 +265,7 @@ __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, in
 // four groups, with x in LDS in natural order; the weight tile feeds the dequantised weights to
 // the matrix cores and needs no group sums.
 template <int MAXR, bool XLDS, int NGC, int VAR = kVarDesign>
-__global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
+__global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : 1) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
@@ -278,8 +281,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
   const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / GV;
   uint32_t* sz = lds;                                        // [64][KG]: S | ZS << 16
   float* xsT = reinterpret_cast<float*>(sz + 64 * KG);       // [KG][16]
-  uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * 16);  // [16][64] ranking keys
-  uint16_t* xl = reinterpret_cast<uint16_t*>(ck + 16 * kBlockN);  // [MAXR][K] when XLDS
+  uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * 16);  // [MAXR][64] ranking keys
+  uint16_t* xl = reinterpret_cast<uint16_t*>(ck + MAXR * kBlockN);  // [MAXR][K] when XLDS
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x, n0 = b * kBlockN;
@@ -573,8 +576,9 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_small_kernel(
     }
   }
 #pragma unroll
-  for (int r = 0; r < RR; ++r)
-    ck[(4 * h + r) * kBlockN + wave * 16 + col] = block_key(nvalid ? acc[r] : -__builtin_inff(), wave * 16 + col);
+  for (int r = 0; r < RR; ++r)  // rows past MAXR (lanes h > 0) hold no row of x
+    if (4 * h + r < MAXR)
+      ck[(4 * h + r) * kBlockN + wave * 16 + col] = block_key(nvalid ? acc[r] : -__builtin_inff(), wave * 16 + col);
   __syncthreads();
   emit_ranked(ck, M, b, N, kc, (int64_t)nblk * kc, cand_score, cand_idx, bmax);
 }
@@ -629,7 +633,7 @@ int launch_small(const uint16_t* x, const float* xs, int M, const uint8_t* packe
                  const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax,
                  int32_t* zc, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
-  const size_t lds = small_lds_bytes(K, XLDS ? MAXR : 0);
+  const size_t lds = small_lds_bytes(K, MAXR, XLDS);
   // the span loop unrolled for the K of the head's family, a run-time loop otherwise
   auto go = [&](auto ngc) {
     hipLaunchKernelGGL((coarse_small_kernel<MAXR, XLDS, decltype(ngc)::value>), dim3(nblk), dim3(kCoarseThreads), lds,
@@ -652,7 +656,7 @@ template <int VAR>
 int launch_small_variant(const uint16_t* x, const float* xs, const uint8_t* packed, const uint16_t* S,
                          const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, hipStream_t s) {
   const int nblk = (int)nblk_of(N);
-  const size_t lds = small_lds_bytes(K, 1, VAR == kVarG64 ? 64 : kGroup);
+  const size_t lds = small_lds_bytes(K, 1, true, VAR == kVarG64 ? 64 : kGroup);
   auto go = [&](auto ngc) {
     hipLaunchKernelGGL((coarse_small_kernel<1, true, decltype(ngc)::value, VAR>), dim3(nblk), dim3(kCoarseThreads), lds,
                        s, x, xs, 1, packed, S, ZS, N, K, kc, nblk, cs, ci, nullptr, nullptr, nullptr);
@@ -664,7 +668,7 @@ int launch_small_variant(const uint16_t* x, const float* xs, const uint8_t* pack
 
 // True when the small kernel keeps x in LDS for M rows of K (and then sums the groups itself).
 bool small_sums_x(int64_t M, int64_t K) {
-  return (M == 1 && small_lds_bytes((int)K, 1) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4) <= 65536);
+  return (M <= 2 && small_lds_bytes((int)K, (int)M, true) <= 65536) || (M <= 4 && small_lds_bytes((int)K, 4, true) <= 65536);
 }
 
 }  // namespace
@@ -690,9 +694,11 @@ namespace {
 int small_band(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                const uint16_t* ZS, int N, int K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
                hipStream_t s) {
-  if (M == 1 && small_lds_bytes(K, 1) <= 65536)
+  if (M == 1 && small_lds_bytes(K, 1, true) <= 65536)
     return launch_small<1, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
-  if (M <= 4 && small_lds_bytes(K, 4) <= 65536)
+  if (M == 2 && small_lds_bytes(K, 2, true) <= 65536)
+    return launch_small<2, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
+  if (M <= 4 && small_lds_bytes(K, 4, true) <= 65536)
     return launch_small<4, true>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
   return launch_small<4, false>(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, y, bmax, zc, s);
 }
@@ -746,9 +752,10 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
   // only the small kernel zeroes counters: the caller passes them when every row runs there
   if (zero_cnt && (xs || !coarse_sums_x(M, K) || !aligned(zero_cnt, 4))) return I2H_ERR_ARG;
   const int64_t ld = nblk_of(N) * kcand;
-  // rows go in chunks of kTileMaxRows; a chunk of one row, or of at most 4 rows with a K the tile
-  // kernel is not built for, runs the small kernel; a larger one the tile kernel where it is built
-  // for K, else the generic kernel
+  // rows go in chunks of kTileMaxRows; a chunk of one or two rows (x in LDS; from three rows the
+  // 16-row tile is faster: x for 3 or 4 rows costs the small kernel occupancy), or of at most 4
+  // rows with a K the tile kernel is not built for, runs the small kernel; a larger one the tile
+  // kernel where it is built for K, else the generic kernel
   for (int64_t m0 = 0; m0 < M; m0 += kTileMaxRows) {
     const int64_t mc = M - m0 < kTileMaxRows ? M - m0 : kTileMaxRows;
     const uint16_t* xc = x + m0 * K;
@@ -760,7 +767,7 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
     int32_t* zcc = zero_cnt ? zero_cnt + m0 : nullptr;
     const bool tile_ok = tile_supported(mc, K);
     int st;
-    if (mc == 1 || (mc <= 4 && !tile_ok))
+    if ((mc <= 2 && small_sums_x(mc, K)) || (mc <= 4 && !tile_ok))
       st = xsc || small_sums_x(mc, K)
                ? small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, bmc, zcc, s)
                : I2H_ERR_ARG;
