@@ -389,7 +389,12 @@ def run_and_check(i2h, xb, Wb, kc=8, R=32, k=1, packed_o=None, coarse_o=None, ro
     (16, 130, 5120, 8, 16, 1),     # three blocks: one workgroup with an idle wave
     (24, 3001, 5120, 12, 64, 16),  # 32-row tile; kcand above 8 (counted emit)
     (40, 1000, 512, 3, 16, 4),     # 64-row tile, three candidates per block
-    (4, 1037, 5120, 8, 32, 16),    # 2-4 rows through the 16-row tile (with i2h_xsum), ragged tail
+    (4, 1037, 5120, 8, 32, 16),    # 3-4 rows through the 16-row tile, ragged tail
+    (2, 1037, 5120, 8, 32, 16),    # two rows through the one-row kernel's 2-row form, ragged tail
+    (2, 1500, 4096, 8, 32, 1),     # the 2-row form unrolled for other K of the family
+    (2, 999, 2048, 3, 16, 4),
+    (2, 3001, 3072, 8, 64, 16),
+    (2, 640, 1024, 8, 32, 1),
     (65, 1000, 5120, 8, 32, 1),    # a 64-row launch and a 1-row chunk on the M = 1 kernel with xs
     (33, 643, 5120, 8, 32, 16),    # 64-row tile with one row of its last m-tile, tail block
     (1, 1, 512, 8, 32, 1),         # a one-token vocabulary: one valid candidate
