@@ -30,6 +30,10 @@ constexpr int kC4Pf = I2H_C4_PF;  // spans of packed bytes (and x) in flight per
 #define I2H_C4_PF_XL 2
 #endif
 constexpr int kC4PfXl = I2H_C4_PF_XL;  // spans in flight when x sits in LDS
+#ifndef I2H_C4_PF_XL5120
+#define I2H_C4_PF_XL5120 2
+#endif
+constexpr int kC4PfXl5120 = I2H_C4_PF_XL5120;  // the same, with the span loop unrolled (K = 5120)
 #ifndef I2H_C4_XL_BYTES
 #define I2H_C4_XL_BYTES 32768
 #endif
@@ -95,7 +99,10 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
 
 // XL: x (at most kC4XlBytes) is staged in LDS once per workgroup and the fragments are read from
 // there, so a ring slot holds only the packed bytes and the scales and PF slots fit in registers.
-template <int MT, bool XL, int PF>
+// NSC > 0: the number of 128-byte spans per half row (K / 256), a compile-time constant, so the
+// span loop is unrolled completely and every wait for a span in flight is exact (a run-time loop
+// with its loads under a test makes the compiler wait for every load at each iteration).
+template <int MT, bool XL, int PF, int NSC = 0>
 __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ xs,
                                                              int M, const uint8_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ S,
@@ -185,14 +192,22 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   Slot ring[PF];
 #pragma unroll
   for (int q = 0; q < PF; ++q) fetch(ring[q], q < NS ? q : NS - 1);
-  for (int gb0 = 0; gb0 < NS; gb0 += PF) {
+  if constexpr (NSC > 0) {
 #pragma unroll
-    for (int q = 0; q < PF; ++q) {
-      const int gb = gb0 + q;
-      if (gb < NS) {
-        body(ring[q], gb);
-        const int nx = gb + PF;
-        fetch(ring[q], nx < NS ? nx : NS - 1);
+    for (int gb = 0; gb < NSC; ++gb) {
+      body(ring[gb % PF], gb);
+      if (gb + PF < NSC) fetch(ring[gb % PF], gb + PF);
+    }
+  } else {
+    for (int gb0 = 0; gb0 < NS; gb0 += PF) {
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        const int gb = gb0 + q;
+        if (gb < NS) {
+          body(ring[q], gb);
+          const int nx = gb + PF;
+          fetch(ring[q], nx < NS ? nx : NS - 1);
+        }
       }
     }
   }
@@ -236,8 +251,12 @@ void launch4(const uint16_t* x, const float* xs, int M, const uint8_t* packed, c
   const size_t xbytes = (size_t)M * K * 2;
   if constexpr (MT == 1) {
     if (xbytes <= kC4XlBytes) {
-      hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl>), dim3((unsigned)nblk), dim3(kC4Threads), lds + xbytes, s,
-                         x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+      if (K == 5120)  // the head's K: the span loop unrolled
+        hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl5120, 20>), dim3((unsigned)nblk), dim3(kC4Threads),
+                           lds + xbytes, s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+      else
+        hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl>), dim3((unsigned)nblk), dim3(kC4Threads), lds + xbytes,
+                           s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
       return;
     }
   }
