@@ -31,7 +31,7 @@ constexpr int kC4Pf = I2H_C4_PF;  // spans of packed bytes (and x) in flight per
 #endif
 constexpr int kC4PfXl = I2H_C4_PF_XL;  // spans in flight when x sits in LDS
 #ifndef I2H_C4_PF_XL5120
-#define I2H_C4_PF_XL5120 2
+#define I2H_C4_PF_XL5120 3
 #endif
 constexpr int kC4PfXl5120 = I2H_C4_PF_XL5120;  // the same, with the span loop unrolled (K = 5120)
 #ifndef I2H_C4_XL_BYTES
@@ -115,6 +115,11 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   float* xsT = smem;             // [KG][MR]: xs transposed, zero past row M
   float* cbuf = smem + KG * MR;  // [MR][64]: the block's logits for the emit
   uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + MR * kBlockN);  // [M][K] when XL
+  // with the span loop unrolled (XL): the block's S | ZS << 16 rows, [64][KG | 1], each wave's 16
+  // rows staged by that wave, so the ring holds only packed bytes
+  constexpr bool kSzL = XL && NSC > 0;
+  const int KGP = KG | 1;
+  uint32_t* szl = reinterpret_cast<uint32_t*>(xl + (XL ? M * K : 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
   const int b = blockIdx.x;
@@ -125,6 +130,15 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   for (int i = tid; i < KG * MR; i += kC4Threads) {
     const int g = i / MR, m = i - g * MR;
     xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
+  }
+  if constexpr (kSzL) {  // this wave's 16 rows (rows past N: zeros, never emitted)
+    const int r0 = b * kBlockN + wave * 16;
+    for (int e = lane; e < 16 * KG; e += kWave) {
+      const int r = e / KG, g = e - r * KG;
+      const bool ok = r0 + r < N;
+      const uint32_t sb = ok ? S[(int64_t)(r0 + r) * KG + g] : 0u, zb = ok ? ZS[(int64_t)(r0 + r) * KG + g] : 0u;
+      szl[(wave * 16 + r) * KGP + g] = sb | (zb << 16);
+    }
   }
   if constexpr (XL)
     for (int u = tid; u < M * K / 8; u += kC4Threads)
@@ -151,10 +165,12 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   auto fetch = [&](Slot& sl, int gb) {
     sl.p0 = ld16(prow + gb * kGroup);
     sl.p1 = ld16(prow + gb * kGroup + 16);
-    sl.s0 = srow[gb];
-    sl.z0 = zrow[gb];
-    sl.s1 = srow[KG / 2 + gb];
-    sl.z1 = zrow[KG / 2 + gb];
+    if constexpr (!kSzL) {
+      sl.s0 = srow[gb];
+      sl.z0 = zrow[gb];
+      sl.s1 = srow[KG / 2 + gb];
+      sl.z1 = zrow[KG / 2 + gb];
+    }
     if constexpr (MT == 1 && !XL) {
       const uint16_t* xq = xh + (int64_t)xrow * K + gb * kGroup;
 #pragma unroll
@@ -185,9 +201,21 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
       }
       xa = xv;
     }
-    half4<MT, 0>(acc, dw, xa, xg, M, K, col, bf16_lo(sl.s0), bf16_lo(sl.z0), xsT + g0 * MR, h);
-    half4<MT, 1>(acc, dw, xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(sl.s1), bf16_lo(sl.z1),
-                 xsT + g1 * MR, h);
+    uint32_t s0, z0, s1, z1;
+    if constexpr (kSzL) {
+      const uint32_t w0 = szl[(wave * 16 + col) * KGP + g0], w1 = szl[(wave * 16 + col) * KGP + g1];
+      s0 = w0 & 0xffffu;
+      z0 = w0 >> 16;
+      s1 = w1 & 0xffffu;
+      z1 = w1 >> 16;
+    } else {
+      s0 = sl.s0;
+      z0 = sl.z0;
+      s1 = sl.s1;
+      z1 = sl.z1;
+    }
+    half4<MT, 0>(acc, dw, xa, xg, M, K, col, bf16_lo(s0), bf16_lo(z0), xsT + g0 * MR, h);
+    half4<MT, 1>(acc, dw, xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(s1), bf16_lo(z1), xsT + g1 * MR, h);
   };
   Slot ring[PF];
 #pragma unroll
@@ -251,9 +279,10 @@ void launch4(const uint16_t* x, const float* xs, int M, const uint8_t* packed, c
   const size_t xbytes = (size_t)M * K * 2;
   if constexpr (MT == 1) {
     if (xbytes <= kC4XlBytes) {
-      if (K == 5120)  // the head's K: the span loop unrolled
+      if (K == 5120)  // the head's K: the span loop unrolled, S / ZS rows in LDS
         hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl5120, 20>), dim3((unsigned)nblk), dim3(kC4Threads),
-                           lds + xbytes, s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
+                           lds + xbytes + (size_t)64 * ((K / kGroup) | 1) * 4, s, x, xs, M, packed, S, ZS, N, K,
+                           kc, nblk, cs, ci, y);
       else
         hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl>), dim3((unsigned)nblk), dim3(kC4Threads), lds + xbytes,
                            s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
