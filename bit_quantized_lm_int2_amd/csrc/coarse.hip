@@ -193,12 +193,13 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 //   * quarters 0-2 are dequantised with a mask alone (dequant.h), the high byte of each half
 //     brought down by one shift shared by the four quarters: 12 VALU ops per 16 weights;
 //   * only the accumulator rows that can hold a real row are scaled.
-// In the head it takes one or two rows (two rows: 112 VGPRs and 34 KB of LDS keep four
-// workgroups per CU; from three rows x in LDS costs occupancy and the tile kernel is faster).
+// In the head it takes one or two rows (one row: at most 80 VGPRs and 23 KB of LDS, six
+// workgroups per CU, two spans in flight per lane; two rows: 34 KB of LDS, four workgroups per
+// CU; from three rows x in LDS costs occupancy and the tile kernel is faster).
 // ---------------------------------------------------------------------------------------------
 
 #ifndef I2H_COARSE_PF
-#define I2H_COARSE_PF 4
+#define I2H_COARSE_PF 2
 #endif
 constexpr int kPf = I2H_COARSE_PF;
 // Packed bytes per lane and span: 1 = aligned 64-byte sectors (lane h takes bytes 16h and
@@ -265,7 +266,7 @@ __device__ __forceinline__ void emit_ranked(const uint64_t* ck, int M, int b, in
 // four groups, with x in LDS in natural order; the weight tile feeds the dequantised weights to
 // the matrix cores and needs no group sums.
 template <int MAXR, bool XLDS, int NGC, int VAR = kVarDesign>
-__global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : 1) void coarse_small_kernel(
+__global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : (MAXR == 1 && VAR == kVarDesign ? 6 : 1)) void coarse_small_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int K, int kc, int nblk, float* __restrict__ cand_score,
