@@ -255,9 +255,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     for (int nt = 0; nt < kNT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const DqConst dqc = dq_const();
   const uint32_t* szc = szw + col * KGP;
-  f32x4 ps[HV];  // this wave's part of a group sum of x (every column alike), per group of the quarter
-#pragma unroll
-  for (int hf = 0; hf < HV; ++hf) ps[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the group of quarter (contiguous-4: group in the span) t, span gb, half hf
   auto gidx = [](int t, int gb, int hf) { return VAR == kVarC4 ? 4 * gb + t : HV * (t * NG + gb) + hf; };
 
@@ -340,25 +337,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
                   __builtin_bit_cast(bf16x8, a[mt]), bw, p[mt][nt][HV == 2 ? s >> 1 : 0], 0, 0, 0);
           }
         }
-        if (own && qq == sq_q && (unsigned)(s - sq_s0) < (unsigned)(4 / T::SP)) {
-          const u32x4 as = *reinterpret_cast<const u32x4*>(xa + sq_mt * 16 * T::RS + xoff(qq, s));
-          const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
-          ps[HV == 2 ? s >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as), ones,
-                                                                           ps[HV == 2 ? s >> 1 : 0], 0, 0, 0);
-        }
 #pragma unroll
         for (int j = 0; j < kPerSlice; ++j) stage_load(st, slot, (qq * 4 + s) * kPerSlice + j, clamp);
         // the scheduler may not pull later slices (their x fragments and dequant) into this one
         __builtin_amdgcn_sched_barrier(0);
-      }
-      if (own && qq == sq_q) {
-        // ps[hf][r]: this wave's part of the sum of group gidx(t, gb, hf) for row 16 sq_mt + 4 h + r
-#pragma unroll
-        for (int hf = 0; hf < HV; ++hf) {
-          if (col == 0)
-            *reinterpret_cast<f32x4*>(xsl + (sq_part * KG + gidx(t, gb, hf)) * T::MR + 16 * sq_mt + 4 * h) = ps[hf];
-          ps[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
       }
       if constexpr (VAR != kVarWTile) {
         // the scale term of the group (the zero term is added after the loop); contiguous-4 reads
@@ -384,6 +366,29 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) asm volatile("" : "+v"(acc[mt][nt]));
+    }
+    if (own) {
+      // this wave's part of the group sums of quarter t0 + sq_q, row tile sq_mt: its 4 / SP slices
+      // of the stage's x against a B operand of ones (ps[hf][r]: the part of the sum of group
+      // gidx(t0 + sq_q, gb, hf) for row 16 sq_mt + 4 h + r, every column alike), once per stage
+      // rather than inside the quarter loop, where the wave-dependent test of each quarter cost
+      // selects and moves on every quarter
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+      f32x4 ps[HV];
+#pragma unroll
+      for (int hf = 0; hf < HV; ++hf) ps[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4 / T::SP; ++j) {
+        const int s = sq_s0 + j;
+        const u32x4 as = *reinterpret_cast<const u32x4*>(xa + sq_mt * 16 * T::RS + xoff(sq_q, s));
+        ps[HV == 2 ? s >> 1 : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, as), ones,
+                                                                         ps[HV == 2 ? s >> 1 : 0], 0, 0, 0);
+      }
+      if (col == 0) {
+#pragma unroll
+        for (int hf = 0; hf < HV; ++hf)
+          *reinterpret_cast<f32x4*>(xsl + (sq_part * KG + gidx(t0 + sq_q, gb, hf)) * T::MR + 16 * sq_mt + 4 * h) = ps[hf];
+      }
     }
   };
 
