@@ -76,6 +76,9 @@ constexpr size_t tile_lds_bytes(int KG) {
 // contiguous-4 stages 512 consecutive k of x per span in natural order and reads four 8-byte runs
 // per tile and span (32 consecutive k of each of the span's four groups); the weight tile feeds
 // the dequantised weights to the matrix cores, with no group sums and no zero term.
+#ifndef I2H_TILE_PREFA_MT
+#define I2H_TILE_PREFA_MT 2
+#endif
 template <int MT, int WAVES, int NGC, int XPF, int RPF, int VAR = kVarDesign>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
@@ -279,9 +282,28 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
           hw[nt][4 + i] = dw[nt][4 + i] >> 8;
         }
       }
+    // the x fragments of the next slice are read from LDS during the current one (up to 32 rows;
+    // the 64-row tile has no registers for them): the wait for an LDS read otherwise stalls every
+    // slice right before its first MFMA
+    constexpr bool kPrefA = MT <= I2H_TILE_PREFA_MT;
+    auto a_read = [&](int qq, int s, u32x4(&dst)[MT]) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) dst[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + xoff(qq, s));
+    };
+    u32x4 an[MT];
+    if constexpr (kPrefA) a_read(0, 0, an);
 #pragma unroll
     for (int qq = 0; qq < T::QS; ++qq) {
       const int t = t0 + qq;  // the quarter (contiguous-4: the group of the span)
+      // the quarter's S | ZS words, read at its start so that the LDS latency is hidden behind its
+      // slices (the scales are formed from them where they are applied)
+      uint32_t sw[HV][kNT];
+      if constexpr (VAR != kVarWTile) {
+#pragma unroll
+        for (int hf = 0; hf < HV; ++hf)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt) sw[hf][nt] = szc[16 * nt * KGP + gidx(t, gb, hf)];
+      }
       f32x4 p[MT][kNT][HV];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -302,8 +324,13 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 a[MT];
+        if constexpr (kPrefA) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) a[mt] = *reinterpret_cast<const u32x4*>(xa + mt * 16 * T::RS + xoff(qq, s));
+          for (int mt = 0; mt < MT; ++mt) a[mt] = an[mt];
+          if (qq + 1 < T::QS || s < 3) a_read(s < 3 ? qq : qq + 1, s < 3 ? s + 1 : 0, an);
+        } else {
+          a_read(qq, s, a);
+        }
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           pin(dw[nt][2 * s]);
@@ -345,13 +372,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
       if constexpr (VAR != kVarWTile) {
         // the scale term of the group (the zero term is added after the loop); contiguous-4 reads
         // its codes at D = 4, so the scale is S itself
+        const float fq = VAR == kVarC4 ? 1.f : kBiasF[t];
 #pragma unroll
         for (int hf = 0; hf < HV; ++hf) {
-          const int gi = gidx(t, gb, hf);
-          const float fq = VAR == kVarC4 ? 1.f : kBiasF[t];
           float s2[kNT];
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) s2[nt] = fq * __uint_as_float(szc[16 * nt * KGP + gi] << 16);
+          for (int nt = 0; nt < kNT; ++nt) s2[nt] = fq * __uint_as_float(sw[hf][nt] << 16);
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
