@@ -261,6 +261,62 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   // the group of quarter (contiguous-4: group in the span) t, span gb, half hf
   auto gidx = [](int t, int gb, int hf) { return VAR == kVarC4 ? 4 * gb + t : HV * (t * NG + gb) + hf; };
 
+  // --- zero term: c -= sum over groups g of xs[m, g] z[n, g], z = (f_t - 1) S + ZS for the quarter
+  // t of g (the bias fold of the dequant), on the matrix cores. Both factors are split exactly into
+  // bf16 parts, -xs (fp32) into three and z (at most 16 significant bits for the scales the packer
+  // writes) into two, and each group takes the 8 k-slots of one lane block: the six cross products
+  // and two zeros. One step covers four groups, lane block h taking group g; zero_read fetches the
+  // step's operands from LDS (the group sums, given or taken here, and the S | ZS word), zero_mfma
+  // splits them and applies the step; with on false the step adds zeros (its operands may not be
+  // written yet, so they are selected away rather than multiplied by 0).
+  auto zero_read = [&](int g, float (&xv)[MT], uint32_t (&zw)[kNT]) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + col;
+      xv[mt] = xsl[g * T::MR + m];  // the given sums, or the parts of those taken here
+      if (T::SP > 1 && own) xv[mt] += xsl[(KG + g) * T::MR + m];
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) zw[nt] = szc[16 * nt * KGP + g];
+  };
+  auto zero_mfma = [&](int g, const float (&xv)[MT], const uint32_t (&zw)[kNT], bool on) {
+    const int t = g / (HV * NG);
+    // kBiasF[t] - 1 (contiguous-4: codes at D = 4, no fold)
+    const float fm1 = VAR == kVarC4 ? 0.f : (t == 0 ? 31.f : (t == 1 ? 7.f : (t == 2 ? 1.f : 0.f)));
+    u32x4 za[MT], zb[kNT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const float v = on ? -xv[mt] : 0.f;
+      const uint32_t p1 = __float_as_uint(v) & 0xffff0000u;
+      const float r1 = v - __uint_as_float(p1);
+      const uint32_t p2 = __float_as_uint(r1) & 0xffff0000u;
+      const uint32_t p3 = __float_as_uint(r1 - __uint_as_float(p2));
+      za[mt] = u32x4{__builtin_amdgcn_perm(p1, p1, 0x07060302u), __builtin_amdgcn_perm(p2, p2, 0x07060302u),
+                     __builtin_amdgcn_perm(p3, p3, 0x07060302u), 0u};
+    }
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) {
+      const uint32_t sz = zw[nt];
+      const float z = fmaf(fm1, __uint_as_float(sz << 16), __uint_as_float(sz & 0xffff0000u));
+      const uint32_t zh = __float_as_uint(z) & 0xffff0000u;
+      const uint32_t zl = __float_as_uint(z - __uint_as_float(zh));
+      const uint32_t pr = __builtin_amdgcn_perm(zl, zh, 0x07060302u);  // bf16 zh | bf16 zl << 16
+      zb[nt] = u32x4{pr, pr, pr, 0u};
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[mt]),
+                                                              __builtin_bit_cast(bf16x8, zb[nt]), acc[mt][nt], 0, 0, 0);
+  };
+  // Up to 32 rows (one x stage per span) the zero term of span gb - 1 runs inside stage gb, whose
+  // barrier has made that span's group sums visible: its LDS reads are issued at the stage's start
+  // and its MFMAs follow the first quarter, where the stream's waits hide them. The last span's
+  // step follows the loop. The 64-row tile has no registers for it and takes every group after
+  // the loop.
+  constexpr bool kZeroIn = MT <= 2 && VAR != kVarWTile;
+
   auto compute = [&](int st, int slot, bool clamp) {
     const int gb = st / T::SPS, t0 = (st % T::SPS) * T::QS;
     // lane h's k in a group: 16 h + 8 (s & 1) + 64 (s >> 1) (its two 16-byte loads), contiguous-4
@@ -292,6 +348,14 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     };
     u32x4 an[MT];
     if constexpr (kPrefA) a_read(0, 0, an);
+    // the zero term of the previous span (stage 0: a step that adds zeros)
+    const int zg = st > 0 ? st - 1 : 0;
+    float zx[HV][MT];
+    uint32_t zw[HV][kNT];
+    if constexpr (kZeroIn) {
+#pragma unroll
+      for (int hf = 0; hf < HV; ++hf) zero_read(gidx(h, zg, hf), zx[hf], zw[hf]);
+    }
 #pragma unroll
     for (int qq = 0; qq < T::QS; ++qq) {
       const int t = t0 + qq;  // the quarter (contiguous-4: the group of the span)
@@ -392,6 +456,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) asm volatile("" : "+v"(acc[mt][nt]));
+      if constexpr (kZeroIn) {
+        if (qq == 0) {
+#pragma unroll
+          for (int hf = 0; hf < HV; ++hf) zero_mfma(gidx(h, zg, hf), zx[hf], zw[hf], st > 0);
+        }
+      }
     }
     if (own) {
       // this wave's part of the group sums of quarter t0 + sq_q, row tile sq_mt: its 4 / SP slices
@@ -465,46 +535,25 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     }
   }
 
-  // --- zero term: c -= sum over groups g of xs[m, g] z[n, g], z = (f_t - 1) S + ZS for the quarter
-  // t of g (the bias fold of the dequant), on the matrix cores. Both factors are split exactly into
-  // bf16 parts, -xs (fp32) into three and z (at most 16 significant bits for the scales the packer
-  // writes) into two, and each group takes the 8 k-slots of one lane block: the six cross products
-  // and two zeros. Step ks covers groups 4 ks + h.
+  // --- the zero term after the loop: the last span's step, or (64 rows) every group, step ks taking
+  // groups 4 ks + h
   if (own) __syncthreads();  // every part of every group sum is in LDS
+  if constexpr (kZeroIn) {
+#pragma unroll
+    for (int hf = 0; hf < HV; ++hf) {
+      float zx[MT];
+      uint32_t zw[kNT];
+      zero_read(gidx(h, NG - 1, hf), zx, zw);
+      zero_mfma(gidx(h, NG - 1, hf), zx, zw, true);
+    }
+  } else {
 #pragma unroll 2
-  for (int ks = 0; ks < (VAR == kVarWTile ? 0 : KG / 4); ++ks) {
-    const int g = 4 * ks + h, t = g / (HV * NG);
-    // kBiasF[t] - 1 (contiguous-4: codes at D = 4, no fold)
-    const float fm1 = VAR == kVarC4 ? 0.f : (t == 0 ? 31.f : (t == 1 ? 7.f : (t == 2 ? 1.f : 0.f)));
-    u32x4 za[MT], zb[kNT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + col;
-      float sm = xsl[g * T::MR + m];  // the given sums, or the parts of those taken here
-      if (T::SP > 1 && own) sm += xsl[(KG + g) * T::MR + m];
-      const float v = -sm;
-      const uint32_t p1 = __float_as_uint(v) & 0xffff0000u;
-      const float r1 = v - __uint_as_float(p1);
-      const uint32_t p2 = __float_as_uint(r1) & 0xffff0000u;
-      const uint32_t p3 = __float_as_uint(r1 - __uint_as_float(p2));
-      za[mt] = u32x4{__builtin_amdgcn_perm(p1, p1, 0x07060302u), __builtin_amdgcn_perm(p2, p2, 0x07060302u),
-                     __builtin_amdgcn_perm(p3, p3, 0x07060302u), 0u};
+    for (int ks = 0; ks < (VAR == kVarWTile ? 0 : KG / 4); ++ks) {
+      float zx[MT];
+      uint32_t zw[kNT];
+      zero_read(4 * ks + h, zx, zw);
+      zero_mfma(4 * ks + h, zx, zw, true);
     }
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const uint32_t w = szc[16 * nt * KGP + g];
-      const float z = fmaf(fm1, __uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-      const uint32_t zh = __float_as_uint(z) & 0xffff0000u;
-      const uint32_t zl = __float_as_uint(z - __uint_as_float(zh));
-      const uint32_t pr = __builtin_amdgcn_perm(zl, zh, 0x07060302u);  // bf16 zh | bf16 zl << 16
-      zb[nt] = u32x4{pr, pr, pr, 0u};
-    }
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, za[mt]),
-                                                              __builtin_bit_cast(bf16x8, zb[nt]), acc[mt][nt], 0, 0, 0);
   }
 
   // --- epilogue: acc[mt][nt][r] is c[m = 16 mt + 4 h + r][n = n0 + 16 nt + col]
