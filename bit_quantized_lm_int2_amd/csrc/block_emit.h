@@ -5,6 +5,7 @@
 // kTRow floats, -inf past the vocabulary's end); keys are fp64-coded (value, column) so that a
 // compare-exchange is v_max_f64 + v_min_f64.
 #pragma once
+#include "dequant.h"
 #include "device_util.h"
 
 namespace i2h {
@@ -66,9 +67,12 @@ __device__ __forceinline__ double dpp_f64(double v) {
 
 // Block top-kc (kc <= 8) of the wave's block for rows < M. tw[m][c] holds the block's logits
 // (-inf past column N). P lanes share a row, each ranking 64 / P of its columns; the P partial
-// top-8 lists meet through DPP quad permutes.
+// top-8 lists meet through DPP quad permutes. The lists are then staged in the wave's own rows of
+// tw ([MR][16]: 8 scores, 8 indices) and stored by 8 consecutive lanes per row, so that each store
+// instruction writes one 32-byte run per row: one scattered dword per lane and slot had made the
+// stores, not the ranking, most of the emit's time at 32 and 64 rows (8x the memory requests).
 template <int MR, int P>
-__device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, int kc, int64_t ld,
+__device__ __forceinline__ void emit_top8(float* tw, int M, int b, int N, int kc, int64_t ld,
                                           float* __restrict__ cand_score, int32_t* __restrict__ cand_idx,
                                           float* __restrict__ bmax) {
   constexpr int V = 64 / P;
@@ -96,17 +100,35 @@ __device__ __forceinline__ void emit_top8(const float* tw, int M, int b, int N, 
     for (int i = 0; i < 8; ++i) o[i] = dpp_f64<0x4E>(k[i]);  // quad_perm [2,3,0,1]: lane ^ 2
     merge_top8(k, o);
   }
-  if (part == 0 && row < MR && row < M) {
-    const int64_t at = (int64_t)row * ld + (int64_t)b * kc;
+  // every lane's reads of tw are issued above; LDS operations of one wave complete in order, and
+  // this keeps the compiler from moving the staging writes above them
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t* stg = reinterpret_cast<uint32_t*>(tw);  // [MR][16]
+  if (part == 0 && row < MR) {
+    u32x4 sc[2], ix[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < kc) {
-        const int tok = b * kBlockN + key_col(k[i]);
-        const bool ok = tok < N;
-        cand_score[at + i] = ok ? key_value(k[i]) : -__builtin_inff();
-        cand_idx[at + i] = ok ? tok : -1;
-        if (i == 0 && bmax != nullptr) bmax[(int64_t)row * (ld / kc) + b] = ok ? key_value(k[i]) : -__builtin_inff();
-      }
+      const int tok = b * kBlockN + key_col(k[i]);
+      const bool ok = tok < N;
+      sc[i >> 2][i & 3] = __float_as_uint(ok ? key_value(k[i]) : -__builtin_inff());
+      ix[i >> 2][i & 3] = (uint32_t)(ok ? tok : -1);
+    }
+    u32x4* d = reinterpret_cast<u32x4*>(stg + row * 16);
+    d[0] = sc[0];
+    d[1] = sc[1];
+    d[2] = ix[0];
+    d[3] = ix[1];
+    if (bmax != nullptr && row < M) bmax[(int64_t)row * (ld / kc) + b] = __uint_as_float(sc[0][0]);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int sl = lane & 7;
+#pragma unroll
+  for (int j = 0; j < MR / 8; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    if (r < M && sl < kc) {
+      const int64_t at = (int64_t)r * ld + (int64_t)b * kc + sl;
+      cand_score[at] = __uint_as_float(stg[r * 16 + sl]);
+      cand_idx[at] = (int32_t)stg[r * 16 + 8 + sl];
     }
   }
 }
