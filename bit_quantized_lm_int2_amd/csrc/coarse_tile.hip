@@ -11,16 +11,19 @@
 // span of the packed rows: the whole span up to 32 rows, one quarter at 64), double-buffered and
 // shared by the waves. The loop applies only the scale of each group to the accumulator; the zero
 // term, the sum over groups of xs[m, g] z[n, g], is one more small contraction on the matrix
-// cores after the loop, with both factors split exactly into bf16 parts, so that the VALU does the
-// dequant and one FMA per output and group. The group sums xs are given (i2h_xsum; staged in LDS
-// before the loop) or, with xs null, taken in the kernel: each wave sums one part of one
-// (quarter, row tile) per stage on the matrix cores, against a B operand of ones, into LDS. The
-// wave's S and ZS rows sit in LDS for the whole K loop. The packed stream is loaded one span ahead,
-// after the next stage of x, so that waiting for x never waits for packed bytes that are not
-// needed yet (loads retire in order); with more than one stage per span (64 rows) the later
-// stages' x loads do queue behind the next span's packed loads.
+// cores (up to 32 rows one step per span inside the loop, one span behind; at 64 rows after the
+// loop), with both factors split exactly into bf16 parts, so that the VALU does the dequant and one
+// FMA per output and group. The group sums xs are given (i2h_xsum; staged in LDS before the loop)
+// or, with xs null, taken in the kernel: each wave sums one part of one (quarter, row tile) per
+// stage on the matrix cores, against a B operand of ones, into LDS. The wave's S and ZS rows sit
+// in LDS for the whole K loop. The packed stream is loaded one span ahead, after the next stage of
+// x, so that waiting for x never waits for packed bytes that are not needed yet (loads retire in
+// order); with more than one stage per span (64 rows) the later stages' x loads do queue behind
+// the next span's packed loads. Up to 32 rows each slice's x fragments are read from LDS one
+// slice ahead.
 // The emit transposes the block through LDS and ranks it with fp64 keys (value, column) in
-// sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions.
+// sorting networks: v_max_f64 / v_min_f64 make a compare-exchange two instructions; the lists go
+// out as one 32-byte run per row and store.
 #include <type_traits>
 
 #include "ablation.h"
