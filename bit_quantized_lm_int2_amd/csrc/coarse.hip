@@ -773,7 +773,10 @@ int coarse_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* 
                ? small_band(xc, xsc, (int)mc, packed, S, ZS, (int)N, (int)K, kcand, csc, cic, yc, bmc, zcc, s)
                : I2H_ERR_ARG;
     else if (tile_ok)
-      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, bmc, zcc, s);
+      // every other chunk takes the blocks in reverse order: it starts on the blocks the chunk
+      // before it read last, which the memory-side cache may still hold
+      st = tile_launch(xc, xsc, mc, packed, S, ZS, N, K, kcand, csc, cic, yc, bmc, zcc, s,
+                       (int)((m0 / kTileMaxRows) & 1));
     else if (!xsc)
       st = I2H_ERR_ARG;
     else

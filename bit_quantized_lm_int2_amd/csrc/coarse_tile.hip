@@ -87,7 +87,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ xs, int M,
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ S,
     const uint16_t* __restrict__ ZS, int N, int kc, int nblk, float* __restrict__ cand_score,
-    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, float* __restrict__ bmax, int32_t* __restrict__ zc) {
+    int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y, float* __restrict__ bmax, int32_t* __restrict__ zc,
+    int rev) {
   using T = Tile<MT, WAVES>;
   static_assert(VAR == kVarDesign || MT == 1, "alternatives: the 16-row tile");
   constexpr int GV = VAR == kVarG64 ? 64 : kGroup;  // quantisation group along k
@@ -102,7 +103,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
   float* xsl = reinterpret_cast<float*>(szl + WAVES * 64 * KGP);
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, h = lane >> 4;
-  const int b = blockIdx.x * WAVES + wave;  // this wave's block; >= nblk only in the last workgroup
+  // rev: the workgroups take their blocks in reverse order (a later launch over the same weights then
+  // starts on the blocks the previous one read last, which the memory-side cache may still hold)
+  const int wg = rev ? (int)gridDim.x - 1 - (int)blockIdx.x : (int)blockIdx.x;
+  const int b = wg * WAVES + wave;  // this wave's block; >= nblk only in the workgroup of the last blocks
   const int n0 = b * kBlockN;
   // zc (may be null): one int per row, set to 0 (the arrival counters of the head's tail)
   if (zc != nullptr && blockIdx.x == 0 && tid < M) zc[tid] = 0;
@@ -602,12 +606,12 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void coarse_tile_kernel(
 template <int MT, int WAVES, int NGC>
 int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
                 const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
-                hipStream_t s) {
+                hipStream_t s, int rev) {
   const int nblk = (int)nblk_of(N);
   const size_t lds = tile_lds_bytes<MT, WAVES>(NGC * 4);
   hipLaunchKernelGGL((coarse_tile_kernel<MT, WAVES, NGC, I2H_TILE_XPF, I2H_TILE_RPF>),
                      dim3((unsigned)((nblk + WAVES - 1) / WAVES)), dim3(64 * WAVES), lds, s, x, xs, M, packed, S, ZS, N,
-                     kc, nblk, cs, ci, y, bmax, zc);
+                     kc, nblk, cs, ci, y, bmax, zc, rev);
   return check_launch();
 }
 
@@ -634,12 +638,12 @@ int launch_tile(const uint16_t* x, const float* xs, int M, const uint8_t* packed
 template <int NGC>
 int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, const uint16_t* S,
               const uint16_t* ZS, int N, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
-              hipStream_t s) {
-  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
+              hipStream_t s, int rev) {
+  if (M <= 16) return launch_tile<1, I2H_TILE_WAVES, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s, rev);
   if constexpr (I2H_TILE_MAXMT >= 2)
-    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES32, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
+    if (M <= 32) return launch_tile<2, I2H_TILE_WAVES32, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s, rev);
   if constexpr (I2H_TILE_MAXMT >= 4)
-    return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s);
+    return launch_tile<4, I2H_TILE_WAVES64, NGC>(x, xs, M, packed, S, ZS, N, kc, cs, ci, y, bmax, zc, s, rev);
   // rows in chunks of 16 through the 16-row tile (a build limited to it)
   const int64_t ld = nblk_of(N) * kc, KG = NGC * 4;
   for (int m0 = 0; m0 < M; m0 += 16) {
@@ -648,7 +652,7 @@ int tile_rows(const uint16_t* x, const float* xs, int M, const uint8_t* packed, 
                                                        mc, packed, S, ZS, N, kc, cs + m0 * ld, ci + m0 * ld,
                                                        y ? y + (int64_t)m0 * N : nullptr,
                                                        bmax ? bmax + (int64_t)m0 * nblk_of(N) : nullptr,
-                                                       zc ? zc + m0 : nullptr, s);
+                                                       zc ? zc + m0 : nullptr, s, rev ^ (m0 / 16 & 1));
     if (st != I2H_OK) return st;
   }
   return I2H_OK;
@@ -664,7 +668,7 @@ int launch_tile_variant(const uint16_t* x, const float* xs, int M, const uint8_t
     constexpr int NGC = decltype(ngc)::value;
     const size_t lds = tile_lds_bytes<1, 4>(NGC * 4 * HV);
     hipLaunchKernelGGL((coarse_tile_kernel<1, 4, NGC, I2H_TILE_XPF, I2H_TILE_RPF, VAR>), dim3((unsigned)((nblk + 3) / 4)),
-                       dim3(256), lds, s, x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, nullptr, nullptr, nullptr);
+                       dim3(256), lds, s, x, xs, M, packed, S, ZS, N, kc, nblk, cs, ci, nullptr, nullptr, nullptr, 0);
   };
   if (K == 5120) go(std::integral_constant<int, 10>{});
   else go(std::integral_constant<int, 1>{});
@@ -678,7 +682,7 @@ int tile_variant_launch(int var, const uint16_t* x, const float* xs, int64_t M, 
                         hipStream_t s) {
   if (M < 1 || M > 16 || (K != 512 && K != 5120)) return I2H_ERR_SHAPE;
   switch (var) {
-    case kVarDesign: return tile_launch(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, nullptr, nullptr, nullptr, s);
+    case kVarDesign: return tile_launch(x, xs, M, packed, S, ZS, N, K, kc, cs, ci, nullptr, nullptr, nullptr, s, 0);
     case kVarG64: return launch_tile_variant<kVarG64>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
     case kVarC4: return launch_tile_variant<kVarC4>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
     case kVarWTile: return launch_tile_variant<kVarWTile>(x, xs, (int)M, packed, S, ZS, (int)N, (int)K, kc, cs, ci, s);
@@ -696,16 +700,16 @@ bool tile_sums_x(int64_t M, int64_t K) { return tile_supported(M, K) && M <= 32;
 
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax, int32_t* zc,
-                hipStream_t s) {
+                hipStream_t s, int rev) {
   if (!tile_supported(M, K)) return I2H_ERR_SHAPE;
   if (!xs && !tile_sums_x(M, K)) return I2H_ERR_ARG;
   switch (K / 512) {
-    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
-    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
-    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
-    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
-    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
-    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s);
+    case 10: return tile_rows<10>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
+    case 8: return tile_rows<8>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
+    case 6: return tile_rows<6>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
+    case 4: return tile_rows<4>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
+    case 2: return tile_rows<2>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
+    default: return tile_rows<1>(x, xs, (int)M, packed, S, ZS, (int)N, kc, cs, ci, y, bmax, zc, s, rev);
   }
 }
 

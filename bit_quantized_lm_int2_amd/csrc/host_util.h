@@ -31,13 +31,14 @@ bool coarse_sums_x(int64_t M, int64_t K);
 // The many-row coarse kernel (coarse_tile.hip): up to kTileMaxRows rows of x per launch, for the
 // K it is built for; it takes the group sums xs from i2h_xsum, or sums x itself when xs is null
 // and tile_sums_x (up to 32 rows). zc (may be null): M ints the launch sets to 0. bmax (may be
-// null): [M, nblk] floats, each block's best score per row (the first slot of its list).
+// null): [M, nblk] floats, each block's best score per row (the first slot of its list). rev:
+// the blocks are taken in reverse order (for a second launch over the same weights).
 constexpr int64_t kTileMaxRows = 64;
 bool tile_supported(int64_t M, int64_t K);
 bool tile_sums_x(int64_t M, int64_t K);
 int tile_launch(const uint16_t* x, const float* xs, int64_t M, const uint8_t* packed, const uint16_t* S,
                 const uint16_t* ZS, int64_t N, int64_t K, int kc, float* cs, int32_t* ci, uint16_t* y, float* bmax,
-                int32_t* zc, hipStream_t s);
+                int32_t* zc, hipStream_t s, int rev = 0);
 
 // The design alternatives (ablation.h: var) through the production kernels, for the checks of
 // i2h_coarse_variant_topk: one row through the one-row kernel, 1..16 rows through the 16-row
