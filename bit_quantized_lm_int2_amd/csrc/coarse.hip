@@ -213,10 +213,14 @@ constexpr int kHalfOff = I2H_SMALL_SECTOR ? 64 : 16;  // byte offset of its seco
 #define I2H_COARSE_SLICE_FENCE 1
 #endif  // 128-byte spans of the packed stream in flight per lane
 
+// Rows of the transposed group-sum table per group: the rows an accumulator lane can hold, 4 when
+// at most two rows are real (every lane then reads the same four, and only rows 0 and 1 are used).
+__host__ __device__ constexpr int small_xs_rows(int maxr) { return maxr <= 2 ? 4 : 16; }
+
 // LDS footprint of coarse_small_kernel in bytes: S|ZS for the block's rows, xs transposed (G: the
 // quantisation group), the block's 64-bit ranking keys for its maxr rows, and x itself when xlds.
 __host__ __device__ constexpr size_t small_lds_bytes(int K, int maxr, bool xlds, int G = kGroup) {
-  return (size_t)64 * (K / G) * 4 + (size_t)(K / G) * 16 * 4 + (size_t)maxr * kBlockN * 8 +
+  return (size_t)64 * (K / G) * 4 + (size_t)(K / G) * small_xs_rows(maxr) * 4 + (size_t)maxr * kBlockN * 8 +
          (xlds ? (size_t)maxr * K * 2 : 0);
 }
 
@@ -281,8 +285,9 @@ __global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : (MAXR == 1 && VAR =
   if constexpr (NGC > 0) K = NGC * 512;
   const int Q = K >> 2, NG = NGC > 0 ? NGC : Q / kGroup, KG = K / GV;
   uint32_t* sz = lds;                                        // [64][KG]: S | ZS << 16
-  float* xsT = reinterpret_cast<float*>(sz + 64 * KG);       // [KG][16]
-  uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * 16);  // [MAXR][64] ranking keys
+  constexpr int XR = small_xs_rows(MAXR);                   // rows of xsT per group
+  float* xsT = reinterpret_cast<float*>(sz + 64 * KG);       // [KG][XR]
+  uint64_t* ck = reinterpret_cast<uint64_t*>(xsT + KG * XR);  // [MAXR][64] ranking keys
   uint16_t* xl = reinterpret_cast<uint16_t*>(ck + MAXR * kBlockN);  // [MAXR][K] when XLDS
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, h = lane >> 4;
@@ -377,27 +382,27 @@ __global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : (MAXR == 1 && VAR =
         for (int o = 1; o < GV / 8; o <<= 1) sm += __shfl_xor(sm, o);
         if ((tid & (GV / 8 - 1)) == 0 && u < xunits) {
           const int m = (8 * u) / K, g = (8 * u - m * K) / GV;
-          xsT[g * 16 + m] = sm;
+          xsT[g * XR + m] = sm;
         }
       }
     }
     if (kSums && xs == nullptr)
-      for (int i = tid; i < KG * 16; i += kCoarseThreads)
-        if ((i & 15) >= M) xsT[i] = 0.f;
+      for (int i = tid; i < KG * XR; i += kCoarseThreads)
+        if (i % XR >= M) xsT[i] = 0.f;
   } else if constexpr (XLDS) {
     for (int u = tid; u < xunits; u += kCoarseThreads) put_x(u, ld16(x + 8 * u));
   }
   if (kSums && xs != nullptr) {
-    for (int i = tid; i < KG * 16; i += kCoarseThreads) {
-      const int g = i >> 4, m = i & 15;
+    for (int i = tid; i < KG * XR; i += kCoarseThreads) {
+      const int g = i / XR, m = i % XR;
       xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
     }
   }
   __syncthreads();
   if (!kXReg && kSums && xs == nullptr) {
     // group sums from the LDS copy of x (only launched so with x in LDS): one thread per group
-    for (int i = tid; i < KG * 16; i += kCoarseThreads) {
-      const int g = i >> 4, m = i & 15;
+    for (int i = tid; i < KG * XR; i += kCoarseThreads) {
+      const int g = i / XR, m = i % XR;
       float sm = 0.f;
       if (m < M) {
         const int t = g / NG, gb = g - t * NG;
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : (MAXR == 1 && VAR =
       for (int i = 0; i < 4; ++i) {  // codes read at D = 4: the scale and zero as they are
         const int gi = 4 * gb + i;
         const uint32_t w = szr[gi];
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * XR + (XR == 16 ? 4 * h : 0));
 #pragma unroll
         for (int r = 0; r < RR; ++r)
           acc[r] = fmaf(-xv[r], __uint_as_float(w & 0xffff0000u), fmaf(__uint_as_float(w << 16), p[i][r], acc[r]));
@@ -493,7 +498,7 @@ __global__ __launch_bounds__(kCoarseThreads, MAXR == 2 ? 4 : (MAXR == 1 && VAR =
         const float zv = __uint_as_float(w & 0xffff0000u);
         const float s2 = kBiasF[t] * sv;
         const float z2 = fmaf(kBiasF[t] - 1.f, sv, zv);
-        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * 16 + 4 * h);
+        const f32x4 xv = *reinterpret_cast<const f32x4*>(xsT + gi * XR + (XR == 16 ? 4 * h : 0));
 #pragma unroll
         for (int r = 0; r < RR; ++r) {
           const float a = fmaf(s2, p[t][r], acc[r]);
