@@ -193,8 +193,8 @@ __global__ __launch_bounds__(kCoarseThreads) void coarse_kernel(
 //   * quarters 0-2 are dequantised with a mask alone (dequant.h), the high byte of each half
 //     brought down by one shift shared by the four quarters: 12 VALU ops per 16 weights;
 //   * only the accumulator rows that can hold a real row are scaled.
-// In the head it takes one or two rows (one row: at most 80 VGPRs and 23 KB of LDS, six
-// workgroups per CU, two spans in flight per lane; two rows: 34 KB of LDS, four workgroups per
+// In the head it takes one or two rows (one row: at most 80 VGPRs and 21 KB of LDS, six
+// workgroups per CU, two spans in flight per lane; two rows: 32 KB of LDS, five workgroups per
 // CU; from three rows x in LDS costs occupancy and the tile kernel is faster).
 // ---------------------------------------------------------------------------------------------
 
