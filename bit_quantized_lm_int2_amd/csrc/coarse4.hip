@@ -33,6 +33,11 @@ constexpr int kC4PfXl = I2H_C4_PF_XL;  // spans in flight when x sits in LDS
 #ifndef I2H_C4_PF_XL5120
 #define I2H_C4_PF_XL5120 3
 #endif
+// waves per SIMD the launch bound asks for on the unrolled path: 6 (79 VGPRs, 22 KB of LDS: six
+// workgroups per CU; 84 VGPRs and five without the bound, 1.1 us slower)
+#ifndef I2H_C4_WPE_XL5120
+#define I2H_C4_WPE_XL5120 6
+#endif
 constexpr int kC4PfXl5120 = I2H_C4_PF_XL5120;  // the same, with the span loop unrolled (K = 5120)
 #ifndef I2H_C4_XL_BYTES
 #define I2H_C4_XL_BYTES 32768
@@ -67,7 +72,7 @@ __device__ __forceinline__ bf16x8 dequant4x8(uint32_t d0, uint32_t d1) {
 template <int MT, int HALF>
 __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8], const u32x4* xa,
                                       const uint16_t* xq, int M, int K, int col, float sv, float zv,
-                                      const float* xsg, int h) {
+                                      const float* xsg, int hrow) {
   f32x4 p[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) p[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -88,7 +93,7 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const f32x4 xv = *reinterpret_cast<const f32x4*>(xsg + mt * 16 + 4 * h);
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(xsg + mt * 16 + hrow);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float a = fmaf(sv, p[mt][r], acc[mt][r]);
@@ -103,21 +108,23 @@ __device__ __forceinline__ void half4(f32x4 (&acc)[MT], const uint32_t (&dw)[8],
 // span loop is unrolled completely and every wait for a span in flight is exact (a run-time loop
 // with its loads under a test makes the compiler wait for every load at each iteration).
 template <int MT, bool XL, int PF, int NSC = 0>
-__global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ xs,
+__global__ __launch_bounds__(kC4Threads, NSC > 0 ? I2H_C4_WPE_XL5120 : 1) void coarse4_kernel(const uint16_t* __restrict__ x, const float* __restrict__ xs,
                                                              int M, const uint8_t* __restrict__ packed,
                                                              const uint16_t* __restrict__ S,
                                                              const uint16_t* __restrict__ ZS, int N, int K, int kc,
                                                              int nblk, float* __restrict__ cand_score,
                                                              int32_t* __restrict__ cand_idx, uint16_t* __restrict__ y) {
   constexpr int MR = 16 * MT;
+  // with the span loop unrolled (XL): the block's S | ZS << 16 rows, [64][KG | 1], each wave's 16
+  // rows staged by that wave, so the ring holds only packed bytes; there at most 3 rows are real
+  // (x in LDS), so the group sums and the emit's logits keep 4 rows, not 16
+  constexpr bool kSzL = XL && NSC > 0;
+  constexpr int XR = kSzL ? 4 : MR;  // rows per group of xsT, rows of cbuf
   extern __shared__ float smem[];
   const int H = K >> 1, NS = H / kGroup, KG = K / kGroup;
-  float* xsT = smem;             // [KG][MR]: xs transposed, zero past row M
-  float* cbuf = smem + KG * MR;  // [MR][64]: the block's logits for the emit
-  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + MR * kBlockN);  // [M][K] when XL
-  // with the span loop unrolled (XL): the block's S | ZS << 16 rows, [64][KG | 1], each wave's 16
-  // rows staged by that wave, so the ring holds only packed bytes
-  constexpr bool kSzL = XL && NSC > 0;
+  float* xsT = smem;             // [KG][XR]: xs transposed, zero past row M
+  float* cbuf = smem + KG * XR;  // [XR][64]: the block's logits for the emit
+  uint16_t* xl = reinterpret_cast<uint16_t*>(cbuf + XR * kBlockN);  // [M][K] when XL
   const int KGP = KG | 1;
   uint32_t* szl = reinterpret_cast<uint32_t*>(xl + (XL ? M * K : 0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -127,8 +134,8 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   const bool nvalid = n < N;
   const int nr = nvalid ? n : 0;
 
-  for (int i = tid; i < KG * MR; i += kC4Threads) {
-    const int g = i / MR, m = i - g * MR;
+  for (int i = tid; i < KG * XR; i += kC4Threads) {
+    const int g = i / XR, m = i - g * XR;
     xsT[i] = m < M ? xs[(int64_t)m * KG + g] : 0.f;
   }
   if constexpr (kSzL) {  // this wave's 16 rows (rows past N: zeros, never emitted)
@@ -214,8 +221,10 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
       s1 = sl.s1;
       z1 = sl.z1;
     }
-    half4<MT, 0>(acc, dw, xa, xg, M, K, col, bf16_lo(s0), bf16_lo(z0), xsT + g0 * MR, h);
-    half4<MT, 1>(acc, dw, xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(s1), bf16_lo(z1), xsT + g1 * MR, h);
+    // (with 4 rows per group every lane reads the same four: only those of the real rows count)
+    half4<MT, 0>(acc, dw, xa, xg, M, K, col, bf16_lo(s0), bf16_lo(z0), xsT + g0 * XR, XR == MR ? 4 * h : 0);
+    half4<MT, 1>(acc, dw, xa + (MT == 1 ? 4 : 0), xg + H, M, K, col, bf16_lo(s1), bf16_lo(z1), xsT + g1 * XR,
+                 XR == MR ? 4 * h : 0);
   };
   Slot ring[PF];
 #pragma unroll
@@ -254,7 +263,8 @@ __global__ __launch_bounds__(kC4Threads) void coarse4_kernel(const uint16_t* __r
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      cbuf[(mt * 16 + 4 * h + r) * kBlockN + wave * 16 + col] = nvalid ? acc[mt][r] : -__builtin_inff();
+      if (mt * 16 + 4 * h + r < XR)
+        cbuf[(mt * 16 + 4 * h + r) * kBlockN + wave * 16 + col] = nvalid ? acc[mt][r] : -__builtin_inff();
   __syncthreads();
 
   const int64_t ld = (int64_t)nblk * kc;
@@ -279,10 +289,11 @@ void launch4(const uint16_t* x, const float* xs, int M, const uint8_t* packed, c
   const size_t xbytes = (size_t)M * K * 2;
   if constexpr (MT == 1) {
     if (xbytes <= kC4XlBytes) {
-      if (K == 5120)  // the head's K: the span loop unrolled, S / ZS rows in LDS
+      if (K == 5120)  // the head's K: the span loop unrolled, S / ZS rows in LDS, 4-row group sums and logits
         hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl5120, 20>), dim3((unsigned)nblk), dim3(kC4Threads),
-                           lds + xbytes + (size_t)64 * ((K / kGroup) | 1) * 4, s, x, xs, M, packed, S, ZS, N, K,
-                           kc, nblk, cs, ci, y);
+                           ((size_t)(K / kGroup) * 4 + (size_t)4 * kBlockN) * sizeof(float) + xbytes +
+                               (size_t)64 * ((K / kGroup) | 1) * 4,
+                           s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
       else
         hipLaunchKernelGGL((coarse4_kernel<MT, true, kC4PfXl>), dim3((unsigned)nblk), dim3(kC4Threads), lds + xbytes,
                            s, x, xs, M, packed, S, ZS, N, K, kc, nblk, cs, ci, y);
